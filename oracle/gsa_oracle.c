@@ -1,0 +1,381 @@
+/*
+ * GSA forward oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, step-by-step CPU implementation of the Global Sparse
+ * Attention (GSA) forward pass of "Speed3R: Sparse Feed-forward 3D
+ * Reconstruction Models" (CVPR 2026, arXiv 2603.08055), as described on the
+ * Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models"
+ * (sections "全局稀疏注意力（GSA）核心设计", "压缩分支", "选择分支",
+ * "门控聚合", "Speed3R-VGGT 适配").  Only the tests, the package smoke check
+ * and the benchmark's CPU-baseline leg may call it; the HIP library never
+ * does, and the two share no code.
+ *
+ * Arithmetic: inputs (bf16 bits or fp32) are widened exactly to double and
+ * every dot product, exponential, sum and division is done in double.  The
+ * single rounding inside the definition is the pooled tensors, which are
+ * stored in the input precision (reading: average pooling of a bf16 tensor
+ * gives a bf16 tensor).  Build with -ffp-contract=off and without fast-math.
+ *
+ * Layouts (all host memory, row-major):
+ *   q, k, v       [N][T_f][H][d], T_f = P + h*w; token p < P of a frame is a
+ *                 special token, token p >= P is image pixel (y, x) =
+ *                 divmod(p - P, w).
+ *   pooled        [M'][H][d] as float (values exactly representable in the
+ *                 input precision); window j = f*(h/s)*(w/s) + wy*(w/s) + wx.
+ *   per-window    rows follow the window's s*s tokens in row-major order
+ *   outputs       (dy outer, dx inner).
+ *
+ * Readings of points the pages leave open (each is also listed with the
+ * design notes of the library):
+ *   - every step is per head; top-k is chosen per head;
+ *   - the scale 1/sqrt(d) is used in all three attentions; the guide score
+ *     used for selection is the raw product Q_comp K_comp^T;
+ *   - top-k order is (score descending, window index ascending); ties go to
+ *     the lower window index; k' = min(k, #candidates), slots past k' = -1;
+ *   - image queries attend only image tokens of the selected windows, plus,
+ *     when fixed-context frames are given, all T_f tokens of those frames in
+ *     one joint softmax; context-frame windows are not top-k candidates when
+ *     ctx_exclude is set;
+ *   - the gate is g = sigmoid(W_g[h] . q) with W_g of shape [H][d], no bias.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int n_frames, n_special, grid_h, grid_w;
+  int n_heads, head_dim, pool, topk;
+  int n_ctx;
+  int ctx_frames[16];
+  int ctx_exclude;
+  double scale; /* 0 -> 1/sqrt(head_dim) */
+  int dtype;    /* 0: bf16 bits (uint16), 1: fp32 */
+} orc_cfg;
+
+/* ---- element access and rounding ------------------------------------- */
+
+static double elem(const void* p, int dtype, int64_t i) {
+  if (dtype == 1) return (double)((const float*)p)[i];
+  uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a float to bf16 (nearest, ties to even) and widen back to float. */
+static float round_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return f;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  u &= 0xFFFF0000u;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static double scale_of(const orc_cfg* c) {
+  return c->scale != 0.0 ? c->scale : 1.0 / sqrt((double)c->head_dim);
+}
+
+/* ---- token and window indexing (the split of X into spec/img rows) ------ */
+
+static int64_t tokens_per_frame(const orc_cfg* c) {
+  return (int64_t)c->n_special + (int64_t)c->grid_h * c->grid_w;
+}
+static int64_t n_tokens(const orc_cfg* c) { return (int64_t)c->n_frames * tokens_per_frame(c); }
+static int64_t windows_x(const orc_cfg* c) { return c->grid_w / c->pool; }
+static int64_t windows_per_frame(const orc_cfg* c) {
+  return (int64_t)(c->grid_h / c->pool) * windows_x(c);
+}
+static int64_t n_windows(const orc_cfg* c) { return (int64_t)c->n_frames * windows_per_frame(c); }
+
+/* Token row of the kk-th pixel (row-major inside the s x s window) of window j. */
+static int64_t window_token(const orc_cfg* c, int64_t j, int kk) {
+  int64_t f = j / windows_per_frame(c), r = j % windows_per_frame(c);
+  int64_t wy = r / windows_x(c), wx = r % windows_x(c);
+  int64_t y = wy * c->pool + kk / c->pool, x = wx * c->pool + kk % c->pool;
+  return f * tokens_per_frame(c) + c->n_special + y * c->grid_w + x;
+}
+
+static int is_ctx_frame(const orc_cfg* c, int64_t f) {
+  for (int i = 0; i < c->n_ctx; ++i)
+    if (c->ctx_frames[i] == f) return 1;
+  return 0;
+}
+
+/* Row (token t, head h) of a [M][H][d] tensor. */
+static int64_t row_off(const orc_cfg* c, int64_t t, int h) {
+  return (t * c->n_heads + h) * (int64_t)c->head_dim;
+}
+
+/* ---- plain softmax attention of one query row over a list of key rows ---- */
+
+/* out[0..d) = sum_t softmax_t(scale * q.k_t) v_t over the n listed tokens. */
+static void attend_tokens(const orc_cfg* c, const double* qrow, const void* k, const void* v,
+                          const int64_t* toks, int64_t n, int h, double* logits, double* out) {
+  const int d = c->head_dim;
+  const double sc = scale_of(c);
+  double mx = -INFINITY;
+  for (int64_t t = 0; t < n; ++t) {
+    int64_t o = row_off(c, toks[t], h);
+    double s = 0.0;
+    for (int e = 0; e < d; ++e) s += qrow[e] * elem(k, c->dtype, o + e);
+    logits[t] = sc * s;
+    if (logits[t] > mx) mx = logits[t];
+  }
+  double den = 0.0;
+  for (int e = 0; e < d; ++e) out[e] = 0.0;
+  for (int64_t t = 0; t < n; ++t) {
+    double w = exp(logits[t] - mx);
+    den += w;
+    int64_t o = row_off(c, toks[t], h);
+    for (int e = 0; e < d; ++e) out[e] += w * elem(v, c->dtype, o + e);
+  }
+  for (int e = 0; e < d; ++e) out[e] /= den;
+}
+
+/* ======================================================================== */
+/* Compression branch, pooling: s x s non-overlapping average pooling of the
+ * image Q/K/V into [M'][H][d], M' = M_img / s^2.  (Paper-Notes page, section
+ * "压缩分支": Q_comp, K_comp, V_comp from s x s non-overlapping average
+ * pooling.)  The s^2 values are summed in float in row-major order starting
+ * from +0, multiplied by 1/s^2 (a float computed once) and rounded to the
+ * input precision. */
+void orc_pool(const orc_cfg* c, const void* x, float* out) {
+  const int64_t nw = n_windows(c);
+  const int H = c->n_heads, d = c->head_dim, s2 = c->pool * c->pool;
+  const float inv_area = 1.0f / (float)s2;
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < nw; ++j)
+    for (int h = 0; h < H; ++h)
+      for (int e = 0; e < d; ++e) {
+        float acc = 0.0f;
+        for (int kk = 0; kk < s2; ++kk)
+          acc += (float)elem(x, c->dtype, row_off(c, window_token(c, j, kk), h) + e);
+        float m = acc * inv_area;
+        out[(j * H + h) * d + e] = c->dtype == 1 ? m : round_bf16(m);
+      }
+}
+
+/* ======================================================================== */
+/* Special tokens: dense softmax attention of each special query over all M
+ * tokens, O_spec = softmax(Q_spec K^T / sqrt(d_k)) V.  (Paper-Notes page,
+ * section "全局稀疏注意力（GSA）核心设计", the special-token equation.)
+ * rows[i] is a special-row id r in [0, N*P): frame r / P, token r % P.
+ * out: [n][H][d]. */
+void orc_special(const orc_cfg* c, const void* q, const void* k, const void* v,
+                 const int64_t* rows, int64_t n, double* out) {
+  const int H = c->n_heads, d = c->head_dim;
+  const int64_t M = n_tokens(c), tf = tokens_per_frame(c);
+#pragma omp parallel
+  {
+    int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * M);
+    double* logits = (double*)malloc(sizeof(double) * M);
+    double* qrow = (double*)malloc(sizeof(double) * d);
+    for (int64_t t = 0; t < M; ++t) toks[t] = t;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t ih = 0; ih < n * H; ++ih) {
+      int64_t i = ih / H;
+      int h = (int)(ih % H);
+      int64_t t = (rows[i] / c->n_special) * tf + rows[i] % c->n_special;
+      for (int e = 0; e < d; ++e) qrow[e] = elem(q, c->dtype, row_off(c, t, h) + e);
+      attend_tokens(c, qrow, k, v, toks, M, h, logits, out + (i * H + h) * d);
+    }
+    free(toks);
+    free(logits);
+    free(qrow);
+  }
+}
+
+/* ======================================================================== */
+/* Compressed attention, guide scores and top-k selection, for the listed
+ * query windows (all heads).
+ *   S_ij  = Q_comp_i . K_comp_j (raw, unscaled)       -- section "压缩分支",
+ *           guide-score equation;
+ *   O'_i  = softmax_j(scale * S_ij) V_comp_j over all M' windows -- same
+ *           section, compressed-attention equation;
+ *   TopK_i = first k' windows of the candidate set sorted by (S_ij desc,
+ *           j asc)                                   -- section "选择分支".
+ * Inputs qc, kc, vc: pooled [M'][H][d] floats.
+ * Outputs (n = number of listed windows):
+ *   oc        [n][H][d]     O'_comp rows;
+ *   topk_idx  [n][H][k]     k' sorted window ids then -1;
+ *   topk_sc   [n][H][k+1]   the k'+1 best guide scores (NaN when absent);
+ *   s_absmax  [n][H]        max_j |S_ij| over the candidates.
+ * Any of the outputs may be NULL. */
+typedef struct {
+  double s;
+  int64_t j;
+} scored;
+
+static int by_score_desc_index_asc(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+void orc_compressed(const orc_cfg* c, const float* qc, const float* kc, const float* vc,
+                    const int64_t* wins, int64_t n, double* oc, int32_t* topk_idx,
+                    double* topk_sc, double* s_absmax) {
+  const int H = c->n_heads, d = c->head_dim, K = c->topk;
+  const int64_t nw = n_windows(c), wpf = windows_per_frame(c);
+  const double sc = scale_of(c);
+#pragma omp parallel
+  {
+    double* S = (double*)malloc(sizeof(double) * nw);
+    scored* cand = (scored*)malloc(sizeof(scored) * nw);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t ih = 0; ih < n * H; ++ih) {
+      int64_t i = wins[ih / H];
+      int h = (int)(ih % H);
+      const float* qi = qc + (i * H + h) * d;
+      /* guide scores S_ij */
+      for (int64_t j = 0; j < nw; ++j) {
+        const float* kj = kc + (j * H + h) * d;
+        double s = 0.0;
+        for (int e = 0; e < d; ++e) s += (double)qi[e] * (double)kj[e];
+        S[j] = s;
+      }
+      /* compressed attention O'_i */
+      if (oc) {
+        double mx = -INFINITY, den = 0.0;
+        double* o = oc + (ih / H * H + h) * d;
+        for (int64_t j = 0; j < nw; ++j)
+          if (sc * S[j] > mx) mx = sc * S[j];
+        for (int e = 0; e < d; ++e) o[e] = 0.0;
+        for (int64_t j = 0; j < nw; ++j) {
+          double w = exp(sc * S[j] - mx);
+          den += w;
+          const float* vj = vc + (j * H + h) * d;
+          for (int e = 0; e < d; ++e) o[e] += w * (double)vj[e];
+        }
+        for (int e = 0; e < d; ++e) o[e] /= den;
+      }
+      /* top-k over the candidate windows */
+      int64_t nc = 0;
+      double amax = 0.0;
+      for (int64_t j = 0; j < nw; ++j) {
+        if (c->ctx_exclude && is_ctx_frame(c, j / wpf)) continue;
+        cand[nc].s = S[j];
+        cand[nc].j = j;
+        ++nc;
+        if (fabs(S[j]) > amax) amax = fabs(S[j]);
+      }
+      qsort(cand, (size_t)nc, sizeof(scored), by_score_desc_index_asc);
+      int64_t kk = nc < K ? nc : K;
+      int64_t base = ih / H * H + h;
+      if (topk_idx)
+        for (int t = 0; t < K; ++t) topk_idx[base * K + t] = t < kk ? (int32_t)cand[t].j : -1;
+      if (topk_sc)
+        for (int t = 0; t <= K; ++t) topk_sc[base * (K + 1) + t] = t < nc && t <= kk ? cand[t].s : NAN;
+      if (s_absmax) s_absmax[base] = amax;
+    }
+    free(S);
+    free(cand);
+  }
+}
+
+/* Guide scores S_ij for given (window i, head h, window j) triples laid out as
+ * idx [n][H][k] for the listed windows; out [n][H][k] (NaN where idx < 0). */
+void orc_guide_scores(const orc_cfg* c, const float* qc, const float* kc, const int64_t* wins,
+                      int64_t n, const int32_t* idx, int k, double* out) {
+  const int H = c->n_heads, d = c->head_dim;
+#pragma omp parallel for schedule(static)
+  for (int64_t ih = 0; ih < n * H; ++ih) {
+    int64_t i = wins[ih / H];
+    int h = (int)(ih % H);
+    for (int t = 0; t < k; ++t) {
+      int32_t j = idx[ih * k + t];
+      if (j < 0) {
+        out[ih * k + t] = NAN;
+        continue;
+      }
+      double s = 0.0;
+      for (int e = 0; e < d; ++e)
+        s += (double)qc[(i * H + h) * d + e] * (double)kc[((int64_t)j * H + h) * d + e];
+      out[ih * k + t] = s;
+    }
+  }
+}
+
+/* ======================================================================== */
+/* Selection branch: each image query of window i attends, in one softmax,
+ * the full-resolution image tokens of the windows in TopK_i (the s^2 queries
+ * of a window share one KV set) -- section "选择分支" -- together with all
+ * T_f tokens of every fixed-context frame -- section "Speed3R-VGGT 适配".
+ * idx: [n][H][k] window ids for the listed windows (entries < 0 ignored).
+ * out: [n][s*s][H][d]. */
+void orc_select(const orc_cfg* c, const void* q, const void* k, const void* v, const int64_t* wins,
+                int64_t n, const int32_t* idx, int kcols, double* out) {
+  const int H = c->n_heads, d = c->head_dim, s2 = c->pool * c->pool;
+  const int64_t tf = tokens_per_frame(c);
+  const int64_t cap = (int64_t)kcols * s2 + (int64_t)c->n_ctx * tf;
+#pragma omp parallel
+  {
+    int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * cap);
+    double* logits = (double*)malloc(sizeof(double) * cap);
+    double* qrow = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t ih = 0; ih < n * H; ++ih) {
+      int64_t i = wins[ih / H];
+      int h = (int)(ih % H);
+      int64_t nt = 0;
+      for (int t = 0; t < kcols; ++t) {
+        int32_t j = idx[ih * kcols + t];
+        if (j < 0) continue;
+        for (int kk = 0; kk < s2; ++kk) toks[nt++] = window_token(c, j, kk);
+      }
+      for (int cf = 0; cf < c->n_ctx; ++cf)
+        for (int64_t p = 0; p < tf; ++p) toks[nt++] = (int64_t)c->ctx_frames[cf] * tf + p;
+      for (int qq = 0; qq < s2; ++qq) {
+        int64_t tq = window_token(c, i, qq);
+        for (int e = 0; e < d; ++e) qrow[e] = elem(q, c->dtype, row_off(c, tq, h) + e);
+        attend_tokens(c, qrow, k, v, toks, nt, h, logits,
+                      out + (((ih / H) * s2 + qq) * H + h) * d);
+      }
+    }
+    free(toks);
+    free(logits);
+    free(qrow);
+  }
+}
+
+/* ======================================================================== */
+/* Upsampling and gated aggregation for the listed windows:
+ *   O_comp = nearest-neighbour upsampling of O'_comp  -- section "压缩分支";
+ *   g = sigmoid(W_g . q), O_img = g O_comp + (1 - g) O_sel -- section
+ *   "门控聚合".
+ * wg: [H][d] in the input precision, or NULL to use gate [n][s*s][H].
+ * oc: [n][H][d] (the windows' O'_comp rows); osel, out: [n][s*s][H][d]. */
+void orc_gate_combine(const orc_cfg* c, const void* q, const void* wg, const double* gate,
+                      const int64_t* wins, int64_t n, const double* oc, const double* osel,
+                      double* out) {
+  const int H = c->n_heads, d = c->head_dim, s2 = c->pool * c->pool;
+#pragma omp parallel for schedule(static)
+  for (int64_t iw = 0; iw < n; ++iw)
+    for (int qq = 0; qq < s2; ++qq) {
+      int64_t tq = window_token(c, wins[iw], qq);
+      for (int h = 0; h < H; ++h) {
+        double g;
+        if (wg) {
+          double z = 0.0;
+          for (int e = 0; e < d; ++e)
+            z += elem(wg, c->dtype, (int64_t)h * d + e) * elem(q, c->dtype, row_off(c, tq, h) + e);
+          g = 1.0 / (1.0 + exp(-z));
+        } else {
+          g = gate[(iw * s2 + qq) * H + h];
+        }
+        for (int e = 0; e < d; ++e) {
+          int64_t o = ((iw * s2 + qq) * H + h) * d + e;
+          out[o] = g * oc[(iw * H + h) * d + e] + (1.0 - g) * osel[o];
+        }
+      }
+    }
+}
+
+/* Token row of the qq-th pixel of window j (exported for the test harness,
+ * which scatters per-window rows back into the token layout). */
+int64_t orc_window_token(const orc_cfg* c, int64_t j, int qq) { return window_token(c, j, qq); }

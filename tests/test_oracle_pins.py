@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle against facts fixed by the pages' definitions.
+
+The pages print no worked GSA example, so every pin here is a special case,
+a closed form, brute force or a library routine reached by a different route
+than the oracle's own loops (numpy reshapes for the window geometry, torch's
+scaled_dot_product_attention in float64 for softmax attention, masks instead
+of gathers, lexsort for ordering).  Each test names the pin and the passage
+(Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models")
+it follows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gen.configs import BF16, F32, GSAShape
+
+
+def shape(**kw):
+    base = dict(name="pin", n_frames=2, n_special=1, grid_h=8, grid_w=8, n_heads=2, head_dim=16,
+                pool=2, topk=3, dtype=F32, seed=7)
+    base.update(kw)
+    return GSAShape(**base)
+
+
+def f64(x, sh):
+    return gen.to_f32(x, sh.dtype).astype(np.float64)
+
+
+# ---- independent geometry: numpy reshapes, not the oracle's index arithmetic ----
+
+def token_grid(sh):
+    return np.arange(sh.m_tokens, dtype=np.int64).reshape(sh.n_frames, sh.tokens_per_frame)
+
+
+def window_token_ids(sh):
+    """[M'][s*s] token rows of each window, from reshapes of the token grid."""
+    s, gh, gw = sh.pool, sh.grid_h, sh.grid_w
+    img = token_grid(sh)[:, sh.n_special:].reshape(sh.n_frames, gh // s, s, gw // s, s)
+    return img.transpose(0, 1, 3, 2, 4).reshape(-1, s * s)
+
+
+def image_token_ids(sh):
+    return token_grid(sh)[:, sh.n_special:].reshape(-1)
+
+
+def special_token_ids(sh):
+    return token_grid(sh)[:, :sh.n_special].reshape(-1)
+
+
+def sdpa(qrows, krows, vrows, scale, mask=None):
+    """softmax(scale q k^T [+mask]) v in float64 via torch's library routine."""
+    q = torch.from_numpy(np.ascontiguousarray(qrows))[None]
+    k = torch.from_numpy(np.ascontiguousarray(krows))[None]
+    v = torch.from_numpy(np.ascontiguousarray(vrows))[None]
+    m = None if mask is None else torch.from_numpy(mask)[None]
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=scale)[0].numpy()
+
+
+def flat(x, sh):
+    return f64(x, sh).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+
+
+# ---------------------------------------------------------------------------
+# P1 -- pooling is the window mean (section "压缩分支", s x s average pooling)
+
+@pytest.mark.parametrize("s", [1, 2, 4])
+def test_pool_integer_inputs_equal_window_mean(s):
+    sh = shape(pool=s, grid_h=8, grid_w=8)
+    rng = np.random.default_rng(1)
+    x = rng.integers(-8, 9, size=sh.qkv_shape).astype(np.float32)
+    got = oracle.pool(sh, x)
+    ref = x.astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)[window_token_ids(sh)].mean(1)
+    np.testing.assert_array_equal(got.astype(np.float64), ref)  # small integers: exact
+
+
+def test_pool_constant_window_and_identity():
+    sh = shape(pool=1)
+    q, _, _, _ = gen.make_inputs(sh)
+    np.testing.assert_array_equal(oracle.pool(sh, q), f64(q, sh)[:, 1:].reshape(-1, 2, 16))
+    sh4 = shape(pool=4)
+    x = np.full(sh4.qkv_shape, 0.3, np.float32)
+    np.testing.assert_array_equal(oracle.pool(sh4, x), np.float32(0.3) * np.ones((sh4.n_windows, 2, 16)))
+
+
+def test_pool_bf16_rounds_the_fp32_mean():
+    sh = shape(pool=4, dtype=BF16)
+    x, _, _, _ = gen.make_inputs(sh)
+    got = oracle.pool(sh, x).astype(np.float64)
+    ref = flat(x, sh)[window_token_ids(sh)].mean(1)
+    # the stored value is a bf16 number within half a bf16 ulp (plus fp32 sum error) of the mean
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+    bits = got.astype(np.float32).view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)
+
+
+# ---------------------------------------------------------------------------
+# P5 -- special tokens: dense softmax attention over all M tokens
+# (section "全局稀疏注意力（GSA）核心设计", special-token equation)
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_special_equals_dense_attention(dtype):
+    sh = shape(n_special=3, dtype=dtype)
+    q, k, v, _ = gen.make_inputs(sh)
+    rows = np.arange(sh.m_spec)
+    got = oracle.special(sh, q, k, v, rows)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[special_token_ids(sh), h], K[:, h], V[:, h], sh.head_dim ** -0.5)
+        np.testing.assert_allclose(got[:, h], ref, rtol=0, atol=1e-12)
+
+
+def test_special_custom_scale_is_applied():
+    sh = shape(n_special=2)
+    q, k, v, _ = gen.make_inputs(sh)
+    rows = np.arange(sh.m_spec)
+    c = oracle.cfg_of(sh, scale=0.5)
+    out = np.empty((rows.size, sh.n_heads, sh.head_dim))
+    oracle._load().orc_special(oracle.ctypes.byref(c), q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                               rows.astype(np.int64).ctypes.data, rows.size, out.ctypes.data)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    ref = sdpa(Q[special_token_ids(sh), 1], K[:, 1], V[:, 1], 0.5)
+    np.testing.assert_allclose(out[:, 1], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Compressed attention (section "压缩分支": O'_comp = Attention(Q_comp, K_comp, V_comp))
+
+def test_compressed_attention_equals_dense_on_pooled():
+    sh = shape(pool=2)
+    q, k, v, _ = gen.make_inputs(sh)
+    qc, kc, vc = oracle.pool(sh, q), oracle.pool(sh, k), oracle.pool(sh, v)
+    wins = np.arange(sh.n_windows)
+    oc, _, _, _ = oracle.compressed(sh, qc, kc, vc, wins)
+    for h in range(sh.n_heads):
+        ref = sdpa(qc[:, h].astype(np.float64), kc[:, h].astype(np.float64), vc[:, h].astype(np.float64),
+                   sh.head_dim ** -0.5)
+        np.testing.assert_allclose(oc[:, h], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P8 -- top-k over the guide scores S = Q_comp K_comp^T (section "压缩分支"
+# guide-score equation; section "选择分支" TopKSelect), ties to the lower index
+
+def _int_pooled(sh, seed):
+    rng = np.random.default_rng(seed)
+    shp = (sh.n_windows, sh.n_heads, sh.head_dim)
+    return [rng.integers(-3, 4, size=shp).astype(np.float32) for _ in range(3)]
+
+
+@pytest.mark.parametrize("topk", [1, 3, 16])
+def test_topk_equals_full_sort(topk):
+    sh = shape(topk=topk, head_dim=8)
+    qc, kc, vc = _int_pooled(sh, 3)  # integer scores: exact in double, so ties are real ties
+    wins = np.arange(sh.n_windows)
+    _, idx, sc, _ = oracle.compressed(sh, qc, kc, vc, wins)
+    for h in range(sh.n_heads):
+        S = qc[:, h].astype(np.float64) @ kc[:, h].astype(np.float64).T
+        for i in range(sh.n_windows):
+            order = np.lexsort((np.arange(sh.n_windows), -S[i]))  # score desc, then index asc
+            np.testing.assert_array_equal(idx[i, h], order[:topk])
+            np.testing.assert_array_equal(sc[i, h, :topk], S[i, order[:topk]])
+            assert sc[i, h, topk] == S[i, order[topk]]
+
+
+def test_topk_ties_go_to_lower_index():
+    sh = shape(topk=2, head_dim=8)
+    qc, kc, vc = _int_pooled(sh, 4)
+    kc[:] = kc[5]  # every key window identical -> every score tied
+    _, idx, _, _ = oracle.compressed(sh, qc, kc, vc, np.arange(sh.n_windows))
+    assert np.all(idx == np.array([0, 1], np.int32))
+
+
+def test_topk_clamps_and_excludes_context_windows():
+    sh = shape(topk=100, ctx_frames=(1,), n_frames=3)
+    qc, kc, vc = _int_pooled(sh, 5)
+    _, idx, sc, _ = oracle.compressed(sh, qc, kc, vc, np.arange(sh.n_windows))
+    wpf = sh.windows_per_frame
+    ncand = 2 * wpf
+    assert np.all(idx[..., ncand:] == -1)
+    real = idx[..., :ncand]
+    assert np.all((real // wpf) != 1)  # context frame windows are never candidates
+    assert np.all(np.sort(real, axis=-1) == np.concatenate([np.arange(wpf), np.arange(2 * wpf, 3 * wpf)]))
+    assert np.all(np.isnan(sc[..., ncand + 1:]))
+
+
+# ---------------------------------------------------------------------------
+# Selection branch (section "选择分支"; fixed context: section "Speed3R-VGGT 适配")
+
+def _selection_mask(sh, idx_h):
+    """[M_img][M] additive mask of the keys each image query may attend, built from window sets."""
+    wt = window_token_ids(sh)
+    img = image_token_ids(sh)
+    pos = {int(t): r for r, t in enumerate(img)}
+    mask = np.full((sh.m_img, sh.m_tokens), -np.inf)
+    for i in range(sh.n_windows):
+        keys = np.concatenate([wt[j] for j in idx_h[i] if j >= 0] +
+                              [token_grid(sh)[f] for f in sh.ctx_frames])
+        for t in wt[i]:
+            mask[pos[int(t)], keys] = 0.0
+    return mask
+
+
+@pytest.mark.parametrize("ctx", [(), (1,)])
+def test_selection_equals_masked_dense_attention(ctx):
+    sh = shape(n_frames=3, topk=3, ctx_frames=ctx)
+    q, k, v, _ = gen.make_inputs(sh)
+    qc, kc, vc = oracle.pool(sh, q), oracle.pool(sh, k), oracle.pool(sh, v)
+    wins = np.arange(sh.n_windows)
+    _, idx, _, _ = oracle.compressed(sh, qc, kc, vc, wins)
+    osel = oracle.select(sh, q, k, v, wins, idx)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    img = image_token_ids(sh)
+    wt = window_token_ids(sh)
+    pos = {int(t): r for r, t in enumerate(img)}
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[img, h], K[:, h], V[:, h], sh.head_dim ** -0.5, _selection_mask(sh, idx[:, h]))
+        got = np.empty_like(ref)
+        for i in range(sh.n_windows):
+            for qq, t in enumerate(wt[i]):
+                got[pos[int(t)]] = osel[i, qq, h]
+        np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_P2_topk_covering_all_windows_is_dense_image_attention():
+    sh = shape(topk=10 ** 6)
+    q, k, v, _ = gen.make_inputs(sh)
+    wins = np.arange(sh.n_windows)
+    idx = np.tile(np.arange(sh.n_windows, dtype=np.int32), (sh.n_windows, sh.n_heads, 1))
+    osel = oracle.select(sh, q, k, v, wins, idx)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    wt = window_token_ids(sh)
+    img = image_token_ids(sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[wt.reshape(-1), h], K[img, h], V[img, h], sh.head_dim ** -0.5)
+        np.testing.assert_allclose(osel[:, :, h].reshape(-1, sh.head_dim), ref, atol=1e-12)
+
+
+def test_P9_context_every_frame_is_dense_attention_over_all_tokens():
+    sh = shape(n_frames=2, topk=4, ctx_frames=(0, 1))
+    q, k, v, _ = gen.make_inputs(sh)
+    qc, kc, vc = oracle.pool(sh, q), oracle.pool(sh, k), oracle.pool(sh, v)
+    wins = np.arange(sh.n_windows)
+    _, idx, _, _ = oracle.compressed(sh, qc, kc, vc, wins)
+    assert np.all(idx == -1)  # no candidates left
+    osel = oracle.select(sh, q, k, v, wins, idx)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    wt = window_token_ids(sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[wt.reshape(-1), h], K[:, h], V[:, h], sh.head_dim ** -0.5)
+        np.testing.assert_allclose(osel[:, :, h].reshape(-1, sh.head_dim), ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Upsample + gate (section "压缩分支" upsampling; section "门控聚合")
+
+def test_P4_explicit_gates_select_one_branch():
+    sh = shape()
+    q, k, v, wg = gen.make_inputs(sh)
+    wins = np.arange(sh.n_windows)
+    rng = np.random.default_rng(0)
+    oc = rng.standard_normal((sh.n_windows, sh.n_heads, sh.head_dim))
+    osel = rng.standard_normal((sh.n_windows, 4, sh.n_heads, sh.head_dim))
+    g0 = np.zeros((sh.n_windows, 4, sh.n_heads))
+    np.testing.assert_array_equal(oracle.gate_combine(sh, q, None, wins, oc, osel, g0), osel)
+    g1 = np.ones_like(g0)
+    np.testing.assert_array_equal(oracle.gate_combine(sh, q, None, wins, oc, osel, g1),
+                                  np.broadcast_to(oc[:, None], osel.shape))
+    # W_g = 0 gives g = 1/2 exactly: the midpoint
+    mid = oracle.gate_combine(sh, q, np.zeros_like(wg), wins, oc, osel)
+    np.testing.assert_allclose(mid, 0.5 * (oc[:, None] + osel), atol=1e-15)
+
+
+def test_gate_direction_large_logit_picks_compressed_branch():
+    sh = shape()
+    q, _, _, wg = gen.make_inputs(sh)
+    q = np.abs(q)  # q . W_g > 0 everywhere when W_g >= 0 ...
+    wg = np.full_like(wg, 50.0)  # ... and very large, so g = sigmoid(.) ~ 1
+    wins = np.arange(sh.n_windows)
+    rng = np.random.default_rng(1)
+    oc = rng.standard_normal((sh.n_windows, sh.n_heads, sh.head_dim))
+    osel = rng.standard_normal((sh.n_windows, 4, sh.n_heads, sh.head_dim))
+    out = oracle.gate_combine(sh, q, wg, wins, oc, osel)
+    np.testing.assert_allclose(out, np.broadcast_to(oc[:, None], osel.shape), atol=1e-12)
+    out = oracle.gate_combine(sh, q, -wg, wins, oc, osel)
+    np.testing.assert_allclose(out, osel, atol=1e-12)
+
+
+def test_forward_upsample_gate_one_gives_each_token_its_window_output():
+    sh = shape()
+    q, k, v, wg = gen.make_inputs(sh)
+    g1 = np.ones((sh.n_windows, 4, sh.n_heads))
+    res = oracle.forward(sh, q, k, v, wg, gate=g1)
+    qc, kc, vc = oracle.pool(sh, q), oracle.pool(sh, k), oracle.pool(sh, v)
+    O = res["o"].reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    wt = window_token_ids(sh)
+    for h in range(sh.n_heads):
+        comp = sdpa(qc[:, h].astype(np.float64), kc[:, h].astype(np.float64),
+                    vc[:, h].astype(np.float64), sh.head_dim ** -0.5)
+        for i in range(sh.n_windows):
+            np.testing.assert_allclose(O[wt[i], h], np.broadcast_to(comp[i], (4, sh.head_dim)), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P3, P6, P7 -- whole-forward special cases
+
+def test_P3_pool1_all_windows_any_gate_is_dense_image_attention():
+    sh = shape(pool=1, topk=10 ** 6, n_special=2)
+    q, k, v, wg = gen.make_inputs(sh)
+    gate = np.random.default_rng(2).random((sh.n_windows, 1, sh.n_heads))
+    res = oracle.forward(sh, q, k, v, wg, gate=gate)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    O = res["o"].reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    img = image_token_ids(sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[img, h], K[img, h], V[img, h], sh.head_dim ** -0.5)
+        np.testing.assert_allclose(O[img, h], ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("ctx", [(), (0,)])
+def test_P6_constant_values_give_constant_output(ctx):
+    sh = shape(n_frames=3, ctx_frames=ctx, n_special=2)
+    q, k, _, wg = gen.make_inputs(sh)
+    c = np.random.default_rng(3).standard_normal((sh.n_heads, sh.head_dim)).astype(np.float32)
+    v = np.broadcast_to(c, sh.qkv_shape).copy()
+    res = oracle.forward(sh, q, k, v, wg)
+    np.testing.assert_allclose(res["o"], np.broadcast_to(c.astype(np.float64), sh.qkv_shape), atol=1e-12)
+
+
+def test_P7_single_window():
+    sh = shape(n_frames=1, grid_h=4, grid_w=4, pool=4, topk=32, n_special=1)
+    q, k, v, wg = gen.make_inputs(sh)
+    res = oracle.forward(sh, q, k, v, wg)
+    assert sh.n_windows == 1
+    assert res["topk"].tolist() == [[[0] + [-1] * 31] * sh.n_heads]
+    np.testing.assert_allclose(res["oc"][0], res["vc"][0].astype(np.float64), atol=1e-12)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    img = image_token_ids(sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[img, h], K[img, h], V[img, h], sh.head_dim ** -0.5)
+        np.testing.assert_allclose(res["osel"][0, :, h], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# generator sanity (not the method: the inputs' recipe)
+
+def test_generator_is_deterministic_and_standard_normal():
+    a = gen.normal((1 << 18,), F32, 11, 1)
+    b = gen.normal((1 << 18,), F32, 11, 1)
+    np.testing.assert_array_equal(a, b)
+    assert abs(a.mean()) < 0.01 and abs(a.std() - 1) < 0.01
+    c = gen.normal((1000,), F32, 11, 1, offset=500)
+    np.testing.assert_array_equal(c[:500], a[500:1000])
+    assert not np.array_equal(a[:1000], gen.normal((1000,), F32, 11, 2))
+    bf = gen.normal((1000,), BF16, 11, 1)
+    np.testing.assert_allclose(gen.to_f32(bf, BF16), a[:1000], rtol=2 ** -8)
+
+
+def test_clustered_recipe_windows_share_a_centroid():
+    sh = shape(recipe="clustered", pool=4, n_heads=2, head_dim=16)
+    k = gen.to_f32(gen.clustered(sh, 5, 2, 5, 7), F32).astype(np.float64)
+    K = k.reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    wt = window_token_ids(sh)
+    spread = K[wt].std(axis=1)  # within-window spread = the 0.1 noise
+    assert 0.06 < spread.mean() < 0.14
+    assert K[special_token_ids(sh)].std() > 0.7
