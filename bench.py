@@ -1,0 +1,261 @@
+"""GSA-layer benchmark on one MI355X.
+
+One step = one gsa_forward over the whole layer (pooling, special-token
+attention, compressed attention with streaming top-k, selection attention with
+the fused upsample + gate) on seeded synthetic inputs already resident in HBM.
+Default workload: the pi^3-style long sequence, 1000 frames x (36x36 image + 5
+special tokens), 16 heads, d = 64, bf16, s = 4, k = 32.
+
+Prints ONE JSON line.  Besides the throughput it reports, for the dominant
+kernel, a roofline object (algorithmic work per launch / its average launch
+duration from HIP events on its stream), the per-stage times, the dense
+global-attention comparator at the same shape, and the CPU oracle timed on a
+bounded sample of the same workload (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 matrix/vector peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "GSA-layer image tokens/s + % bf16 MFMA peak at 1000 frames x 1296 tok, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="pi3-long", help="workload name (see gen/configs.py)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-windows", type=int, default=64)
+    ap.add_argument("--cpu-special", type=int, default=16)
+    return ap.parse_args()
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_global_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("workload") != workload or rec.get("sources") != kernel_sources_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import sparse_global_attention_amd as gsa
+    from gen.configs import config_by_name
+
+    sh = config_by_name(args.config)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    q, k, v, wg = gen.make_inputs(sh)
+    t_gen = time.time() - t0
+
+    def to_dev(x):
+        if sh.dtype == gen.BF16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    dq, dk, dv, dwg = (to_dev(x) for x in (q, k, v, wg))
+    cfg = gsa.GSAConfig.from_shape(sh)
+    o = torch.empty_like(dq)
+    ws = torch.empty(gsa.gsa_workspace_size(cfg, gsa.GSA_OP_FORWARD), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gsa.gsa_forward(cfg, dq, dk, dv, dwg, o, ws, stream=stream)
+
+    # ---- whole-layer throughput -------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    value = sh.m_img / (ms_step * 1e-3)
+    fl = sh.flops()
+    gsa_flops = fl["special"] + fl["compressed"] + fl["selection"]
+    eff_tflops = gsa_flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if sh.dtype == gen.BF16 else PEAK_F32_TFLOPS
+
+    # ---- per-stage launches (public entry points), HIP events on the same stream ----
+    H, d = sh.n_heads, sh.head_dim
+    shp = (sh.n_windows, H, d)
+    qc, kc, vc = (torch.empty(shp, dtype=dq.dtype, device=dev) for _ in range(3))
+    oc = torch.empty(shp, dtype=torch.float32, device=dev)
+    idx = torch.empty((sh.n_windows, H, sh.topk), dtype=torch.int32, device=dev)
+    osel = torch.empty((sh.m_img, H, d), dtype=torch.float32, device=dev)
+    ws_spec = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_SPECIAL)), dtype=torch.uint8, device=dev)
+    ws_sel = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_SELECT)), dtype=torch.uint8, device=dev)
+    o2 = torch.empty_like(dq)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = max(2, args.steps)
+    st = {}
+    st["pool"] = timed(lambda: gsa.gsa_pool(cfg, dq, dk, dv, qc, kc, vc, stream=stream), reps)
+    st["compressed_topk"] = timed(lambda: gsa.gsa_compressed_attn_topk(cfg, qc, kc, vc, oc, idx, stream=stream), reps)
+    st["special"] = timed(lambda: gsa.gsa_special_attn(cfg, dq, dk, dv, o2, ws_spec, stream=stream), reps)
+    st["select_standalone"] = timed(lambda: gsa.gsa_select_attn(cfg, dq, dk, dv, idx, osel, ws_sel, stream=stream), reps)
+    st["gate_combine"] = timed(lambda: gsa.gsa_gate_combine(cfg, dq, dwg, None, oc, osel, o2, stream=stream), reps)
+
+    # the attention kernels are the heaviest launches; report the larger one's roofline
+    esz = 2 if sh.dtype == gen.BF16 else 4
+    if st["compressed_topk"] >= st["special"]:
+        kname, kms, kflops = "flash_kernel<topk> (compressed attention + streaming top-k)", st["compressed_topk"], fl["compressed"]
+        ktag = "compressed_topk"
+    else:
+        kname, kms, kflops = "flash_kernel<partial> + merge (special-token attention)", st["special"], fl["special"]
+        ktag = "special"
+    achieved = kflops / (kms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(ktag, sh.name),
+                "kernel": kname, "work_per_launch_flop": kflops, "avg_launch_ms": round(kms, 4)}
+
+    # HBM view of the memory-bound steps (algorithmic bytes)
+    pool_bytes = 3 * sh.m_img * H * d * esz + 3 * sh.n_windows * H * d * esz
+    gather_bytes = sh.n_windows * H * sh.topk_eff * sh.pool ** 2 * 2 * d * esz
+
+    detail = {
+        "stage_ms": {k_: round(v_, 4) for k_, v_ in st.items()},
+        "effective_tflops": round(eff_tflops, 2),
+        "frac_bf16_mfma_peak": round(eff_tflops / peak, 4),
+        "gsa_flops": gsa_flops,
+        "flops": fl,
+        "pool_hbm_gbs": round(pool_bytes / (st["pool"] * 1e-3) / 1e9, 1),
+        "pool_frac_hbm": round(pool_bytes / (st["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "select_gather_bytes": gather_bytes,
+        "wall_s_timed_region": round(t_wall, 3),
+        "input_gen_s": round(t_gen, 1),
+        "sources": kernel_sources_hash(),
+    }
+    del ws_spec, ws_sel, o2, osel
+
+    # ---- dense comparator at the same shape --------------------------------------
+    if not args.no_dense:
+        od = torch.empty_like(dq)
+        t_dense = timed(lambda: gsa.gsa_dense_attn(cfg, dq, dk, dv, od, stream=stream), 1)
+        detail["dense_ms"] = round(t_dense, 2)
+        detail["dense_tflops"] = round(fl["dense"] / (t_dense * 1e-3) / 1e12, 2)
+        detail["speedup_vs_dense"] = round(t_dense / ms_step, 2)
+        del od
+
+    # ---- CPU oracle baseline on a bounded sample -----------------------------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(sh, q, k, v, wg, args.cpu_windows, args.cpu_special)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "image tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == gen.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": sh.name, "frames": sh.n_frames, "special_per_frame": sh.n_special,
+                   "grid": [sh.grid_h, sh.grid_w], "heads": H, "head_dim": d, "pool": sh.pool,
+                   "topk": sh.topk, "ctx_frames": list(sh.ctx_frames), "image_tokens": sh.m_img,
+                   "recipe": sh.recipe},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(sh, q, k, v, wg, n_win, n_spec):
+    """The oracle (as it stands) on a bounded sample of the workload, extrapolated to the layer.
+
+    Full pooling of Q/K/V, then every step for n_win sampled query windows (all
+    heads) and the special attention of n_spec sampled special rows (all heads).
+    Layer estimate = pool + (M'/n_win) * window part + (M_spec/n_spec) * special part.
+    """
+    import numpy as np
+
+    import gen
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    wins = gen.sample_windows(sh, n_win)
+    rows = gen.sample_special(sh, n_spec)
+    t0 = time.perf_counter()
+    qc, kc, vc = oracle.pool(sh, q), oracle.pool(sh, k), oracle.pool(sh, v)
+    t_pool = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oc, idx, _, _ = oracle.compressed(sh, qc, kc, vc, wins)
+    osel = oracle.select(sh, q, k, v, wins, idx)
+    oracle.gate_combine(sh, q, wg, wins, oc, osel)
+    t_win = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    if sh.m_spec:
+        oracle.special(sh, q, k, v, rows)
+    t_spec = time.perf_counter() - t0
+    est = t_pool + t_win * sh.n_windows / len(wins) + (t_spec * sh.m_spec / len(rows) if sh.m_spec else 0.0)
+    return {"value": round(sh.m_img / est, 3), "unit": "image tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"full pooling of Q/K/V ({t_pool:.1f} s) + all steps for {len(wins)} of {sh.n_windows} "
+                       f"query windows x {sh.n_heads} heads ({t_win:.1f} s) + special attention for "
+                       f"{len(rows)} of {sh.m_spec} special rows x {sh.n_heads} heads ({t_spec:.1f} s); "
+                       f"linear extrapolation to the layer = {est:.0f} s"),
+            "measured_s": round(t_pool + t_win + t_spec, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * libgsa -- Global Sparse Attention (GSA) forward on AMD Instinct MI355X (gfx950).
+ *
+ * GSA is the sparse replacement for dense global attention introduced by
+ * "Speed3R: Sparse Feed-forward 3D Reconstruction Models" (CVPR 2026,
+ * arXiv 2603.08055).  Citations below name the Paper-Notes page
+ * "Speed3R: Sparse Feed-forward 3D Reconstruction Models" and its sections.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Shapes: N frames, P special tokens per frame, an h x w image-token grid per
+ * frame, T_f = P + h*w tokens per frame, M = N*T_f tokens, M_spec = N*P,
+ * M_img = N*h*w, H heads of dimension d (d must be 64), pool size s (h and w
+ * divisible by s), M' = M_img / s^2 windows, top-k k.
+ *
+ * Layouts (row-major, contiguous, element type = cfg->dtype unless stated):
+ *   q, k, v, o   [N][T_f][H][d]. Token p < P of a frame is special; token
+ *                p >= P is image pixel (y, x) = divmod(p - P, w).
+ *   qc, kc, vc   [M'][H][d]; window j = f*(h/s)*(w/s) + wy*(w/s) + wx
+ *                (frame-major, then window row, then window column).
+ *   oc           float [M'][H][d].
+ *   topk_idx     int32 [M'][H][k], per (window, head) sorted by guide score
+ *                descending, ties to the lower window index; slots past the
+ *                number of candidate windows hold -1.
+ *   topk_score   float [M'][H][k] raw guide scores of those windows (or NULL).
+ *   o_sel        float [M_img][H][d], image token u = f*h*w + y*w + x.
+ *   gate         float [M_img][H].
+ *   wg           [H][d] gate projection W_g (one scalar gate per token and head).
+ *
+ * Ownership: every tensor pointer is a DEVICE pointer owned by the caller and
+ * must be 16-byte aligned; the workspace must be 256-byte aligned.  libgsa
+ * never allocates device memory; gsa_workspace_size states the scratch it
+ * needs.  Outputs must not alias inputs.
+ *
+ * Execution: every call validates its arguments on the host first; on any
+ * validation error it returns that status without touching the device.
+ * Otherwise it enqueues kernels on `stream` (a hipStream_t; NULL = the
+ * default stream) of the current device and returns GSA_OK without
+ * synchronising.  A failed kernel launch returns GSA_ERR_HIP.  Results are
+ * bitwise deterministic for a given configuration and device.  The library
+ * keeps no mutable global state, so calls from several threads are safe.
+ */
+#ifndef GSA_H_
+#define GSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GSA_OK = 0,
+  GSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad k, bad context frame, aliasing */
+  GSA_ERR_SHAPE = 2,       /* h or w not divisible by s, non-positive sizes, size overflow */
+  GSA_ERR_UNSUPPORTED = 3, /* d != 64, s > 8, k > 128, unknown dtype */
+  GSA_ERR_WORKSPACE = 4,   /* workspace smaller than gsa_workspace_size() */
+  GSA_ERR_HIP = 5          /* a HIP launch failed */
+} gsa_status;
+
+typedef enum { GSA_BF16 = 0, GSA_F32 = 1 } gsa_dtype;
+
+typedef enum {
+  GSA_OP_FORWARD = 0, /* gsa_forward */
+  GSA_OP_SPECIAL = 1, /* gsa_special_attn */
+  GSA_OP_SELECT = 2,  /* gsa_select_attn */
+  GSA_OP_DENSE = 3    /* gsa_dense_attn */
+} gsa_op;
+
+#define GSA_MAX_CTX_FRAMES 16
+
+typedef struct {
+  int32_t n_frames;  /* N >= 1 */
+  int32_t n_special; /* P >= 0 (P = 0: no special tokens) */
+  int32_t grid_h;    /* h >= 1 */
+  int32_t grid_w;    /* w >= 1 */
+  int32_t n_heads;   /* H >= 1 */
+  int32_t head_dim;  /* d, must be 64 */
+  int32_t pool;      /* s in [1, 8], divides h and w */
+  int32_t topk;      /* k in [1, 128]; clamped internally to the candidate count */
+  int32_t n_ctx_frames;                   /* number of fixed-context frames, 0..16 */
+  int32_t ctx_frames[GSA_MAX_CTX_FRAMES]; /* distinct frame ids in [0, N) */
+  int32_t ctx_exclude_from_topk;          /* 1: context frames' windows are not top-k candidates */
+  float scale;                            /* softmax scale; 0 means 1/sqrt(d) */
+  int32_t dtype;                          /* gsa_dtype of q/k/v/o/wg/qc/kc/vc */
+} gsa_config;
+
+/* Device scratch (bytes) needed by the entry point `op` for this config. */
+gsa_status gsa_workspace_size(const gsa_config* cfg, gsa_op op, size_t* bytes);
+
+/*
+ * s x s non-overlapping average pooling of the image Q/K/V into qc/kc/vc
+ * (section "压缩分支": Q_comp, K_comp, V_comp in R^{M' x d}, M' = M_img/s^2).
+ * Each pooled value is the float sum of the s^2 window values taken in
+ * row-major order, times 1/s^2, rounded to the dtype (nearest even).
+ */
+gsa_status gsa_pool(const gsa_config* cfg, const void* q, const void* k, const void* v, void* qc,
+                    void* kc, void* vc, void* stream);
+
+/*
+ * Compressed attention fused with a streaming top-k over the guide scores
+ * (section "压缩分支": O'_comp = Attention(Q_comp, K_comp, V_comp) and
+ * S_guide = Q_comp K_comp^T; section "选择分支": TopKSelect of the most
+ * relevant windows; section "高效 Triton Kernel 实现": top-k kept while the
+ * score tiles are on chip, the score matrix is never stored).  Softmax over
+ * all M' windows with the config scale; top-k over the raw scores of the
+ * candidate windows (all windows, minus the context frames' windows when
+ * ctx_exclude_from_topk is set), per head.  Writes oc, topk_idx and, if not
+ * NULL, topk_score.
+ */
+gsa_status gsa_compressed_attn_topk(const gsa_config* cfg, const void* qc, const void* kc,
+                                    const void* vc, float* oc, int32_t* topk_idx,
+                                    float* topk_score, void* stream);
+
+/*
+ * Selection-branch attention (section "选择分支": each image query attends the
+ * full-resolution K/V of its window's top-k windows, the s^2 queries of a
+ * window share one KV set; section "Speed3R-VGGT 适配": plus all T_f tokens
+ * of each fixed-context frame, in one joint softmax).  topk_idx entries < 0
+ * or >= M' are skipped.  Writes o_sel.  Workspace: GSA_OP_SELECT bytes.
+ */
+gsa_status gsa_select_attn(const gsa_config* cfg, const void* q, const void* k, const void* v,
+                           const int32_t* topk_idx, float* o_sel, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Special-token attention (section "全局稀疏注意力（GSA）核心设计":
+ * O_spec = softmax(Q_spec K^T / sqrt(d_k)) V over all M tokens).  Writes the
+ * special rows of o only.  Workspace: GSA_OP_SPECIAL bytes.
+ */
+gsa_status gsa_special_attn(const gsa_config* cfg, const void* q, const void* k, const void* v,
+                            void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Nearest-neighbour upsampling and gated aggregation (section "压缩分支":
+ * O_comp = Upsample(O'_comp); section "门控聚合": g = sigmoid(W_g Q_img),
+ * O_img = g O_comp + (1 - g) O_sel).  If wg is NULL the gate is taken from
+ * `gate` instead (explicit gates, e.g. exactly 0 or 1).  Writes the image
+ * rows of o only.
+ */
+gsa_status gsa_gate_combine(const gsa_config* cfg, const void* q, const void* wg,
+                            const float* gate, const float* oc, const float* o_sel, void* o,
+                            void* stream);
+
+/*
+ * The whole GSA forward: pooling, special attention, compressed attention with
+ * top-k, selection attention with the fused upsample + gate epilogue.  Writes
+ * every row of o.  Workspace: GSA_OP_FORWARD bytes.
+ */
+gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, const void* v,
+                       const void* wg, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dense global attention of all M tokens over all M tokens at the same shape
+ * (the attention GSA replaces; benchmark comparator).  Writes every row of o.
+ */
+gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, const void* v,
+                          void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gsa_status_string(gsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSA_H_ */

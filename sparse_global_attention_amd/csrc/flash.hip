@@ -1,0 +1,538 @@
+// Tiled softmax attention on the gfx950 matrix cores, in three output modes:
+//
+//  * kFlashFinal    dense attention, normalised rows written in the input
+//                   dtype (the dense comparator: all M queries over all M keys);
+//  * kFlashPartial  split-K partials (normalised o and log-sum-exp) merged by
+//                   merge_kernel: the special-token attention of the
+//                   Paper-Notes page "Speed3R: Sparse Feed-forward 3D
+//                   Reconstruction Models", section "全局稀疏注意力（GSA）核心设计"
+//                   (M_spec queries over all M keys), and the fixed-context
+//                   part of the selection branch (section "Speed3R-VGGT 适配");
+//  * kFlashTopk     compressed attention over the pooled windows fused with a
+//                   streaming top-k over the raw guide scores S = Qc Kc^T
+//                   (section "压缩分支" and section "选择分支"; the fused
+//                   top-k-in-the-attention-sweep idea of section
+//                   "高效 Triton Kernel 实现").  S is never written out.
+//
+// Work decomposition: a workgroup of WAVES wavefronts owns 32*WAVES query
+// rows of one head and one key split; each wavefront owns 32 query rows.  Key
+// tiles of 32 keys are staged once per workgroup in LDS (K as rows, V
+// transposed so the PV operand is a contiguous read) and shared by all its
+// waves.  Per tile and wave:
+//   S^T[32 keys x 32 q] = K Q^T       4 x v_mfma_f32_32x32x16_bf16 (K=d=64)
+//   online softmax on S^T             exp2 of log2e-scaled logits, lazy rescale
+//   O^T[64 dv x 32 q] += V^T P^T      4 x v_mfma_f32_32x32x16_bf16
+// Lane l holds query l%32 and 16 of the tile's keys; the other 16 keys of the
+// same query sit in lane l^32.
+//
+// Streaming top-k (kFlashTopk): per query a min-heap of the k best
+// (score, window) pairs lives in LDS, ordered by (score desc, index asc), so
+// its root is the current k-th best.  Keys are swept in ascending index order,
+// so a new key that ties the root's score loses the tie: a score can only
+// enter if it is strictly above the root score tau.  Each tile first compares
+// 4-key group maxima with tau (the maxima are needed for the softmax anyway);
+// only then are single scores tested and appended to a small per-lane buffer
+// in LDS.  Buffers are flushed into the heaps in batches (the two lanes of a
+// query take turns), which keeps the rare insertions from stalling the wave on
+// every tile.
+#include <math.h>
+
+#include "gsa_device.h"
+#include "gsa_kernels.h"
+
+namespace gsa {
+
+constexpr int kKT = 32;              // keys per tile
+constexpr float kLazyRescale = 8.0f; // rescale only when the max grows by > 2^8
+constexpr int kBufCap = 16;          // per-lane top-k candidate buffer (entries)
+
+template <typename T>
+struct Tile {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int KSTRIDE = kHeadDim + VE;  // K row stride in LDS (+16 B: conflict-free b128 reads)
+  static constexpr int VSTRIDE = sizeof(T) == 2 ? kKT + 4 : kKT + 4;  // V^T row stride
+  static constexpr int K_ELEMS = kKT * KSTRIDE;
+  static constexpr int V_ELEMS = kHeadDim * VSTRIDE;
+  static constexpr int BYTES = ((K_ELEMS + V_ELEMS) * (int)sizeof(T) + 15) / 16 * 16;
+};
+
+// ---- matrix-core fragments (32x32 family) ----------------------------------
+template <typename T>
+struct Frag32;
+
+template <>
+struct Frag32<__bf16> {
+  using TL = Tile<__bf16>;
+  struct Q {
+    bf16x8 v[4];
+  };
+  // Q^T operand: lane (q, hf) holds d = 32*hf + 8*ks + [0, 8) for ks = 0..3.
+  __device__ static Q load_q(const __bf16* row, int hf) {
+    Q f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (row) {
+        f.v[ks] = *reinterpret_cast<const bf16x8*>(row + 32 * hf + 8 * ks);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[ks][e] = (__bf16)0.0f;
+      }
+    }
+    return f;
+  }
+  // S^T = K Q^T over d (the same d order on both operands).
+  __device__ static f32x16 qk(const __bf16* kt, int r, int hf, const Q& q) {
+    const __bf16* base = kt + r * TL::KSTRIDE + 32 * hf;
+    bf16x8 a[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(base + 8 * ks);
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) s = mfma32(a[ks], q.v[ks], s);
+    return s;
+  }
+  // O^T += V^T P^T.  The P operand of lane (q, hf) for key group m is its own
+  // S^T elements 8m..8m+7, i.e. keys 16m + 8*(e/4) + 4*hf + e%4; the V^T
+  // operand of lane (dv, hf) reads the same keys for channel dv.
+  __device__ static void pv(const __bf16* vt, int r, int hf, const f32x16& p, f32x16 o[2]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = (__bf16)p[8 * m + e];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const __bf16* row = vt + (32 * n + r) * TL::VSTRIDE + 16 * m + 4 * hf;
+        bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+        bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 8);
+        bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[n] = mfma32(a, b, o[n]);
+      }
+    }
+  }
+};
+
+template <>
+struct Frag32<float> {
+  using TL = Tile<float>;
+  struct Q {
+    float v[32];
+  };
+  // lane (q, hf) holds d = 32*hf + i for i = 0..31; MFMA i contracts that d.
+  __device__ static Q load_q(const float* row, int hf) {
+    Q f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f32x4 x = row ? *reinterpret_cast<const f32x4*>(row + 32 * hf + 4 * i) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f.v[4 * i + e] = x[e];
+    }
+    return f;
+  }
+  __device__ static f32x16 qk(const float* kt, int r, int hf, const Q& q) {
+    const float* base = kt + r * TL::KSTRIDE + 32 * hf;
+    f32x16 s = {};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f32x4 a = *reinterpret_cast<const f32x4*>(base + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mfma32(a[e], q.v[4 * i + e], s);
+    }
+    return s;
+  }
+  // element i of lane (q, hf) is key 8*(i/4) + 4*hf + i%4; one MFMA per i.
+  __device__ static void pv(const float* vt, int r, int hf, const f32x16& p, f32x16 o[2]) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 x = *reinterpret_cast<const f32x4*>(vt + (32 * n + r) * TL::VSTRIDE + 8 * a4 + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[n] = mfma32(x[e], p[4 * a4 + e], o[n]);
+      }
+    }
+  }
+};
+
+// ---- cooperative K/V tile staging ------------------------------------------
+template <typename T, int NT>
+struct TileLoader {
+  using TL = Tile<T>;
+  static constexpr int VE = TL::VE;
+  static constexpr int VPR = kHeadDim / VE;
+  static constexpr int NV = kKT * VPR / NT;
+  static_assert(NV >= 1 && NV * NT == kKT * VPR, "tile must split evenly over the workgroup");
+  uint4 kr[NV], vr[NV];
+
+  __device__ void load(const T* K, const T* V, int64_t stride, int64_t hoff, int64_t key0,
+                       int64_t kend, int tid) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int idx = tid + i * NT;
+      int key = idx / VPR, c = idx % VPR;
+      int64_t kk = key0 + key;
+      if (kk < kend) {
+        kr[i] = ld16(K + kk * stride + hoff + c * VE);
+        vr[i] = ld16(V + kk * stride + hoff + c * VE);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ void store(T* kt, T* vt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int idx = tid + i * NT;
+      int key = idx / VPR, c = idx % VPR;
+      st16(kt + key * TL::KSTRIDE + c * VE, kr[i]);
+      const T* x = reinterpret_cast<const T*>(&vr[i]);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) vt[(c * VE + e) * TL::VSTRIDE + key] = x[e];
+    }
+  }
+};
+
+// ---- streaming top-k helpers ------------------------------------------------
+struct Cand {
+  float s;
+  int j;
+};
+// a ranks below b in the order (score desc, index asc)
+__device__ __forceinline__ bool worse(Cand a, Cand b) { return a.s < b.s || (a.s == b.s && a.j > b.j); }
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Heap element i of query r lives at hp[i*32 + r] (queries interleaved so the
+// lanes of a wave touch consecutive words).  Root = worst of the kept set.
+__device__ void sift_down(Cand* hp, int r, int i, int n, Cand x) {
+  while (true) {
+    int ci = 2 * i + 1;
+    if (ci >= n) break;
+    Cand cc = hp[ci * 32 + r];
+    if (ci + 1 < n) {
+      Cand c2 = hp[(ci + 1) * 32 + r];
+      if (worse(c2, cc)) {
+        cc = c2;
+        ++ci;
+      }
+    }
+    if (worse(cc, x)) {
+      hp[i * 32 + r] = cc;
+      i = ci;
+    } else {
+      break;
+    }
+  }
+  hp[i * 32 + r] = x;
+}
+
+__device__ void heap_insert(Cand* hp, int r, int& n, int K, Cand x) {
+  if (n < K) {
+    int i = n++;
+    while (i > 0) {
+      int pi = (i - 1) >> 1;
+      Cand pc = hp[pi * 32 + r];
+      if (worse(x, pc)) {
+        hp[i * 32 + r] = pc;
+        i = pi;
+      } else {
+        break;
+      }
+    }
+    hp[i * 32 + r] = x;
+  } else if (worse(hp[r], x)) {
+    sift_down(hp, r, 0, K, x);
+  }
+}
+
+struct TopkState {
+  Cand* heap;  // this wave's heaps: [K][32]
+  Cand* buf;   // this wave's buffers: [kBufCap][64]
+  int hsize;   // entries in this lane's query heap (same in both lanes of the query)
+  int cnt;     // entries in this lane's buffer
+  float tau;   // current k-th best score of the query (-inf until the heap is full)
+
+  // Move every buffered candidate into the heaps; the two lanes of a query
+  // take turns because they share its heap.
+  __device__ void flush(int lane, int r, int hf, int K) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (hf == half) {
+        for (int b = 0; b < cnt; ++b) heap_insert(heap, r, hsize, K, buf[b * 64 + lane]);
+      }
+      wave_sync();
+      int other = xor_lane(hsize, 32);
+      if (hf != half) hsize = other;
+    }
+    cnt = 0;
+    tau = hsize >= K ? heap[r].s : -INFINITY;
+  }
+};
+
+__device__ __forceinline__ bool excluded_window(const FlashParams& p, int64_t key) {
+  if (p.n_excl == 0) return false;
+  int64_t f = key / p.wins_per_frame;
+  for (int x = 0; x < p.n_excl; ++x)
+    if (f == p.excl_frames[x]) return true;
+  return false;
+}
+
+// ---- the kernel ---------------------------------------------------------------
+template <typename T, int WAVES, int MODE>
+__global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
+  using TL = Tile<T>;
+  using F = Frag32<T>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  T* kt = reinterpret_cast<T*>(smem);
+  T* vt = kt + TL::K_ELEMS;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 31, hf = lane >> 5;
+
+  constexpr int QW = WAVES * 32;
+  const int64_t n_qt = (p.n_q + QW - 1) / QW;
+  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t qt = w % n_qt;
+  const int64_t hs = w / n_qt;
+  const int h = (int)(hs % p.n_heads);
+  const int split = (int)(hs / p.n_heads);
+
+  const int64_t qrow = qt * QW + wv * 32 + r;
+  const bool qvalid = qrow < p.n_q;
+  const int64_t hoff = (int64_t)h * kHeadDim;
+  const int64_t qtok = (qrow / p.qa) * p.qb + p.qc + qrow % p.qa;
+  const T* K = static_cast<const T*>(p.k);
+  const T* V = static_cast<const T*>(p.v);
+  typename F::Q qf = F::load_q(qvalid ? static_cast<const T*>(p.q) + qtok * p.row_stride + hoff : nullptr, hf);
+
+  f32x16 o[2] = {{}, {}};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float c = p.scale_log2;
+
+  TopkState tk;
+  if constexpr (MODE == kFlashTopk) {
+    Cand* base = reinterpret_cast<Cand*>(smem + TL::BYTES);
+    tk.heap = base + wv * p.topk * 32;
+    tk.buf = base + WAVES * p.topk * 32 + wv * kBufCap * 64;
+    tk.hsize = 0;
+    tk.cnt = 0;
+    tk.tau = -INFINITY;
+  }
+
+  TileLoader<T, WAVES * 64> ld;
+  int ri = p.split_r0[split];
+  const int re = p.split_r0[split + 1];
+  while (ri < re && p.kbeg[ri] >= p.kend[ri]) ++ri;
+  int64_t key0 = 0;
+  if (ri < re) {
+    key0 = p.kbeg[ri];
+    ld.load(K, V, p.row_stride, hoff, key0, p.kend[ri], tid);
+  }
+
+  while (ri < re) {
+    const int64_t cur0 = key0, cur_end = p.kend[ri];
+    int ni = ri;
+    int64_t nk = key0 + kKT;
+    if (nk >= p.kend[ni]) {
+      ++ni;
+      while (ni < re && p.kbeg[ni] >= p.kend[ni]) ++ni;
+      if (ni < re) nk = p.kbeg[ni];
+    }
+    __syncthreads();
+    ld.store(kt, vt, tid);
+    __syncthreads();
+    if (ni < re) ld.load(K, V, p.row_stride, hoff, nk, p.kend[ni], tid);
+
+    f32x16 s = F::qk(kt, r, hf, qf);
+    if (cur0 + kKT > cur_end) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int64_t key = cur0 + 8 * (i / 4) + 4 * hf + (i % 4);
+        if (key >= cur_end) s[i] = -INFINITY;
+      }
+    }
+    float g[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) g[a] = fmaxf(fmaxf(s[4 * a], s[4 * a + 1]), fmaxf(s[4 * a + 2], s[4 * a + 3]));
+    float mx = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
+
+    if constexpr (MODE == kFlashTopk) {
+      if (wave_any(mx > tk.tau)) {
+        int need = 0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) need += g[a] > tk.tau ? 4 : 0;
+        if (wave_any(tk.cnt + need > kBufCap)) tk.flush(lane, r, hf, p.topk);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          if (wave_any(g[a] > tk.tau)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t key = cur0 + 8 * a + 4 * hf + e;
+              if (s[4 * a + e] > tk.tau && !excluded_window(p, key)) {
+                tk.buf[tk.cnt * 64 + lane] = Cand{s[4 * a + e], (int)key};
+                ++tk.cnt;
+              }
+            }
+          }
+        }
+      }
+    }
+
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float mnew = mx * c;
+    const bool need = mnew > m_run + kLazyRescale;
+    if (wave_any(need)) {
+      if (need) {
+        const float alpha = fast_exp2(m_run - mnew);
+        m_run = mnew;
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[n][i] *= alpha;
+      }
+    }
+    f32x16 pw;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      pw[i] = fast_exp2(fmaf(s[i], c, -m_run));
+      psum += pw[i];
+    }
+    l_run += psum;
+    F::pv(vt, r, hf, pw, o);
+
+    ri = ni;
+    key0 = nk;
+  }
+
+  // ---- epilogue ----
+  const float l = l_run + xor_lane(l_run, 32);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (qvalid) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int dv0 = 32 * n + 8 * a + 4 * hf;
+        f32x4 v4 = {o[n][4 * a] * inv, o[n][4 * a + 1] * inv, o[n][4 * a + 2] * inv, o[n][4 * a + 3] * inv};
+        if constexpr (MODE == kFlashFinal) {
+          T* dst = static_cast<T*>(p.o) + qtok * p.row_stride + hoff + dv0;
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 b4 = {(__bf16)v4[0], (__bf16)v4[1], (__bf16)v4[2], (__bf16)v4[3]};
+            *reinterpret_cast<bf16x4*>(dst) = b4;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = v4;
+          }
+        } else if constexpr (MODE == kFlashPartial) {
+          float* dst = p.part_o + ((split * p.n_q + qrow) * p.n_heads + h) * kHeadDim + dv0;
+          *reinterpret_cast<f32x4*>(dst) = v4;
+        } else {
+          float* dst = p.oc + (qrow * p.n_heads + h) * kHeadDim + dv0;
+          *reinterpret_cast<f32x4*>(dst) = v4;
+        }
+      }
+    }
+    if constexpr (MODE == kFlashPartial) {
+      if (hf == 0)
+        p.part_lse[(split * p.n_q + qrow) * p.n_heads + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    }
+  }
+
+  if constexpr (MODE == kFlashTopk) {
+    tk.flush(lane, r, hf, p.topk);
+    const int K = p.topk;
+    if (hf == 0) {
+      // heapsort: repeatedly move the worst kept entry to the back
+      for (int end = tk.hsize - 1; end > 0; --end) {
+        Cand top = tk.heap[r];
+        Cand last = tk.heap[end * 32 + r];
+        tk.heap[end * 32 + r] = top;
+        sift_down(tk.heap, r, 0, end, last);
+      }
+    }
+    wave_sync();
+    if (qvalid) {
+      int32_t* di = p.topk_idx + (qrow * p.n_heads + h) * K;
+      float* ds = p.topk_score ? p.topk_score + (qrow * p.n_heads + h) * K : nullptr;
+      for (int t = hf; t < K; t += 2) {
+        const bool have = t < tk.hsize;
+        const Cand x = have ? tk.heap[t * 32 + r] : Cand{-INFINITY, -1};
+        di[t] = have ? x.j : -1;
+        if (ds) ds[t] = have ? x.s : -INFINITY;
+      }
+    }
+  }
+}
+
+// Combine split partials: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t qh = gid / 16;
+  const int chunk = (int)(gid % 16);
+  if (qh >= p.n_q * p.n_heads) return;
+  const int64_t q = qh / p.n_heads;
+  const int h = (int)(qh % p.n_heads);
+  float mx = -INFINITY;
+  for (int s = 0; s < p.n_splits; ++s) mx = fmaxf(mx, p.part_lse[(s * p.n_q + q) * p.n_heads + h]);
+  float den = 0.0f;
+  f32x4 acc = {0, 0, 0, 0};
+  for (int s = 0; s < p.n_splits; ++s) {
+    const float lse = p.part_lse[(s * p.n_q + q) * p.n_heads + h];
+    const float wgt = lse == -INFINITY ? 0.0f : expf(lse - mx);
+    den += wgt;
+    f32x4 x = *reinterpret_cast<const f32x4*>(p.part_o + ((s * p.n_q + q) * p.n_heads + h) * kHeadDim + 4 * chunk);
+    acc += wgt * x;
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  const int64_t tok = (q / p.qa) * p.qb + p.qc + q % p.qa;
+  T* dst = static_cast<T*>(p.o) + tok * p.row_stride + (int64_t)h * kHeadDim + 4 * chunk;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[e] * inv);
+}
+
+template <typename T, int WAVES, int MODE>
+static hipError_t launch_flash_t(const FlashParams& p, hipStream_t stream) {
+  const int64_t n_qt = (p.n_q + WAVES * 32 - 1) / (WAVES * 32);
+  const int64_t blocks = n_qt * p.n_heads * p.n_splits;
+  if (blocks == 0) return hipSuccess;
+  size_t lds = Tile<T>::BYTES;
+  if (MODE == kFlashTopk) lds += (size_t)WAVES * ((size_t)p.topk * 32 + kBufCap * 64) * sizeof(Cand);
+  const void* fn = reinterpret_cast<const void*>(&flash_kernel<T, WAVES, MODE>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((flash_kernel<T, WAVES, MODE>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_flash_dt(int mode, const FlashParams& p, hipStream_t stream) {
+  if (mode == kFlashFinal) return launch_flash_t<T, 4, kFlashFinal>(p, stream);
+  if (mode == kFlashPartial) return launch_flash_t<T, 4, kFlashPartial>(p, stream);
+  // top-k heaps take WAVES * k * 256 bytes of LDS: fewer waves for larger k
+  if (p.topk <= 32) return launch_flash_t<T, 4, kFlashTopk>(p, stream);
+  if (p.topk <= 64) return launch_flash_t<T, 2, kFlashTopk>(p, stream);
+  return launch_flash_t<T, 1, kFlashTopk>(p, stream);
+}
+
+hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t stream) {
+  return dtype == kBF16 ? launch_flash_dt<__bf16>(mode, p, stream) : launch_flash_dt<float>(mode, p, stream);
+}
+
+hipError_t launch_merge(int dtype, const MergeParams& p, hipStream_t stream) {
+  const int64_t threads = p.n_q * p.n_heads * 16;
+  if (threads == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(merge_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<float>, dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gsa

@@ -1,0 +1,441 @@
+// C ABI of libgsa: argument validation, workspace layout and launch sequences.
+// The operations are those of the Paper-Notes page "Speed3R: Sparse
+// Feed-forward 3D Reconstruction Models" (sections "全局稀疏注意力（GSA）核心设计",
+// "压缩分支", "选择分支", "门控聚合", "Speed3R-VGGT 适配"); see gsa.h for each
+// entry point's contract.
+#include <math.h>
+#include <string.h>
+
+#include "gsa.h"
+#include "gsa_device.h"
+#include "gsa_kernels.h"
+
+using namespace gsa;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kSplitTargetBlocks = 4096;  // special attention: aim for >> 256 CUs of work
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Call {
+  Geometry g;
+  int dtype;
+  int64_t esz;  // bytes per element of q/k/v/o
+  float scale;
+  int topk;
+  int n_ctx;
+  int ctx[GSA_MAX_CTX_FRAMES];
+  int exclude;
+};
+
+gsa_status check_cfg(const gsa_config* c, Call* out) {
+  if (!c) return GSA_ERR_INVALID_ARG;
+  if (c->dtype != GSA_BF16 && c->dtype != GSA_F32) return GSA_ERR_UNSUPPORTED;
+  if (c->n_frames < 1 || c->n_special < 0 || c->grid_h < 1 || c->grid_w < 1 || c->n_heads < 1 || c->pool < 1)
+    return GSA_ERR_SHAPE;
+  if (c->head_dim != kHeadDim) return GSA_ERR_UNSUPPORTED;
+  if (c->pool > 8) return GSA_ERR_UNSUPPORTED;
+  if (c->grid_h % c->pool != 0 || c->grid_w % c->pool != 0) return GSA_ERR_SHAPE;
+  if (c->topk < 1) return GSA_ERR_INVALID_ARG;
+  if (c->topk > 128) return GSA_ERR_UNSUPPORTED;
+  if (c->n_ctx_frames < 0 || c->n_ctx_frames > GSA_MAX_CTX_FRAMES) return GSA_ERR_INVALID_ARG;
+  for (int i = 0; i < c->n_ctx_frames; ++i) {
+    if (c->ctx_frames[i] < 0 || c->ctx_frames[i] >= c->n_frames) return GSA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (c->ctx_frames[j] == c->ctx_frames[i]) return GSA_ERR_INVALID_ARG;
+  }
+  if (c->ctx_exclude_from_topk != 0 && c->ctx_exclude_from_topk != 1) return GSA_ERR_INVALID_ARG;
+  if (!(c->scale >= 0.0f) || isinf(c->scale)) return GSA_ERR_INVALID_ARG;
+
+  Geometry& g = out->g;
+  g.n_frames = c->n_frames;
+  g.n_special = c->n_special;
+  g.grid_h = c->grid_h;
+  g.grid_w = c->grid_w;
+  g.n_heads = c->n_heads;
+  g.pool = c->pool;
+  g.tf = (int64_t)c->n_special + (int64_t)c->grid_h * c->grid_w;
+  g.m_tokens = g.n_frames * g.tf;
+  g.m_spec = g.n_frames * g.n_special;
+  g.m_img = g.n_frames * g.grid_h * g.grid_w;
+  g.wx = g.grid_w / g.pool;
+  g.wpf = (g.grid_h / g.pool) * g.wx;
+  g.n_windows = g.n_frames * g.wpf;
+  g.sb = (g.pool * g.pool + 7) / 8 * 8;
+  // window ids are int32 in topk_idx; keep every element count well inside int64
+  if (g.n_windows > INT32_MAX || g.m_tokens > ((int64_t)1 << 40) / (g.n_heads * kHeadDim)) return GSA_ERR_SHAPE;
+
+  out->dtype = c->dtype;
+  out->esz = c->dtype == GSA_BF16 ? 2 : 4;
+  out->scale = c->scale > 0.0f ? c->scale : 1.0f / sqrtf((float)kHeadDim);
+  out->topk = c->topk;
+  out->n_ctx = c->n_ctx_frames;
+  for (int i = 0; i < c->n_ctx_frames; ++i) out->ctx[i] = c->ctx_frames[i];
+  out->exclude = c->ctx_exclude_from_topk;
+  return GSA_OK;
+}
+
+bool ptr_ok(const void* p) { return p != nullptr && ((uintptr_t)p & 15) == 0; }
+
+// ---- workspace layout ----------------------------------------------------------
+struct Plan {
+  int n_split;  // special-attention key splits
+  int64_t qc, kc, vc, oc, topk, kblk, vblk, spec_o, spec_lse, ctx_o, ctx_lse, total;
+};
+
+int special_splits(const Call& c) {
+  const Geometry& g = c.g;
+  if (g.m_spec == 0) return 1;
+  const int64_t per_split = g.n_heads * ((g.m_spec + 127) / 128);
+  int64_t n = (kSplitTargetBlocks + per_split - 1) / per_split;
+  const int64_t max_by_keys = (g.m_tokens + 4 * 32 - 1) / (4 * 32);  // >= 4 key tiles per split
+  if (n > max_by_keys) n = max_by_keys;
+  if (n > kMaxRanges) n = kMaxRanges;
+  return n < 1 ? 1 : (int)n;
+}
+
+Plan make_plan(const Call& c, gsa_op op) {
+  const Geometry& g = c.g;
+  Plan p;
+  memset(&p, 0, sizeof(p));
+  p.n_split = special_splits(c);
+  const int64_t pooled = g.n_windows * g.n_heads * kHeadDim * c.esz;
+  const int64_t blk = g.n_windows * g.n_heads * g.sb * kHeadDim * c.esz;
+  const int64_t spec_o = (int64_t)p.n_split * g.m_spec * g.n_heads * kHeadDim * 4;
+  const int64_t spec_lse = (int64_t)p.n_split * g.m_spec * g.n_heads * 4;
+  const int64_t ctx_o = c.n_ctx ? g.m_img * g.n_heads * kHeadDim * 4 : 0;
+  const int64_t ctx_lse = c.n_ctx ? g.m_img * g.n_heads * 4 : 0;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  if (op == GSA_OP_FORWARD) {
+    p.qc = take(pooled);
+    p.kc = take(pooled);
+    p.vc = take(pooled);
+    p.oc = take(g.n_windows * g.n_heads * kHeadDim * 4);
+    p.topk = take(g.n_windows * g.n_heads * (int64_t)c.topk * 4);
+  }
+  if (op == GSA_OP_FORWARD || op == GSA_OP_SELECT) {
+    p.kblk = take(blk);
+    p.vblk = take(blk);
+    p.ctx_o = take(ctx_o);
+    p.ctx_lse = take(ctx_lse);
+  }
+  if (op == GSA_OP_FORWARD || op == GSA_OP_SPECIAL) {
+    p.spec_o = take(spec_o);
+    p.spec_lse = take(spec_lse);
+  }
+  p.total = off;
+  return p;
+}
+
+gsa_status check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
+  if (pl.total == 0) return GSA_OK;
+  if (ws == nullptr || ((uintptr_t)ws & (kAlign - 1)) != 0) return GSA_ERR_INVALID_ARG;
+  if ((int64_t)ws_bytes < pl.total) return GSA_ERR_WORKSPACE;
+  return GSA_OK;
+}
+
+char* at(void* ws, int64_t off) { return static_cast<char*>(ws) + off; }
+
+gsa_status hip_status(hipError_t e) { return e == hipSuccess ? GSA_OK : GSA_ERR_HIP; }
+
+// ---- launch sequences --------------------------------------------------------------
+FlashParams flash_base(const Call& c, const void* q, const void* k, const void* v) {
+  FlashParams f;
+  memset(&f, 0, sizeof(f));
+  f.q = q;
+  f.k = k;
+  f.v = v;
+  f.row_stride = c.g.n_heads * kHeadDim;
+  f.n_heads = (int)c.g.n_heads;
+  f.scale_log2 = c.scale * kLog2e;
+  return f;
+}
+
+void set_rows_identity(FlashParams& f, int64_t n) {
+  f.n_q = n;
+  f.qa = n > 0 ? n : 1;
+  f.qb = 0;
+  f.qc = 0;
+}
+
+hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void* k, const void* v, void* o,
+                       void* ws, hipStream_t st) {
+  const Geometry& g = c.g;
+  if (g.m_spec == 0) return hipSuccess;
+  FlashParams f = flash_base(c, q, k, v);
+  f.n_q = g.m_spec;
+  f.qa = g.n_special;
+  f.qb = g.tf;
+  f.qc = 0;
+  // even split of the M keys into n_split ranges (multiples of 32 keys)
+  const int ns = pl.n_split;
+  const int64_t tiles = (g.m_tokens + 31) / 32;
+  f.n_splits = ns;
+  for (int s = 0; s < ns; ++s) {
+    f.split_r0[s] = s;
+    f.kbeg[s] = tiles * s / ns * 32;
+    f.kend[s] = s + 1 == ns ? g.m_tokens : tiles * (s + 1) / ns * 32;
+  }
+  f.split_r0[ns] = ns;
+  f.part_o = reinterpret_cast<float*>(at(ws, pl.spec_o));
+  f.part_lse = reinterpret_cast<float*>(at(ws, pl.spec_lse));
+  hipError_t e = launch_flash(c.dtype, kFlashPartial, f, st);
+  if (e != hipSuccess) return e;
+  MergeParams m;
+  m.part_o = f.part_o;
+  m.part_lse = f.part_lse;
+  m.n_splits = ns;
+  m.n_q = g.m_spec;
+  m.qa = g.n_special;
+  m.qb = g.tf;
+  m.qc = 0;
+  m.n_heads = (int)g.n_heads;
+  m.row_stride = g.n_heads * kHeadDim;
+  m.o = o;
+  return launch_merge(c.dtype, m, st);
+}
+
+hipError_t run_compressed(const Call& c, const void* qc, const void* kc, const void* vc, float* oc, int32_t* idx,
+                          float* score, hipStream_t st) {
+  const Geometry& g = c.g;
+  FlashParams f = flash_base(c, qc, kc, vc);
+  set_rows_identity(f, g.n_windows);
+  f.n_splits = 1;
+  f.split_r0[0] = 0;
+  f.split_r0[1] = 1;
+  f.kbeg[0] = 0;
+  f.kend[0] = g.n_windows;
+  f.oc = oc;
+  f.topk_idx = idx;
+  f.topk_score = score;
+  f.topk = c.topk;
+  f.wins_per_frame = g.wpf;
+  f.n_excl = c.exclude ? c.n_ctx : 0;
+  for (int i = 0; i < f.n_excl; ++i) f.excl_frames[i] = c.ctx[i];
+  return launch_flash(c.dtype, kFlashTopk, f, st);
+}
+
+// Context frames' part of the selection softmax: image queries over all T_f tokens of each context frame.
+hipError_t run_context(const Call& c, const Plan& pl, const void* q, const void* k, const void* v, void* ws,
+                       hipStream_t st) {
+  const Geometry& g = c.g;
+  FlashParams f = flash_base(c, q, k, v);
+  f.n_q = g.m_img;
+  f.qa = g.grid_h * g.grid_w;
+  f.qb = g.tf;
+  f.qc = g.n_special;
+  f.n_splits = 1;
+  f.split_r0[0] = 0;
+  f.split_r0[1] = c.n_ctx;
+  for (int i = 0; i < c.n_ctx; ++i) {
+    f.kbeg[i] = (int64_t)c.ctx[i] * g.tf;
+    f.kend[i] = f.kbeg[i] + g.tf;
+  }
+  f.part_o = reinterpret_cast<float*>(at(ws, pl.ctx_o));
+  f.part_lse = reinterpret_cast<float*>(at(ws, pl.ctx_lse));
+  return launch_flash(c.dtype, kFlashPartial, f, st);
+}
+
+PoolParams pool_base(const Call& c) {
+  PoolParams p;
+  memset(&p, 0, sizeof(p));
+  p.g = c.g;
+  p.inv_area = 1.0f / (float)(c.g.pool * c.g.pool);
+  return p;
+}
+
+SelectParams select_base(const Call& c, const Plan& pl, const void* q, const int32_t* idx, void* ws) {
+  SelectParams s;
+  memset(&s, 0, sizeof(s));
+  s.q = q;
+  s.kblk = at(ws, pl.kblk);
+  s.vblk = at(ws, pl.vblk);
+  s.topk_idx = idx;
+  s.topk = c.topk;
+  s.g = c.g;
+  s.scale_log2 = c.scale * kLog2e;
+  if (c.n_ctx) {
+    s.ctx_o = reinterpret_cast<const float*>(at(ws, pl.ctx_o));
+    s.ctx_lse = reinterpret_cast<const float*>(at(ws, pl.ctx_lse));
+  }
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gsa_status_string(gsa_status s) {
+  switch (s) {
+    case GSA_OK: return "GSA_OK";
+    case GSA_ERR_INVALID_ARG: return "GSA_ERR_INVALID_ARG: null, misaligned or aliasing pointer, or invalid argument value";
+    case GSA_ERR_SHAPE: return "GSA_ERR_SHAPE: grid not divisible by the pool size, non-positive or oversized shape";
+    case GSA_ERR_UNSUPPORTED: return "GSA_ERR_UNSUPPORTED: head_dim != 64, pool > 8, topk > 128 or unknown dtype";
+    case GSA_ERR_WORKSPACE: return "GSA_ERR_WORKSPACE: workspace smaller than gsa_workspace_size()";
+    case GSA_ERR_HIP: return "GSA_ERR_HIP: a HIP kernel launch failed";
+  }
+  return "unknown gsa_status";
+}
+
+gsa_status gsa_workspace_size(const gsa_config* cfg, gsa_op op, size_t* bytes) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!bytes) return GSA_ERR_INVALID_ARG;
+  if (op < GSA_OP_FORWARD || op > GSA_OP_DENSE) return GSA_ERR_INVALID_ARG;
+  *bytes = (size_t)make_plan(c, op).total;
+  return GSA_OK;
+}
+
+gsa_status gsa_pool(const gsa_config* cfg, const void* q, const void* k, const void* v, void* qc, void* kc,
+                    void* vc, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(qc) || !ptr_ok(kc) || !ptr_ok(vc)) return GSA_ERR_INVALID_ARG;
+  PoolParams p = pool_base(c);
+  p.src[0] = q;
+  p.src[1] = k;
+  p.src[2] = v;
+  p.dst[0] = qc;
+  p.dst[1] = kc;
+  p.dst[2] = vc;
+  p.first_tensor = 0;
+  return hip_status(launch_pool(c.dtype, p, 3, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_compressed_attn_topk(const gsa_config* cfg, const void* qc, const void* kc, const void* vc, float* oc,
+                                    int32_t* topk_idx, float* topk_score, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(qc) || !ptr_ok(kc) || !ptr_ok(vc) || !ptr_ok(oc) || !ptr_ok(topk_idx)) return GSA_ERR_INVALID_ARG;
+  if (topk_score && !ptr_ok(topk_score)) return GSA_ERR_INVALID_ARG;
+  return hip_status(run_compressed(c, qc, kc, vc, oc, topk_idx, topk_score, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_select_attn(const gsa_config* cfg, const void* q, const void* k, const void* v,
+                           const int32_t* topk_idx, float* o_sel, void* ws, size_t ws_bytes, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(topk_idx) || !ptr_ok(o_sel)) return GSA_ERR_INVALID_ARG;
+  Plan pl = make_plan(c, GSA_OP_SELECT);
+  if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  PoolParams pp = pool_base(c);
+  pp.src[1] = k;
+  pp.src[2] = v;
+  pp.kblk = at(ws, pl.kblk);
+  pp.vblk = at(ws, pl.vblk);
+  pp.first_tensor = 1;
+  hipError_t e = launch_pool(c.dtype, pp, 2, st);
+  if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
+  if (e != hipSuccess) return GSA_ERR_HIP;
+  SelectParams sp = select_base(c, pl, q, topk_idx, ws);
+  sp.osel = o_sel;
+  return hip_status(launch_select(c.dtype, sp, st));
+}
+
+gsa_status gsa_special_attn(const gsa_config* cfg, const void* q, const void* k, const void* v, void* o, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v) return GSA_ERR_INVALID_ARG;
+  Plan pl = make_plan(c, GSA_OP_SPECIAL);
+  if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
+  return hip_status(run_special(c, pl, q, k, v, o, ws, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_gate_combine(const gsa_config* cfg, const void* q, const void* wg, const float* gate, const float* oc,
+                            const float* o_sel, void* o, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(oc) || !ptr_ok(o_sel) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
+  if (wg == nullptr && gate == nullptr) return GSA_ERR_INVALID_ARG;
+  if ((wg && !ptr_ok(wg)) || (!wg && !ptr_ok(gate))) return GSA_ERR_INVALID_ARG;
+  if (o == q) return GSA_ERR_INVALID_ARG;
+  CombineParams p;
+  p.q = q;
+  p.wg = wg;
+  p.gate = gate;
+  p.oc = oc;
+  p.osel = o_sel;
+  p.o = o;
+  p.g = c.g;
+  return hip_status(launch_combine(c.dtype, p, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg, void* o,
+                       void* ws, size_t ws_bytes, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(wg) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v) return GSA_ERR_INVALID_ARG;
+  Plan pl = make_plan(c, GSA_OP_FORWARD);
+  if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // 1. pooling of Q/K/V plus the blocked K / transposed-V copies for the gather
+  PoolParams pp = pool_base(c);
+  pp.src[0] = q;
+  pp.src[1] = k;
+  pp.src[2] = v;
+  pp.dst[0] = at(ws, pl.qc);
+  pp.dst[1] = at(ws, pl.kc);
+  pp.dst[2] = at(ws, pl.vc);
+  pp.kblk = at(ws, pl.kblk);
+  pp.vblk = at(ws, pl.vblk);
+  pp.first_tensor = 0;
+  hipError_t e = launch_pool(c.dtype, pp, 3, st);
+  // 2. special tokens over all tokens
+  if (e == hipSuccess) e = run_special(c, pl, q, k, v, o, ws, st);
+  // 3. compressed attention + top-k
+  float* oc = reinterpret_cast<float*>(at(ws, pl.oc));
+  int32_t* idx = reinterpret_cast<int32_t*>(at(ws, pl.topk));
+  if (e == hipSuccess) e = run_compressed(c, pp.dst[0], pp.dst[1], pp.dst[2], oc, idx, nullptr, st);
+  // 4. fixed-context partial
+  if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
+  // 5. selection + upsample + gate
+  if (e == hipSuccess) {
+    SelectParams sp = select_base(c, pl, q, idx, ws);
+    sp.wg = wg;
+    sp.oc = oc;
+    sp.o = o;
+    e = launch_select(c.dtype, sp, st);
+  }
+  return hip_status(e);
+}
+
+gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, const void* v, void* o, void* ws,
+                          size_t ws_bytes, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  (void)ws;
+  (void)ws_bytes;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v) return GSA_ERR_INVALID_ARG;
+  FlashParams f = flash_base(c, q, k, v);
+  set_rows_identity(f, c.g.m_tokens);
+  f.n_splits = 1;
+  f.split_r0[0] = 0;
+  f.split_r0[1] = 1;
+  f.kbeg[0] = 0;
+  f.kend[0] = c.g.m_tokens;
+  f.o = o;
+  return hip_status(launch_flash(c.dtype, kFlashFinal, f, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Kernel parameter blocks and launchers of libgsa (host and device visible).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gsa {
+
+enum Dtype { kBF16 = 0, kF32 = 1 };
+
+// Token / window geometry of one GSA call (derived from gsa_config).
+struct Geometry {
+  int64_t n_frames, n_special, grid_h, grid_w, n_heads, pool;
+  int64_t tf;         // tokens per frame, P + h*w
+  int64_t m_tokens;   // N * tf
+  int64_t m_spec;     // N * P
+  int64_t m_img;      // N * h * w
+  int64_t wx;         // windows per window-row, w / s
+  int64_t wpf;        // windows per frame
+  int64_t n_windows;  // M'
+  int64_t sb;         // key slots per window in the blocked K/V copies: s*s rounded up to 8
+};
+
+// Token row of the kk-th pixel (row-major inside the window) of window j.
+__host__ __device__ __forceinline__ int64_t window_token(const Geometry& g, int64_t j, int64_t kk) {
+  int64_t f = j / g.wpf, r = j - f * g.wpf;
+  int64_t wy = r / g.wx, wxx = r - wy * g.wx;
+  int64_t dy = kk / g.pool, dx = kk - dy * g.pool;
+  return f * g.tf + g.n_special + (wy * g.pool + dy) * g.grid_w + wxx * g.pool + dx;
+}
+// Image-token index u = f*h*w + y*w + x of the kk-th pixel of window j.
+__host__ __device__ __forceinline__ int64_t window_image_index(const Geometry& g, int64_t j, int64_t kk) {
+  int64_t f = j / g.wpf, r = j - f * g.wpf;
+  int64_t wy = r / g.wx, wxx = r - wy * g.wx;
+  int64_t dy = kk / g.pool, dx = kk - dy * g.pool;
+  return (f * g.grid_h + wy * g.pool + dy) * g.grid_w + wxx * g.pool + dx;
+}
+
+// ---- pooling (+ optional blocked K / transposed-V copies) -------------------
+struct PoolParams {
+  const void* src[3];  // q, k, v in the token layout
+  void* dst[3];        // pooled [M'][H][d] (an entry may be null: no mean written)
+  void* kblk;          // optional [M'][H][sb][d] copy of K, window-local key order
+  void* vblk;          // optional [M'][H][d][sb] transposed copy of V
+  Geometry g;
+  float inv_area;      // 1.0f / (s*s)
+  int first_tensor;    // grid.y enumerates tensors first_tensor .. first_tensor+grid.y-1
+};
+hipError_t launch_pool(int dtype, const PoolParams& p, int n_tensors, hipStream_t stream);
+
+// ---- tiled flash attention (special / dense / context / compressed+top-k) ----
+constexpr int kMaxRanges = 64;
+constexpr int kMaxExcl = 16;
+enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashTopk = 2 };
+
+struct FlashParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t row_stride;  // elements between consecutive rows of q/k/v (H*d)
+  int n_heads;
+  // query rows r in [0, n_q) map to token rows (r / qa) * qb + qc + r % qa
+  int64_t n_q, qa, qb, qc;
+  // key ranges; split s covers ranges [split_r0[s], split_r0[s+1]) in order
+  int n_splits;
+  int split_r0[kMaxRanges + 1];
+  int64_t kbeg[kMaxRanges], kend[kMaxRanges];
+  float scale_log2;  // softmax scale * log2(e)
+  // kFlashFinal: normalised output in the input dtype at rows token(r) of o
+  void* o;
+  // kFlashPartial: part_o [split][n_q][H][d] (normalised), part_lse [split][n_q][H] (natural log)
+  float* part_o;
+  float* part_lse;
+  // kFlashTopk: oc [n_q][H][d] fp32, topk_idx/topk_score [n_q][H][topk]
+  float* oc;
+  int32_t* topk_idx;
+  float* topk_score;
+  int topk;
+  int64_t wins_per_frame;
+  int n_excl;                 // frames whose windows are not top-k candidates
+  int excl_frames[kMaxExcl];
+};
+hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t stream);
+
+// Combine split partials into the final rows of o (input dtype).
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  int n_splits;
+  int64_t n_q, qa, qb, qc;
+  int n_heads;
+  int64_t row_stride;
+  void* o;
+};
+hipError_t launch_merge(int dtype, const MergeParams& p, hipStream_t stream);
+
+// ---- selection attention over gathered top-k windows ------------------------
+struct SelectParams {
+  const void* q;        // token layout
+  const void* kblk;     // [M'][H][sb][d]
+  const void* vblk;     // [M'][H][d][sb]
+  const int32_t* topk_idx;  // [M'][H][topk]
+  int topk;
+  Geometry g;
+  float scale_log2;
+  const float* ctx_o;   // optional context partial [M_img][H][d] (normalised)
+  const float* ctx_lse; // and its log-sum-exp [M_img][H]
+  float* osel;          // standalone output [M_img][H][d]
+  const void* wg;       // fused epilogue: gate projection [H][d]
+  const float* oc;      // fused epilogue: compressed output [M'][H][d]
+  void* o;              // fused epilogue: output rows in the token layout
+};
+hipError_t launch_select(int dtype, const SelectParams& p, hipStream_t stream);
+
+// ---- standalone upsample + gate + blend ----------------------------------------
+struct CombineParams {
+  const void* q;
+  const void* wg;      // [H][d] or null
+  const float* gate;   // [M_img][H], used when wg is null
+  const float* oc;     // [M'][H][d]
+  const float* osel;   // [M_img][H][d]
+  void* o;
+  Geometry g;
+};
+hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t stream);
+
+}  // namespace gsa

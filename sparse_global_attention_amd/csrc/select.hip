@@ -1,0 +1,349 @@
+// Selection-branch attention and the upsample + gate epilogue.
+//
+// Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models":
+//  * section "选择分支": every image query attends the full-resolution K/V of
+//    its window's top-k windows; the s^2 queries of one window share one KV
+//    set, so one wavefront serves one (window, head) and gathers each selected
+//    window once;
+//  * section "Speed3R-VGGT 适配": optional fixed context (all tokens of the
+//    reference frames) joins the same softmax; its part is computed by the
+//    dense flash kernel as a partial (o, lse) and merged here;
+//  * section "压缩分支" (nearest-neighbour upsampling) and section "门控聚合"
+//    (g = sigmoid(W_g q), O = g O_comp + (1 - g) O_sel): fused epilogue.
+//
+// Gather-bound.  The K/V of a selected (window, head) are read from two
+// contiguous blocks written by the pooling pass -- K rows [sb][d] and V
+// transposed [d][sb] -- so every lane issues 16-byte loads that land directly
+// in matrix-core operand layout (no LDS, no barriers; waves are independent).
+// A chunk is 32 key slots (two windows at s = 4); the next chunk's loads are
+// issued before the current chunk's matrix-core work.
+//   S^T[32 slots x 16 q] : 2 tiles x 2 x v_mfma_f32_16x16x32_bf16 (K = d)
+//   O^T[64 dv x 16 q]   += V^T P^T : 4 x v_mfma_f32_16x16x32_bf16 (K = 32 slots)
+// Lane l = 16 g + ql holds query ql and slots 8g..8g+7 of the chunk.
+#include <math.h>
+
+#include "gsa_device.h"
+#include "gsa_kernels.h"
+
+namespace gsa {
+
+template <typename T>
+struct SelChunk {
+  static constexpr int VE = 16 / sizeof(T);
+  static constexpr int KV = 16 / VE;  // 16-byte loads per 16 channels of a K row
+  static constexpr int VV = 8 / VE;   // 16-byte loads per 8 slots of a V^T row
+  uint4 k[2][KV];
+  uint4 v[4][VV];
+  int jv;    // window of this lane's 8 S^T slots (-1: none)
+  int kkv0;  // window-local key of the first of them
+};
+
+template <typename T>
+struct Frag16;
+
+template <>
+struct Frag16<__bf16> {
+  struct Q {
+    bf16x8 v[2];
+  };
+  // lane (q, g) holds d = 16 g + 8 ks + [0, 8)
+  __device__ static Q load_q(const __bf16* row, int g) {
+    Q f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (row) {
+        f.v[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * g + 8 * ks);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.v[ks][e] = (__bf16)0.0f;
+      }
+    }
+    return f;
+  }
+  __device__ static float q_dot(const Q& f, const __bf16* w, int g) {
+    float z = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z += (float)f.v[ks][e] * (float)w[16 * g + 8 * ks + e];
+    return z;
+  }
+  __device__ static f32x4 qk(const uint4 (&k)[2], const Q& q) {
+    f32x4 s = {0, 0, 0, 0};
+    s = mfma16(__builtin_bit_cast(bf16x8, k[0]), q.v[0], s);
+    s = mfma16(__builtin_bit_cast(bf16x8, k[1]), q.v[1], s);
+    return s;
+  }
+  __device__ static void pv(const uint4 (&v)[4][1], const f32x4& p0, const f32x4& p1, f32x4 o[4]) {
+    bf16x8 b = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],
+                (__bf16)p1[0], (__bf16)p1[1], (__bf16)p1[2], (__bf16)p1[3]};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) o[m] = mfma16(__builtin_bit_cast(bf16x8, v[m][0]), b, o[m]);
+  }
+};
+
+template <>
+struct Frag16<float> {
+  struct Q {
+    float v[16];
+  };
+  // lane (q, g) holds d = 16 g + i; MFMA i contracts that d.
+  __device__ static Q load_q(const float* row, int g) {
+    Q f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 x = row ? *reinterpret_cast<const f32x4*>(row + 16 * g + 4 * i) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f.v[4 * i + e] = x[e];
+    }
+    return f;
+  }
+  __device__ static float q_dot(const Q& f, const float* w, int g) {
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z += f.v[i] * w[16 * g + i];
+    return z;
+  }
+  __device__ static f32x4 qk(const uint4 (&k)[4], const Q& q) {
+    f32x4 s = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 a = __builtin_bit_cast(f32x4, k[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = mfma16(a[e], q.v[4 * i + e], s);
+    }
+    return s;
+  }
+  // slot 8g + 4 tau + e <-> S_tau[e] (B) and v element 4 tau + e (A)
+  __device__ static void pv(const uint4 (&v)[4][2], const f32x4& p0, const f32x4& p1, f32x4 o[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f32x4 lo = __builtin_bit_cast(f32x4, v[m][0]);
+      f32x4 hi = __builtin_bit_cast(f32x4, v[m][1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[m] = mfma16(lo[e], p0[e], o[m]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[m] = mfma16(hi[e], p1[e], o[m]);
+    }
+  }
+};
+
+// Window id of top-k entry t, from the two registers holding entries lane and
+// lane+64.  Entries past k, negative or not below M' read as -1 (skipped).
+__device__ __forceinline__ int topk_entry(int tr0, int tr1, int t, int K, int64_t n_windows) {
+  int a = __builtin_amdgcn_ds_bpermute((t & 63) << 2, tr0);
+  int b = __builtin_amdgcn_ds_bpermute((t & 63) << 2, tr1);
+  int j = t < 64 ? a : b;
+  return (t >= K || j < 0 || j >= n_windows) ? -1 : j;
+}
+
+template <typename T>
+__device__ __forceinline__ void load_chunk(SelChunk<T>& ch, const SelectParams& p, int64_t h, int c, int ql,
+                                           int g, int tr0, int tr1) {
+  using C = SelChunk<T>;
+  const int64_t sb = p.g.sb, H = p.g.n_heads;
+  const T* kblk = static_cast<const T*>(p.kblk);
+  const T* vblk = static_cast<const T*>(p.vblk);
+  // K operand: A-row ql of tile tau is slot 8*(ql/4) + 4*tau + ql%4 of the chunk
+  const int64_t ga = (int64_t)c * 32 + 8 * (ql >> 2);
+  const int ja = topk_entry(tr0, tr1, (int)(ga / sb), p.topk, p.g.n_windows);
+  const int64_t kka = ga % sb + (ql & 3);
+  const T* kb = kblk + (((int64_t)(ja < 0 ? 0 : ja) * H + h) * sb + kka) * kHeadDim + 16 * g;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int x = 0; x < C::KV; ++x) ch.k[tau][x] = ld16(kb + 4 * tau * kHeadDim + x * C::VE);
+  // V^T operand and S^T rows of this lane: slots 8g .. 8g+7 of the chunk
+  const int64_t gv = (int64_t)c * 32 + 8 * g;
+  ch.jv = topk_entry(tr0, tr1, (int)(gv / sb), p.topk, p.g.n_windows);
+  ch.kkv0 = (int)(gv % sb);
+  const T* vb = vblk + ((int64_t)(ch.jv < 0 ? 0 : ch.jv) * H + h) * kHeadDim * sb + ch.kkv0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int x = 0; x < C::VV; ++x) ch.v[m][x] = ld16(vb + (16 * m + ql) * sb + x * C::VE);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
+  using F = Frag16<T>;
+  const Geometry& geo = p.g;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int ql = lane & 15, g = lane >> 4;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+  if (item >= geo.n_windows * geo.n_heads) return;
+  const int64_t win = item / geo.n_heads;
+  const int64_t h = item % geo.n_heads;
+  const int64_t H = geo.n_heads;
+  const int s2 = (int)(geo.pool * geo.pool);
+  const int K = p.topk;
+  const float c = p.scale_log2;
+
+  const int32_t* trow = p.topk_idx + item * K;
+  const int tr0 = lane < K ? trow[lane] : -1;
+  const int tr1 = lane + 64 < K ? trow[lane + 64] : -1;
+  const int n_chunks = (int)((K * geo.sb + 31) / 32);
+  const int n_sub = (s2 + 15) / 16;
+
+  for (int qs = 0; qs < n_sub; ++qs) {
+    const int kq = qs * 16 + ql;  // window-local query index
+    const bool qvalid = kq < s2;
+    const int64_t tok = window_token(geo, win, qvalid ? kq : 0);
+    const T* qrow = static_cast<const T*>(p.q) + (tok * H + h) * kHeadDim;
+    typename F::Q qf = F::load_q(qvalid ? qrow : nullptr, g);
+
+    f32x4 o[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    SelChunk<T> cur, nxt;
+    if (n_chunks > 0) load_chunk<T>(cur, p, h, 0, ql, g, tr0, tr1);
+    for (int ci = 0; ci < n_chunks; ++ci) {
+      if (ci + 1 < n_chunks) load_chunk<T>(nxt, p, h, ci + 1, ql, g, tr0, tr1);
+      f32x4 s0 = F::qk(cur.k[0], qf);
+      f32x4 s1 = F::qk(cur.k[1], qf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool v0 = cur.jv >= 0 && cur.kkv0 + e < s2;
+        const bool v1 = cur.jv >= 0 && cur.kkv0 + 4 + e < s2;
+        if (!v0) s0[e] = -INFINITY;
+        if (!v1) s1[e] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                       fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+      mx = fmaxf(mx, xor_lane(mx, 16));
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      const float mnew = mx * c;
+      if (mnew > m_run) {  // few chunks per window: rescale eagerly
+        const float alpha = fast_exp2(m_run - mnew);
+        m_run = mnew;
+        l_run *= alpha;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) o[m] *= alpha;
+      }
+      f32x4 p0, p1;
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p0[e] = m_run == -INFINITY ? 0.0f : fast_exp2(fmaf(s0[e], c, -m_run));
+        p1[e] = m_run == -INFINITY ? 0.0f : fast_exp2(fmaf(s1[e], c, -m_run));
+        ps += p0[e] + p1[e];
+      }
+      l_run += ps;
+      F::pv(cur.v, p0, p1, o);
+      if (ci + 1 < n_chunks) cur = nxt;
+    }
+
+    float l = l_run + xor_lane(l_run, 16);
+    l = l + xor_lane(l, 32);
+
+    const int64_t u = window_image_index(geo, win, qvalid ? kq : 0);
+    float wsel = 1.0f, wctx = 0.0f;
+    f32x4 octx[4];
+    if (p.ctx_o) {
+      const float lc = p.ctx_lse[u * H + h] * kLog2e;
+      const float mm = fmaxf(m_run, lc);
+      wsel = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mm);
+      wctx = lc == -INFINITY ? 0.0f : fast_exp2(lc - mm);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        octx[m] = *reinterpret_cast<const f32x4*>(p.ctx_o + (u * H + h) * kHeadDim + 16 * m + 4 * g);
+    }
+    const float den = l * wsel + wctx;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    f32x4 res[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      res[m] = o[m] * wsel;
+      if (p.ctx_o) res[m] += octx[m] * wctx;
+      res[m] *= inv;
+    }
+
+    if (p.o) {
+      // fused upsample + gate + blend
+      const float z0 = F::q_dot(qf, static_cast<const T*>(p.wg) + h * kHeadDim, g);
+      float z = z0 + xor_lane(z0, 16);
+      z = z + xor_lane(z, 32);
+      const float gate = 1.0f / (1.0f + expf(-z));
+      if (qvalid) {
+        T* dst = static_cast<T*>(p.o) + (tok * H + h) * kHeadDim;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int dv0 = 16 * m + 4 * g;
+          f32x4 ocv = *reinterpret_cast<const f32x4*>(p.oc + (win * H + h) * kHeadDim + dv0);
+          f32x4 out = gate * ocv + (1.0f - gate) * res[m];
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 b4 = {(__bf16)out[0], (__bf16)out[1], (__bf16)out[2], (__bf16)out[3]};
+            *reinterpret_cast<bf16x4*>(dst + dv0) = b4;
+          } else {
+            *reinterpret_cast<f32x4*>(dst + dv0) = out;
+          }
+        }
+      }
+    } else if (qvalid) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        *reinterpret_cast<f32x4*>(p.osel + (u * H + h) * kHeadDim + 16 * m + 4 * g) = res[m];
+    }
+  }
+}
+
+// Standalone upsample + gate + blend: 8 lanes per (image token, head), each
+// owning 8 channels; the gate dot product is reduced across the 8 lanes.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const Geometry& geo = p.g;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t uh = gid >> 3;
+  const int part = (int)(gid & 7);
+  const bool active = uh < geo.m_img * geo.n_heads;
+  const int64_t uu = active ? uh : 0;
+  const int64_t u = uu / geo.n_heads, h = uu % geo.n_heads, H = geo.n_heads;
+  const int64_t hw = geo.grid_h * geo.grid_w;
+  const int64_t f = u / hw, pix = u % hw, y = pix / geo.grid_w, x = pix % geo.grid_w;
+  const int64_t tok = f * geo.tf + geo.n_special + pix;
+  const int64_t win = f * geo.wpf + (y / geo.pool) * geo.wx + x / geo.pool;
+  const T* qrow = static_cast<const T*>(p.q) + (tok * H + h) * kHeadDim + 8 * part;
+  float gate;
+  if (p.wg) {
+    const T* w = static_cast<const T*>(p.wg) + h * kHeadDim + 8 * part;
+    float z = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z += to_f32(qrow[e]) * to_f32(w[e]);
+    z += __shfl_xor(z, 1);
+    z += __shfl_xor(z, 2);
+    z += __shfl_xor(z, 4);
+    gate = 1.0f / (1.0f + expf(-z));
+  } else {
+    gate = p.gate[u * H + h];
+  }
+  if (!active) return;
+  const float* ocr = p.oc + (win * H + h) * kHeadDim + 8 * part;
+  const float* osr = p.osel + (u * H + h) * kHeadDim + 8 * part;
+  T* dst = static_cast<T*>(p.o) + (tok * H + h) * kHeadDim + 8 * part;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = from_f32<T>(gate * ocr[e] + (1.0f - gate) * osr[e]);
+}
+
+hipError_t launch_select(int dtype, const SelectParams& p, hipStream_t stream) {
+  const int64_t items = p.g.n_windows * p.g.n_heads;
+  if (items == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((items + 3) / 4);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(select_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(select_kernel<float>, dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t stream) {
+  const int64_t threads = p.g.m_img * p.g.n_heads * 8;
+  if (threads == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(combine_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gsa

@@ -1,0 +1,125 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+that include/gsa.h declares, and rejects bad arguments on the host without
+touching a device (each case below fails validation before any launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    so = os.path.join(ROOT, "sparse_global_attention_amd", "libgsa.so")
+    if not os.path.exists(so):
+        from sparse_global_attention_amd import build as b  # noqa: F401  (import fails without the .so)
+    import sparse_global_attention_amd as g
+    return g
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gsa.h")).read()
+    return sorted(set(re.findall(r"^(?:const char\*|gsa_status)\s+(gsa_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for want in ("gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn", "gsa_special_attn",
+                 "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_workspace_size", "gsa_status_string"):
+        assert want in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, re.M))
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, missing
+    assert set(lib.EXPORTS) == set(header_functions())
+
+
+def test_status_strings(lib):
+    assert lib.gsa_status_string(0) == "GSA_OK"
+    for s in range(1, 6):
+        assert lib.gsa_status_string(s).startswith("GSA_ERR_")
+    assert "unknown" in lib.gsa_status_string(99)
+
+
+def cfg(lib, **kw):
+    base = dict(n_frames=4, n_special=1, grid_h=8, grid_w=8, n_heads=2, head_dim=64, pool=2, topk=4,
+                dtype=lib.GSA_BF16)
+    base.update(kw)
+    return lib.GSAConfig.make(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(grid_h=9), 2), (dict(grid_w=6, pool=4), 2), (dict(n_frames=0), 2), (dict(n_heads=0), 2),
+    (dict(head_dim=128), 3), (dict(pool=16, grid_h=16, grid_w=16), 3), (dict(topk=129), 3), (dict(dtype=7), 3),
+    (dict(topk=0), 1), (dict(ctx_frames=(4,)), 1), (dict(ctx_frames=(1, 1)), 1), (dict(scale=-1.0), 1),
+    (dict(scale=float("nan")), 1), (dict(ctx_exclude_from_topk=2), 1),
+])
+def test_config_validation(lib, kw, status):
+    size = ctypes.c_size_t()
+    assert lib.call_status("gsa_workspace_size", ctypes.byref(cfg(lib, **kw)), 0, ctypes.byref(size)) == status
+
+
+def test_null_config_and_bad_op(lib):
+    size = ctypes.c_size_t()
+    assert lib.call_status("gsa_workspace_size", None, 0, ctypes.byref(size)) == 1
+    assert lib.call_status("gsa_workspace_size", ctypes.byref(cfg(lib)), 9, ctypes.byref(size)) == 1
+    assert lib.call_status("gsa_workspace_size", ctypes.byref(cfg(lib)), 0, None) == 1
+
+
+def test_workspace_sizes(lib):
+    c = cfg(lib, n_frames=32, n_special=5, grid_h=32, grid_w=32, n_heads=16, pool=4, topk=16)
+    fw = lib.gsa_workspace_size(c, lib.GSA_OP_FORWARD)
+    sel = lib.gsa_workspace_size(c, lib.GSA_OP_SELECT)
+    spec = lib.gsa_workspace_size(c, lib.GSA_OP_SPECIAL)
+    assert lib.gsa_workspace_size(c, lib.GSA_OP_DENSE) == 0
+    mw, H, d = 32 * 64, 16, 64
+    pooled = mw * H * d * 2
+    assert sel == 2 * mw * H * 16 * d * 2  # blocked K and V^T copies, 16 slots per window
+    assert fw >= 3 * pooled + mw * H * d * 4 + mw * H * 16 * 4 + sel + spec
+    assert spec > 0
+    ctx = cfg(lib, n_frames=8, ctx_frames=(0, 5))
+    assert lib.gsa_workspace_size(ctx, lib.GSA_OP_SELECT) > lib.gsa_workspace_size(cfg(lib, n_frames=8),
+                                                                                    lib.GSA_OP_SELECT)
+
+
+# Addresses that are never dereferenced: every call below fails validation first.
+A = 0x10000
+MISALIGNED = 0x10004
+
+
+def test_pointer_validation(lib):
+    c = ctypes.byref(cfg(lib))
+    assert lib.call_status("gsa_pool", c, None, A, A, A, A, A, None) == 1
+    assert lib.call_status("gsa_pool", c, MISALIGNED, A, A, A, A, A, None) == 1
+    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, A, None, None, None) == 1
+    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, A, A, MISALIGNED, None) == 1
+    assert lib.call_status("gsa_gate_combine", c, A, None, None, A, A, A + 64, None) == 1  # no wg and no gate
+    assert lib.call_status("gsa_forward", c, A, A, A, A, A, A, 1 << 30, None) == 1  # o aliases q
+    assert lib.call_status("gsa_special_attn", c, A, A, A, A, A, 1 << 30, None) == 1  # o aliases q
+    assert lib.call_status("gsa_dense_attn", c, A, A + 16, A + 32, A, None, 0, None) == 1  # o aliases q
+
+
+def test_workspace_validation(lib):
+    cc = cfg(lib)
+    c = ctypes.byref(cc)
+    need = lib.gsa_workspace_size(cc, lib.GSA_OP_FORWARD)
+    o = A + (1 << 20)
+    assert lib.call_status("gsa_forward", c, A, A, A, A, o, A, need - 1, None) == 4
+    assert lib.call_status("gsa_forward", c, A, A, A, A, o, None, need, None) == 1
+    assert lib.call_status("gsa_forward", c, A, A, A, A, o, A + 16, need, None) == 1  # ws not 256-aligned
+    need = lib.gsa_workspace_size(cc, lib.GSA_OP_SELECT)
+    assert lib.call_status("gsa_select_attn", c, A, A, A, A, o, A, need - 256, None) == 4
+    need = lib.gsa_workspace_size(cc, lib.GSA_OP_SPECIAL)
+    assert lib.call_status("gsa_special_attn", c, A, A, A, o, A, need - 1, None) == 4
+
+
+def test_binding_raises_gsa_error(lib):
+    with pytest.raises(lib.GSAError) as e:
+        lib.gsa_workspace_size(cfg(lib, grid_h=7), lib.GSA_OP_FORWARD)
+    assert e.value.status == lib.GSA_ERR_SHAPE

@@ -1,0 +1,205 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by
+element, on seeded inputs small enough for the whole oracle: the tiny fp32
+workload, the 32-frame bf16 workload, and edge shapes (ragged tails, s in
+{1, 2, 4, 8}, P = 0, fixed context, k beyond the candidate count, k = 64/128).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gen.configs import BF16, F32, SMALL_BF16, TINY_F32, GSAShape
+from gsa_testlib import (Case, assert_close, check_topk, special_token_ids, to_host, window_image_ids,
+                         window_token_ids)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny_f32": TINY_F32,
+    "small_bf16": SMALL_BF16,
+    "odd_bf16": GSAShape("odd 3f-12x8-h3-s4-k5", 3, 2, 12, 8, 3, 64, 4, 5, BF16, seed=21),
+    "odd_f32": GSAShape("odd 3f-12x8-h3-s4-k5 fp32", 3, 2, 12, 8, 3, 64, 4, 5, F32, seed=22),
+    "s8": GSAShape("s8 3f-16x16-h2-s8-k3", 3, 1, 16, 16, 2, 64, 8, 3, BF16, seed=23),
+    "s1": GSAShape("s1 2f-6x5-h2-s1-k7", 2, 1, 6, 5, 2, 64, 1, 7, BF16, seed=24),
+    "s2_bf16": GSAShape("s2 4f-8x8-h2-s2-k4", 4, 3, 8, 8, 2, 64, 2, 4, BF16, seed=25),
+    "p0": GSAShape("p0 4f-8x12-h2-s4-k3", 4, 0, 8, 12, 2, 64, 4, 3, BF16, seed=26),
+    "ctx": GSAShape("ctx 6f-8x8-h2-s4-k3+ctx{0,3}", 6, 2, 8, 8, 2, 64, 4, 3, BF16, ctx_frames=(0, 3), seed=27),
+    "ctx_f32": GSAShape("ctx 5f-8x8-h1-s2-k6+ctx{4}", 5, 1, 8, 8, 1, 64, 2, 6, F32, ctx_frames=(4,), seed=28),
+    "k_clamp": GSAShape("kclamp 2f-8x8-h2-s4-k64", 2, 1, 8, 8, 2, 64, 4, 64, BF16, seed=29),
+    "k64": GSAShape("k64 10f-16x16-h2-s4-k64", 10, 1, 16, 16, 2, 64, 4, 64, BF16, seed=30),
+    "k128": GSAShape("k128 10f-16x16-h1-s4-k128", 10, 1, 16, 16, 1, 64, 4, 128, BF16, seed=31),
+}
+
+
+class Result:
+    """GPU intermediates of one workload and the oracle's."""
+
+    def __init__(self, sh):
+        self.sh = sh
+        self.case = c = Case(sh)
+        # HIP path
+        self.gqc, self.gkc, self.gvc = c.pool()
+        self.goc, self.gidx, self.gsc = c.compressed(self.gqc, self.gkc, self.gvc)
+        self.gosel = c.select(self.gidx)
+        self.gspec = c.special()
+        self.gout = c.forward()
+        torch.cuda.synchronize()
+        # oracle
+        wins = np.arange(sh.n_windows)
+        self.qc, self.kc, self.vc = (oracle.pool(sh, x) for x in (c.q, c.k, c.v))
+        self.oc, self.idx, self.sc, self.amax = oracle.compressed(sh, self.qc, self.kc, self.vc, wins)
+        self.gidx_h = self.gidx.cpu().numpy()
+        self.osel_gpu_idx = oracle.select(sh, c.q, c.k, c.v, wins, self.gidx_h)
+        rows = np.arange(sh.m_spec)
+        self.spec = oracle.special(sh, c.q, c.k, c.v, rows) if sh.m_spec else None
+
+
+_cache = {}
+
+
+def result(name):
+    if name not in _cache:
+        _cache[name] = Result(SHAPES[name])
+    return _cache[name]
+
+
+ALL = list(SHAPES)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_pool_bit_exact(name):
+    r = result(name)
+    for g, o in ((r.gqc, r.qc), (r.gkc, r.kc), (r.gvc, r.vc)):
+        got = g.float().cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), o.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_compressed_attention_and_topk(name):
+    r = result(name)
+    sh = r.sh
+    assert_close(to_host(r.goc), r.oc, sh.dtype, f"{name} O'_comp")
+    gpu_s = oracle.guide_scores(sh, r.qc, r.kc, np.arange(sh.n_windows), r.gidx_h)
+    check_topk(sh, r.gidx_h, r.idx, r.sc, r.amax, gpu_s)
+    # the returned scores are the raw guide scores of the returned windows
+    kp = sh.topk_eff
+    gsc = r.gsc.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(gsc[..., :kp], gpu_s[..., :kp], rtol=1e-5, atol=1e-5 * r.amax.max())
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_selection_attention(name):
+    r = result(name)
+    sh = r.sh
+    osel = to_host(r.gosel)  # [M_img][H][d] by image token
+    got = osel[window_image_ids(sh)]  # -> [M'][s*s][H][d]
+    assert_close(got, r.osel_gpu_idx, sh.dtype, f"{name} O_sel")
+
+
+@pytest.mark.parametrize("name", [n for n in ALL if SHAPES[n].n_special > 0])
+def test_special_attention(name):
+    r = result(name)
+    sh = r.sh
+    got = to_host(r.gspec).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    assert_close(got[special_token_ids(sh)], r.spec, sh.dtype, f"{name} O_spec")
+    # image rows are left untouched by the special-token call
+    img = np.setdiff1d(np.arange(sh.m_tokens), special_token_ids(sh))
+    assert np.all(got[img] == 0.0)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_forward_matches_oracle(name):
+    r = result(name)
+    sh = r.sh
+    c = r.case
+    wins = np.arange(sh.n_windows)
+    oimg = oracle.gate_combine(sh, c.q, c.wg, wins, r.oc, r.osel_gpu_idx)
+    got = to_host(r.gout).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    assert_close(got[window_token_ids(sh)], oimg, sh.dtype, f"{name} O_img")
+    if sh.m_spec:
+        assert_close(got[special_token_ids(sh)], r.spec, sh.dtype, f"{name} O_spec (forward)")
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "odd_f32", "ctx"])
+def test_forward_equals_composed_calls(name):
+    import sparse_global_attention_amd as gsa
+    r = result(name)
+    sh, c = r.sh, r.case
+    o = r.gspec.clone()
+    gsa.gsa_gate_combine(c.cfg, c.dq, c.dwg, None, r.goc, r.gosel, o)
+    torch.cuda.synchronize()
+    fused = to_host(r.gout)
+    composed = to_host(o)
+    tol = 1e-6 if sh.dtype == F32 else 2 ** -7
+    np.testing.assert_allclose(fused, composed, atol=tol, rtol=tol)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "tiny_f32"])
+def test_explicit_gates_select_one_branch(name):
+    import sparse_global_attention_amd as gsa
+    r = result(name)
+    sh, c = r.sh, r.case
+    for gval, branch in ((0.0, "sel"), (1.0, "comp")):
+        gate = torch.full((sh.m_img, sh.n_heads), gval, dtype=torch.float32, device="cuda")
+        o = torch.zeros_like(c.dq)
+        gsa.gsa_gate_combine(c.cfg, c.dq, None, gate, r.goc, r.gosel, o)
+        torch.cuda.synchronize()
+        got = to_host(o).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)[window_token_ids(sh)]
+        if branch == "sel":
+            want = to_host(r.gosel.to(c.dq.dtype))[window_image_ids(sh)]
+        else:
+            want = np.broadcast_to(to_host(r.goc.to(c.dq.dtype))[:, None], got.shape)
+        assert np.array_equal(got, want), (name, gval)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "ctx", "odd_f32"])
+def test_constant_values_give_constant_output(name):
+    sh = SHAPES[name]
+    cst = np.random.default_rng(5).standard_normal((sh.n_heads, sh.head_dim)).astype(np.float32)
+    v32 = np.ascontiguousarray(np.broadcast_to(cst, sh.qkv_shape))
+    if sh.dtype == BF16:
+        v = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        cst = gen.to_f32(v[0, 0], BF16)
+    else:
+        v = v32
+    c = Case(sh, v=v)
+    out = to_host(c.forward())
+    assert_close(out, np.broadcast_to(cst.astype(np.float64), sh.qkv_shape), sh.dtype, f"{name} constant V")
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "ctx"])
+def test_forward_is_deterministic(name):
+    r = result(name)
+    again = r.case.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16) if again.dtype == torch.bfloat16 else again,
+                       r.gout.view(torch.int16) if r.gout.dtype == torch.bfloat16 else r.gout)
+
+
+def test_topk_ties_go_to_lower_window():
+    sh = GSAShape("ties 4f-8x8-h2-s4-k3", 4, 1, 8, 8, 2, 64, 4, 3, BF16, seed=40)
+    c = Case(sh)
+    qc, kc, vc = c.pool()
+    kc[:] = kc[5].clone()  # every key window identical: every guide score ties
+    _, idx, _ = c.compressed(qc, kc, vc)
+    torch.cuda.synchronize()
+    assert np.all(idx.cpu().numpy() == np.array([0, 1, 2], np.int32))
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "odd_f32"])
+def test_dense_comparator_rows(name):
+    sh = SHAPES[name]
+    c = Case(sh)
+    out = to_host(c.dense()).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    rows = np.unique(np.concatenate([[0, sh.m_tokens - 1],
+                                     np.random.default_rng(3).choice(sh.m_tokens, 30, replace=False)]))
+    Q = gen.to_f32(c.q, sh.dtype).astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    K = gen.to_f32(c.k, sh.dtype).astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    V = gen.to_f32(c.v, sh.dtype).astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    ref = np.empty((rows.size, sh.n_heads, sh.head_dim))
+    for h in range(sh.n_heads):
+        s = Q[rows, h] @ K[:, h].T / 8.0
+        w = np.exp(s - s.max(1, keepdims=True))
+        ref[:, h] = (w / w.sum(1, keepdims=True)) @ V[:, h]
+    assert_close(out[rows], ref, sh.dtype, f"{name} dense rows")
