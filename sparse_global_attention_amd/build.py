@@ -22,7 +22,9 @@ OBJ = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # keep matrix-core accumulators in VGPRs (no AGPR copies around each MFMA)
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

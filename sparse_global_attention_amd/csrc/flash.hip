@@ -44,17 +44,46 @@ namespace gsa {
 
 constexpr int kKT = 32;              // keys per tile
 constexpr float kLazyRescale = 8.0f; // rescale only when the max grows by > 2^8
-constexpr int kBufCap = 16;          // per-lane top-k candidate buffer (entries)
 
+// LDS tile of 32 keys.
+// bf16: K and V are stored row-major (one 128-byte row per key) with the
+// 16-byte chunks of row r permuted as c -> c ^ (r % 8): reads of the same
+// chunk by 8 consecutive rows then hit 8 different bank groups, with no
+// padding.  V is read transposed by ds_read_b64_tr_b16.
+// fp32: K rows padded by 16 bytes; V stored transposed (channel rows) since
+// there is no transposing read for 32-bit data.
 template <typename T>
-struct Tile {
-  static constexpr int VE = 16 / sizeof(T);
-  static constexpr int KSTRIDE = kHeadDim + VE;  // K row stride in LDS (+16 B: conflict-free b128 reads)
-  static constexpr int VSTRIDE = sizeof(T) == 2 ? kKT + 4 : kKT + 4;  // V^T row stride
+struct Tile;
+
+template <>
+struct Tile<__bf16> {
+  static constexpr int VE = 8;
+  static constexpr int K_ELEMS = kKT * kHeadDim;
+  static constexpr int V_ELEMS = kKT * kHeadDim;
+  static constexpr int BYTES = (K_ELEMS + V_ELEMS) * 2;
+  // element offset of 16-byte chunk c of key row `key`
+  __device__ static int chunk(int key, int c) { return key * kHeadDim + ((c ^ (key & 7)) << 3); }
+};
+
+template <>
+struct Tile<float> {
+  static constexpr int VE = 4;
+  static constexpr int KSTRIDE = kHeadDim + VE;
+  static constexpr int VSTRIDE = kKT + 4;
   static constexpr int K_ELEMS = kKT * KSTRIDE;
   static constexpr int V_ELEMS = kHeadDim * VSTRIDE;
-  static constexpr int BYTES = ((K_ELEMS + V_ELEMS) * (int)sizeof(T) + 15) / 16 * 16;
+  static constexpr int BYTES = (K_ELEMS + V_ELEMS) * 4;
 };
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i%4 of the 8-byte chunks addressed by lanes 4e + i/4 (e = 0..3) of its group.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<__bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 // ---- matrix-core fragments (32x32 family) ----------------------------------
 template <typename T>
@@ -82,31 +111,52 @@ struct Frag32<__bf16> {
   }
   // S^T = K Q^T over d (the same d order on both operands).
   __device__ static f32x16 qk(const __bf16* kt, int r, int hf, const Q& q) {
-    const __bf16* base = kt + r * TL::KSTRIDE + 32 * hf;
     bf16x8 a[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(base + 8 * ks);
+    for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(kt + TL::chunk(r, 4 * hf + ks));
     f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) s = mfma32(a[ks], q.v[ks], s);
     return s;
   }
+  // P operand: the bf16 values of the lane's S^T elements; the row sum adds
+  // exactly these rounded values, so numerator and denominator agree.
+  struct P {
+    bf16x8 v[2];
+  };
+  __device__ static P to_p(const f32x16& p, float& psum) {
+    P r;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.v[m][e] = (__bf16)p[8 * m + e];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) psum = add_pair(bf16x2{r.v[m][2 * e], r.v[m][2 * e + 1]}, psum);
+    return r;
+  }
   // O^T += V^T P^T.  The P operand of lane (q, hf) for key group m is its own
   // S^T elements 8m..8m+7, i.e. keys 16m + 8*(e/4) + 4*hf + e%4; the V^T
-  // operand of lane (dv, hf) reads the same keys for channel dv.
-  __device__ static void pv(const __bf16* vt, int r, int hf, const f32x16& p, f32x16 o[2]) {
+  // operand of lane (dv, hf) needs the same keys for channel dv.  With V rows
+  // in LDS, lane j of each 16-lane group G addresses key 16m + 8c + 4(G/2) + j/4,
+  // channels 32n + 16(G%2) + 4(j%4) .. +3; the transposing read then hands
+  // lane l exactly V[16m + 8c + 4hf + e'][32n + l%32] for e' = 0..3.
+  __device__ static void pv(const __bf16* vt, int lane, const P& p, f32x16 o[2]) {
+    const int G = lane >> 4, j = lane & 15;
+    const int krow = 4 * (G >> 1) + (j >> 2);      // + 16m + 8c
+    const int dv = 16 * (G & 1) + 4 * (j & 3);     // + 32n
+    const int sw = krow & 7;                       // chunk swizzle of every row this lane reads
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      bf16x8 b;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = (__bf16)p[8 * m + e];
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const __bf16* row = vt + (32 * n + r) * TL::VSTRIDE + 16 * m + 4 * hf;
-        bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-        bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 8);
+        const int off = (((4 * n + (dv >> 3)) ^ sw) << 3) + (dv & 7);
+        const __bf16* q0 = vt + (16 * m + krow) * kHeadDim + off;
+        bf16x4 lo = lds_read_tr16(q0);
+        bf16x4 hi = lds_read_tr16(q0 + 8 * kHeadDim);
         bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[n] = mfma32(a, b, o[n]);
+        o[n] = mfma32(a, p.v[m], o[n]);
       }
     }
   }
@@ -140,15 +190,24 @@ struct Frag32<float> {
     }
     return s;
   }
+  struct P {
+    f32x16 v;
+  };
+  __device__ static P to_p(const f32x16& p, float& psum) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) psum += p[i];
+    return P{p};
+  }
   // element i of lane (q, hf) is key 8*(i/4) + 4*hf + i%4; one MFMA per i.
-  __device__ static void pv(const float* vt, int r, int hf, const f32x16& p, f32x16 o[2]) {
+  __device__ static void pv(const float* vt, int lane, const P& p, f32x16 o[2]) {
+    const int r = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         f32x4 x = *reinterpret_cast<const f32x4*>(vt + (32 * n + r) * TL::VSTRIDE + 8 * a4 + 4 * hf);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[n] = mfma32(x[e], p[4 * a4 + e], o[n]);
+        for (int e = 0; e < 4; ++e) o[n] = mfma32(x[e], p.v[4 * a4 + e], o[n]);
       }
     }
   }
@@ -185,10 +244,15 @@ struct TileLoader {
     for (int i = 0; i < NV; ++i) {
       int idx = tid + i * NT;
       int key = idx / VPR, c = idx % VPR;
-      st16(kt + key * TL::KSTRIDE + c * VE, kr[i]);
-      const T* x = reinterpret_cast<const T*>(&vr[i]);
+      if constexpr (sizeof(T) == 2) {
+        st16(kt + TL::chunk(key, c), kr[i]);
+        st16(vt + TL::chunk(key, c), vr[i]);
+      } else {
+        st16(kt + key * TL::KSTRIDE + c * VE, kr[i]);
+        const T* x = reinterpret_cast<const T*>(&vr[i]);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) vt[(c * VE + e) * TL::VSTRIDE + key] = x[e];
+        for (int e = 0; e < VE; ++e) vt[(c * VE + e) * TL::VSTRIDE + key] = x[e];
+      }
     }
   }
 };
@@ -202,7 +266,7 @@ struct Cand {
 __device__ __forceinline__ bool worse(Cand a, Cand b) { return a.s < b.s || (a.s == b.s && a.j > b.j); }
 
 __device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -249,20 +313,28 @@ __device__ void heap_insert(Cand* hp, int r, int& n, int K, Cand x) {
   }
 }
 
-struct TopkState {
-  Cand* heap;  // this wave's heaps: [K][32]
-  Cand* buf;   // this wave's buffers: [kBufCap][64]
-  int hsize;   // entries in this lane's query heap (same in both lanes of the query)
-  int cnt;     // entries in this lane's buffer
-  float tau;   // current k-th best score of the query (-inf until the heap is full)
+constexpr int kBufCap = 16;  // per-lane buffered candidates
 
-  // Move every buffered candidate into the heaps; the two lanes of a query
+__device__ __forceinline__ bool excluded_window(const FlashParams& p, int64_t key);
+
+struct TopkState {
+  Cand* heap;    // this wave's heaps: [K][32]
+  Cand* buf;     // this wave's candidate buffers: [kBufCap][64]
+  int hsize;     // entries in this lane's query heap (same in both lanes of the query)
+  int cnt;       // candidates in this lane's buffer
+  float tau;     // current k-th best score of the query (-inf until the heap is full)
+  float tau_u;   // tau in the shifted exponent units fma(tau, c, -m) of the running max m
+
+  // Move every buffered candidate into the heaps.  The two lanes of a query
   // take turns because they share its heap.
-  __device__ void flush(int lane, int r, int hf, int K) {
+  __device__ void flush(const FlashParams& p, int lane, int r, int hf, int K) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if (hf == half) {
-        for (int b = 0; b < cnt; ++b) heap_insert(heap, r, hsize, K, buf[b * 64 + lane]);
+        for (int b = 0; b < cnt; ++b) {
+          const Cand x = buf[b * 64 + lane];
+          if (!excluded_window(p, x.j)) heap_insert(heap, r, hsize, K, x);
+        }
       }
       wave_sync();
       int other = xor_lane(hsize, 32);
@@ -287,8 +359,9 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
   using TL = Tile<T>;
   using F = Frag32<T>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  T* kt = reinterpret_cast<T*>(smem);
-  T* vt = kt + TL::K_ELEMS;
+  // two K/V tile buffers: tile t is read from buffer t%2 while tile t+1 is stored into the other
+  T* const kbuf0 = reinterpret_cast<T*>(smem);
+  T* const kbuf1 = reinterpret_cast<T*>(smem + TL::BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
@@ -308,45 +381,49 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
   typename F::Q qf = F::load_q(qvalid ? static_cast<const T*>(p.q) + qtok * p.row_stride + hoff : nullptr, hf);
+  // Let the query fragment land before any tile prefetch is issued, so the
+  // loop never has to drain the prefetch queue to be sure of it.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 o[2] = {{}, {}};
   float m_run = -INFINITY, l_run = 0.0f;
+  bool first = true;
   const float c = p.scale_log2;
 
   TopkState tk;
   if constexpr (MODE == kFlashTopk) {
-    Cand* base = reinterpret_cast<Cand*>(smem + TL::BYTES);
+    Cand* base = reinterpret_cast<Cand*>(smem + 2 * TL::BYTES);
     tk.heap = base + wv * p.topk * 32;
     tk.buf = base + WAVES * p.topk * 32 + wv * kBufCap * 64;
     tk.hsize = 0;
     tk.cnt = 0;
     tk.tau = -INFINITY;
+    tk.tau_u = -INFINITY;
   }
 
-  TileLoader<T, WAVES * 64> ld;
-  int ri = p.split_r0[split];
-  const int re = p.split_r0[split + 1];
-  while (ri < re && p.kbeg[ri] >= p.kend[ri]) ++ri;
-  int64_t key0 = 0;
-  if (ri < re) {
-    key0 = p.kbeg[ri];
-    ld.load(K, V, p.row_stride, hoff, key0, p.kend[ri], tid);
-  }
+  // Key tiles of this split: tile t covers keys kb + 32t .. kb + 32t + 31.
+  // Prefetches past the last tile re-read the last tile (never used), so the
+  // load/store pattern has no branches and the compiler can keep two tiles of
+  // loads in flight across the barriers.
+  const int64_t kb = p.kbeg[split], ke = p.kend[split];
+  const int n_tiles = (int)((ke - kb + kKT - 1) / kKT);
+  auto tile_key = [&](int t) { return kb + (int64_t)(t < n_tiles ? t : n_tiles - 1) * kKT; };
+  TileLoader<T, WAVES * 64> sa, sb;
+  sa.load(K, V, p.row_stride, hoff, tile_key(0), ke, tid);
+  sb.load(K, V, p.row_stride, hoff, tile_key(1), ke, tid);
+  sa.store(kbuf0, kbuf0 + TL::K_ELEMS, tid);
+  sa.load(K, V, p.row_stride, hoff, tile_key(2), ke, tid);
+  lds_barrier();
 
-  while (ri < re) {
-    const int64_t cur0 = key0, cur_end = p.kend[ri];
-    int ni = ri;
-    int64_t nk = key0 + kKT;
-    if (nk >= p.kend[ni]) {
-      ++ni;
-      while (ni < re && p.kbeg[ni] >= p.kend[ni]) ++ni;
-      if (ni < re) nk = p.kbeg[ni];
-    }
-    __syncthreads();
-    ld.store(kt, vt, tid);
-    __syncthreads();
-    if (ni < re) ld.load(K, V, p.row_stride, hoff, nk, p.kend[ni], tid);
-
+  // One tile: compute tile t from LDS, then move tile t+1 from register stage
+  // `nxt` into the other LDS buffer and reuse `nxt` for tile t+3.  The loop
+  // below is unrolled by two so the stages swap roles without register copies
+  // (a copy would wait for the in-flight loads).
+  auto step = [&](int t, TileLoader<T, WAVES * 64>& nxt) {
+    // a step past the last tile (odd tile count) sees only masked keys
+    const int64_t cur0 = kb + (int64_t)t * kKT, cur_end = ke;
+    const T* kt = (t & 1) ? kbuf1 : kbuf0;
+    const T* vt = kt + TL::K_ELEMS;
     f32x16 s = F::qk(kt, r, hf, qf);
     if (cur0 + kKT > cur_end) {
 #pragma unroll
@@ -355,59 +432,91 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
         if (key >= cur_end) s[i] = -INFINITY;
       }
     }
-    float g[4];
+    if (first) {
+      // the running max starts at the first tile's max (every tile holds a valid key)
+      float mx = s[0];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) g[a] = fmaxf(fmaxf(s[4 * a], s[4 * a + 1]), fmaxf(s[4 * a + 2], s[4 * a + 3]));
-    float mx = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
-
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      m_run = mx * c;
+      first = false;
+    }
+    // u = shifted log2-domain logits; every max below is taken on u, which the
+    // compiler knows to be canonical, so the reductions are bare v_max3 ops
+    f32x16 u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = fmaf(s[i], c, -m_run);
+    float mu;
     if constexpr (MODE == kFlashTopk) {
-      if (wave_any(mx > tk.tau)) {
+      // 4-key group maxima, shared by the top-k filter and the softmax.  u is a
+      // non-decreasing function of the raw score, so "group max >= tau_u" keeps
+      // every group holding a score above tau; exact tests run on raw scores.
+      float g[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) g[a] = max3(fmaxf(u[4 * a], u[4 * a + 1]), u[4 * a + 2], u[4 * a + 3]);
+      mu = max3(fmaxf(g[0], g[1]), g[2], g[3]);
+      if (wave_any(mu >= tk.tau_u)) {
+        // a passing group adds at most 4 entries: flush first if any lane could overflow
         int need = 0;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) need += g[a] > tk.tau ? 4 : 0;
-        if (wave_any(tk.cnt + need > kBufCap)) tk.flush(lane, r, hf, p.topk);
+        for (int a = 0; a < 4; ++a) need += g[a] >= tk.tau_u ? 4 : 0;
+        if (wave_any(tk.cnt + need > kBufCap)) {
+          tk.flush(p, lane, r, hf, p.topk);
+          tk.tau_u = fmaf(tk.tau, c, -m_run);
+        }
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          if (wave_any(g[a] > tk.tau)) {
+          const bool take = g[a] >= tk.tau_u;
+          if (wave_any(take)) {
+            if (take) {
+              // write every score of the group, keep those strictly above the raw
+              // root score (a tie loses: the root holds an earlier, lower index)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int64_t key = cur0 + 8 * a + 4 * hf + e;
-              if (s[4 * a + e] > tk.tau && !excluded_window(p, key)) {
-                tk.buf[tk.cnt * 64 + lane] = Cand{s[4 * a + e], (int)key};
-                ++tk.cnt;
+              for (int e = 0; e < 4; ++e) {
+                tk.buf[tk.cnt * 64 + lane] = Cand{s[4 * a + e], (int)(cur0 + 8 * a + 4 * hf + e)};
+                tk.cnt += s[4 * a + e] > tk.tau ? 1 : 0;
               }
             }
           }
         }
       }
+    } else {
+      const float m0 = max3(u[0], u[1], u[2]), m1 = max3(u[3], u[4], u[5]), m2 = max3(u[6], u[7], u[8]);
+      const float m3 = max3(u[9], u[10], u[11]), m4 = max3(u[12], u[13], u[14]);
+      mu = max3(max3(m0, m1, m2), max3(m3, m4, u[15]), u[15]);
     }
-
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float mnew = mx * c;
-    const bool need = mnew > m_run + kLazyRescale;
+    mu = fmaxf(mu, xor_lane(mu, 32));
+    // lazy rescale: only when the max has grown by more than 2^kLazyRescale
+    const bool need = mu > kLazyRescale;
     if (wave_any(need)) {
       if (need) {
-        const float alpha = fast_exp2(m_run - mnew);
-        m_run = mnew;
+        const float alpha = fast_exp2(-mu);
+        m_run += mu;
         l_run *= alpha;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[n][i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) u[i] -= mu;
       }
+      if constexpr (MODE == kFlashTopk) tk.tau_u = fmaf(tk.tau, c, -m_run);
     }
     f32x16 pw;
-    float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      pw[i] = fast_exp2(fmaf(s[i], c, -m_run));
-      psum += pw[i];
-    }
-    l_run += psum;
-    F::pv(vt, r, hf, pw, o);
+    for (int i = 0; i < 16; ++i) pw[i] = fast_exp2(u[i]);
+    const typename F::P pp = F::to_p(pw, l_run);
+    F::pv(vt, lane, pp, o);
 
-    ri = ni;
-    key0 = nk;
+
+    T* kn = (t & 1) ? kbuf0 : kbuf1;
+    nxt.store(kn, kn + TL::K_ELEMS, tid);
+    nxt.load(K, V, p.row_stride, hoff, tile_key(t + 3), ke, tid);
+    lds_barrier();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, sb);
+    step(t + 1, sa);
   }
 
   // ---- epilogue ----
@@ -444,7 +553,7 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
   }
 
   if constexpr (MODE == kFlashTopk) {
-    tk.flush(lane, r, hf, p.topk);
+    tk.flush(p, lane, r, hf, p.topk);
     const int K = p.topk;
     if (hf == 0) {
       // heapsort: repeatedly move the worst kept entry to the back
@@ -501,7 +610,7 @@ static hipError_t launch_flash_t(const FlashParams& p, hipStream_t stream) {
   const int64_t n_qt = (p.n_q + WAVES * 32 - 1) / (WAVES * 32);
   const int64_t blocks = n_qt * p.n_heads * p.n_splits;
   if (blocks == 0) return hipSuccess;
-  size_t lds = Tile<T>::BYTES;
+  size_t lds = 2 * (size_t)Tile<T>::BYTES;
   if (MODE == kFlashTopk) lds += (size_t)WAVES * ((size_t)p.topk * 32 + kBufCap * 64) * sizeof(Cand);
   const void* fn = reinterpret_cast<const void*>(&flash_kernel<T, WAVES, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -105,8 +105,8 @@ Plan make_plan(const Call& c, gsa_op op) {
   const int64_t blk = g.n_windows * g.n_heads * g.sb * kHeadDim * c.esz;
   const int64_t spec_o = (int64_t)p.n_split * g.m_spec * g.n_heads * kHeadDim * 4;
   const int64_t spec_lse = (int64_t)p.n_split * g.m_spec * g.n_heads * 4;
-  const int64_t ctx_o = c.n_ctx ? g.m_img * g.n_heads * kHeadDim * 4 : 0;
-  const int64_t ctx_lse = c.n_ctx ? g.m_img * g.n_heads * 4 : 0;
+  const int64_t ctx_o = (int64_t)c.n_ctx * g.m_img * g.n_heads * kHeadDim * 4;
+  const int64_t ctx_lse = (int64_t)c.n_ctx * g.m_img * g.n_heads * 4;
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
     int64_t at = off;
@@ -179,11 +179,9 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
   const int64_t tiles = (g.m_tokens + 31) / 32;
   f.n_splits = ns;
   for (int s = 0; s < ns; ++s) {
-    f.split_r0[s] = s;
     f.kbeg[s] = tiles * s / ns * 32;
     f.kend[s] = s + 1 == ns ? g.m_tokens : tiles * (s + 1) / ns * 32;
   }
-  f.split_r0[ns] = ns;
   f.part_o = reinterpret_cast<float*>(at(ws, pl.spec_o));
   f.part_lse = reinterpret_cast<float*>(at(ws, pl.spec_lse));
   hipError_t e = launch_flash(c.dtype, kFlashPartial, f, st);
@@ -208,8 +206,6 @@ hipError_t run_compressed(const Call& c, const void* qc, const void* kc, const v
   FlashParams f = flash_base(c, qc, kc, vc);
   set_rows_identity(f, g.n_windows);
   f.n_splits = 1;
-  f.split_r0[0] = 0;
-  f.split_r0[1] = 1;
   f.kbeg[0] = 0;
   f.kend[0] = g.n_windows;
   f.oc = oc;
@@ -231,9 +227,7 @@ hipError_t run_context(const Call& c, const Plan& pl, const void* q, const void*
   f.qa = g.grid_h * g.grid_w;
   f.qb = g.tf;
   f.qc = g.n_special;
-  f.n_splits = 1;
-  f.split_r0[0] = 0;
-  f.split_r0[1] = c.n_ctx;
+  f.n_splits = c.n_ctx;  // one split (and one partial) per context frame
   for (int i = 0; i < c.n_ctx; ++i) {
     f.kbeg[i] = (int64_t)c.ctx[i] * g.tf;
     f.kend[i] = f.kbeg[i] + g.tf;
@@ -261,6 +255,7 @@ SelectParams select_base(const Call& c, const Plan& pl, const void* q, const int
   s.topk = c.topk;
   s.g = c.g;
   s.scale_log2 = c.scale * kLog2e;
+  s.n_ctx = c.n_ctx;
   if (c.n_ctx) {
     s.ctx_o = reinterpret_cast<const float*>(at(ws, pl.ctx_o));
     s.ctx_lse = reinterpret_cast<const float*>(at(ws, pl.ctx_lse));
@@ -430,8 +425,6 @@ gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, c
   FlashParams f = flash_base(c, q, k, v);
   set_rows_identity(f, c.g.m_tokens);
   f.n_splits = 1;
-  f.split_r0[0] = 0;
-  f.split_r0[1] = 1;
   f.kbeg[0] = 0;
   f.kend[0] = c.g.m_tokens;
   f.o = o;

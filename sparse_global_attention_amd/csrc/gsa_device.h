@@ -31,11 +31,30 @@ __device__ __forceinline__ int xor_lane(int x, int mask) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// fences global memory, which makes every wave wait for its in-flight global
+// loads (the tile prefetch) at the barrier; this one does not.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Raw hardware exp2 (v_exp_f32): denormal results flush to zero, which only
 // drops softmax weights below 2^-126.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Three-way max.  On values the compiler knows to be canonical (results of
+// ordinary float arithmetic) this lowers to a bare v_max3_f32.
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// a + x.lo + x.hi for a pair of bf16 values (v_dot2c_f32_bf16 against 1.0).
+__device__ __forceinline__ float add_pair(bf16x2 x, float a) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, one, a, false);
+}
 
 // ---- MFMA wrappers (gfx950) ----------------------------------------------
 // 32x32 family: D[32x32] += A[32xK] B[Kx32]; lane l holds A row l%32, B column

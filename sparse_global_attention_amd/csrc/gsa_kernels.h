@@ -61,9 +61,8 @@ struct FlashParams {
   int n_heads;
   // query rows r in [0, n_q) map to token rows (r / qa) * qb + qc + r % qa
   int64_t n_q, qa, qb, qc;
-  // key ranges; split s covers ranges [split_r0[s], split_r0[s+1]) in order
+  // key splits: split s covers the non-empty contiguous key range [kbeg[s], kend[s])
   int n_splits;
-  int split_r0[kMaxRanges + 1];
   int64_t kbeg[kMaxRanges], kend[kMaxRanges];
   float scale_log2;  // softmax scale * log2(e)
   // kFlashFinal: normalised output in the input dtype at rows token(r) of o
@@ -103,8 +102,9 @@ struct SelectParams {
   int topk;
   Geometry g;
   float scale_log2;
-  const float* ctx_o;   // optional context partial [M_img][H][d] (normalised)
-  const float* ctx_lse; // and its log-sum-exp [M_img][H]
+  int n_ctx;            // context partials (one per context frame), 0 if none
+  const float* ctx_o;   // [n_ctx][M_img][H][d] (normalised)
+  const float* ctx_lse; // [n_ctx][M_img][H] log-sum-exp
   float* osel;          // standalone output [M_img][H][d]
   const void* wg;       // fused epilogue: gate projection [H][d]
   const float* oc;      // fused epilogue: compressed output [M'][H][d]

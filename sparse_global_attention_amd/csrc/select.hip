@@ -237,26 +237,27 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
     l = l + xor_lane(l, 32);
 
     const int64_t u = window_image_index(geo, win, qvalid ? kq : 0);
-    float wsel = 1.0f, wctx = 0.0f;
-    f32x4 octx[4];
-    if (p.ctx_o) {
-      const float lc = p.ctx_lse[u * H + h] * kLog2e;
-      const float mm = fmaxf(m_run, lc);
-      wsel = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mm);
-      wctx = lc == -INFINITY ? 0.0f : fast_exp2(lc - mm);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        octx[m] = *reinterpret_cast<const f32x4*>(p.ctx_o + (u * H + h) * kHeadDim + 16 * m + 4 * g);
-    }
-    const float den = l * wsel + wctx;
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    // join the context frames' partials (o_c normalised, lse_c natural log) into
+    // the same softmax: weights 2^(m_run - M) for the gathered part and
+    // 2^(lse_c log2 e - M) for each context part, M the largest exponent.
+    float mm = m_run;
+    for (int x = 0; x < p.n_ctx; ++x) mm = fmaxf(mm, p.ctx_lse[(x * geo.m_img + u) * H + h] * kLog2e);
+    const float wsel = m_run == -INFINITY ? 0.0f : fast_exp2(m_run - mm);
     f32x4 res[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      res[m] = o[m] * wsel;
-      if (p.ctx_o) res[m] += octx[m] * wctx;
-      res[m] *= inv;
+    for (int m = 0; m < 4; ++m) res[m] = o[m] * wsel;
+    float den = l * wsel;
+    for (int x = 0; x < p.n_ctx; ++x) {
+      const float lc = p.ctx_lse[(x * geo.m_img + u) * H + h] * kLog2e;
+      const float wc = lc == -INFINITY ? 0.0f : fast_exp2(lc - mm);
+      den += wc;
+      const float* oc_row = p.ctx_o + ((x * geo.m_img + u) * H + h) * kHeadDim + 4 * g;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) res[m] += wc * *reinterpret_cast<const f32x4*>(oc_row + 16 * m);
     }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) res[m] *= inv;
 
     if (p.o) {
       // fused upsample + gate + blend

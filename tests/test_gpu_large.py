@@ -1,0 +1,87 @@
+"""Parity at the full workload sizes, in the launch configuration the bench
+times (gsa_forward), checked on sampled outputs the oracle computes one by one:
+
+* pooled Q/K/V: every element, bit for bit;
+* compressed attention and top-k: sampled query windows x all heads
+  (tie-band rule for the index sets);
+* the forward's image rows of those windows (oracle selection driven by the
+  GPU's index sets, then upsample + gate);
+* the forward's special rows: sampled special tokens x all heads;
+* determinism: a second forward is bitwise identical.
+
+Workloads: VGGT-style 128 frames with fixed context {0, 100}; the pi^3-style
+1000-frame sequence; the peaky clustered 1024-frame sequence.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gen.configs import PEAKY, PI3_LONG, VGGT_CTX
+from gsa_testlib import Case, assert_close, check_topk, special_token_ids, to_host, window_token_ids
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+WORKLOADS = {"vggt_ctx": (VGGT_CTX, 1024), "pi3_long": (PI3_LONG, 512), "peaky": (PEAKY, 512)}
+N_SPECIAL_ROWS = 64
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.mark.timeout(1100)
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_sampled_parity(name):
+    sh, n_win = WORKLOADS[name]
+    t0 = time.time()
+    log(f"[{name}] {sh.name}: generating inputs")
+    c = Case(sh)
+    log(f"[{name}] inputs on device ({time.time() - t0:.0f} s); forward + pool + top-k on the GPU")
+    out = c.forward()
+    qc, kc, vc = c.pool()
+    oc, idx, _ = c.compressed(qc, kc, vc, with_scores=False)
+    again = c.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "forward is not deterministic"
+    del again
+
+    wins = gen.sample_windows(sh, n_win)
+    rows = gen.sample_special(sh, N_SPECIAL_ROWS)
+    wtok = torch.from_numpy(window_token_ids(sh)[wins].reshape(-1)).cuda()
+    stok = torch.from_numpy(special_token_ids(sh)[rows]).cuda()
+    o_img = to_host(out.view(sh.m_tokens, sh.n_heads, sh.head_dim).index_select(0, wtok))
+    o_spec = to_host(out.view(sh.m_tokens, sh.n_heads, sh.head_dim).index_select(0, stok))
+    gidx = idx.index_select(0, torch.from_numpy(wins).cuda()).cpu().numpy()
+    goc = to_host(oc.index_select(0, torch.from_numpy(wins).cuda()))
+    gpooled = [x.float().cpu().numpy() for x in (qc, kc, vc)]
+    del out, qc, kc, vc, oc, idx
+    torch.cuda.empty_cache()
+
+    log(f"[{name}] oracle: pooling ({time.time() - t0:.0f} s)")
+    pooled = [oracle.pool(sh, x) for x in (c.q, c.k, c.v)]
+    for g, o, what in zip(gpooled, pooled, "QKV"):
+        assert np.array_equal(g.view(np.uint32), o.view(np.uint32)), f"{name}: pooled {what} differs"
+    qc_h, kc_h, vc_h = pooled
+
+    log(f"[{name}] oracle: compressed attention + top-k for {len(wins)} windows ({time.time() - t0:.0f} s)")
+    ooc, oidx, osc, amax = oracle.compressed(sh, qc_h, kc_h, vc_h, wins)
+    assert_close(goc, ooc, sh.dtype, f"{name} O'_comp")
+    gs = oracle.guide_scores(sh, qc_h, kc_h, wins, gidx)
+    banded = check_topk(sh, gidx, oidx, osc, amax, gs)
+    log(f"[{name}] top-k: {banded} of {gidx.shape[0] * gidx.shape[1]} (window, head) rows in the tie band")
+
+    log(f"[{name}] oracle: selection + gate ({time.time() - t0:.0f} s)")
+    osel = oracle.select(sh, c.q, c.k, c.v, wins, gidx)
+    oimg = oracle.gate_combine(sh, c.q, c.wg, wins, ooc, osel)
+    mx, mean, rel = assert_close(o_img.reshape(oimg.shape), oimg, sh.dtype, f"{name} O_img (sampled)")
+    log(f"[{name}] O_img: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}")
+
+    log(f"[{name}] oracle: special attention for {len(rows)} rows ({time.time() - t0:.0f} s)")
+    ospec = oracle.special(sh, c.q, c.k, c.v, rows)
+    mx, mean, rel = assert_close(o_spec, ospec, sh.dtype, f"{name} O_spec (sampled)")
+    log(f"[{name}] O_spec: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}; done in {time.time() - t0:.0f} s")
