@@ -40,34 +40,58 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-windows", type=int, default=64)
     ap.add_argument("--cpu-special", type=int, default=16)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters) and exit")
     return ap.parse_args()
 
 
-def kernel_sources_hash() -> str:
+def copy_probe(mib: int):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+
+
+KERNEL_SOURCES = {
+    "flash_kernel<bf16,4,topk>": ("flash.hip", "gsa_device.h", "gsa_kernels.h"),
+    "flash_kernel<bf16,4,partial>": ("flash.hip", "gsa_device.h", "gsa_kernels.h"),
+    "select_kernel<bf16>": ("select.hip", "gsa_device.h", "gsa_kernels.h"),
+    "pool_kernel<bf16>": ("pool.hip", "gsa_device.h", "gsa_kernels.h"),
+}
+
+
+def kernel_sources_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_global_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "sparse_global_attention_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches the current sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch (fetched + written) from the committed rocprofv3 counter summary
+    profiles/hbm_traffic_<workload>.md, or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload.split()[0]}.md")
     if not os.path.exists(path):
         return None
-    try:
-        rec = json.load(open(path)).get(kernel)
-    except (ValueError, OSError):
-        return None
-    if not rec or rec.get("workload") != workload or rec.get("sources") != kernel_sources_hash():
-        return None
-    return rec.get("bytes_per_launch")
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] == kernel:
+            if cells[6] != kernel_sources_hash(kernel):
+                return None
+            return round((float(cells[4]) + float(cells[5])) * 1e9)
+    return None
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Use --gpus 1.", file=sys.stderr)
@@ -154,15 +178,15 @@ def main():
     # the attention kernels are the heaviest launches; report the larger one's roofline
     esz = 2 if sh.dtype == gen.BF16 else 4
     if st["compressed_topk"] >= st["special"]:
-        kname, kms, kflops = "flash_kernel<topk> (compressed attention + streaming top-k)", st["compressed_topk"], fl["compressed"]
-        ktag = "compressed_topk"
+        kname, kms, kflops = "flash_kernel<bf16,4,topk>", st["compressed_topk"], fl["compressed"]
+        kdesc = "compressed attention fused with the streaming top-k (gsa_compressed_attn_topk)"
     else:
-        kname, kms, kflops = "flash_kernel<partial> + merge (special-token attention)", st["special"], fl["special"]
-        ktag = "special"
+        kname, kms, kflops = "flash_kernel<bf16,4,partial>", st["special"], fl["special"]
+        kdesc = "special-token attention partials (gsa_special_attn, incl. the small merge kernel)"
     achieved = kflops / (kms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": measured_traffic(ktag, sh.name),
-                "kernel": kname, "work_per_launch_flop": kflops, "avg_launch_ms": round(kms, 4)}
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(kname, sh.name),
+                "kernel": kname, "what": kdesc, "work_per_launch_flop": kflops, "avg_launch_ms": round(kms, 4)}
 
     # HBM view of the memory-bound steps (algorithmic bytes)
     pool_bytes = 3 * sh.m_img * H * d * esz + 3 * sh.n_windows * H * d * esz
@@ -179,7 +203,6 @@ def main():
         "select_gather_bytes": gather_bytes,
         "wall_s_timed_region": round(t_wall, 3),
         "input_gen_s": round(t_gen, 1),
-        "sources": kernel_sources_hash(),
     }
     del ws_spec, ws_sel, o2, osel
 
