@@ -170,16 +170,19 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
   const Geometry& geo = p.g;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int ql = lane & 15, g = lane >> 4;
+  // Head-major order: all waves in flight gather from the same head's K/V
+  // blocks (M' x 4 KB), a working set the 256 MB Infinity Cache can hold a
+  // large part of, instead of all heads' blocks at once.
   const int64_t item = (int64_t)blockIdx.x * 4 + wv;
   if (item >= geo.n_windows * geo.n_heads) return;
-  const int64_t win = item / geo.n_heads;
-  const int64_t h = item % geo.n_heads;
+  const int64_t h = item / geo.n_windows;
+  const int64_t win = item % geo.n_windows;
   const int64_t H = geo.n_heads;
   const int s2 = (int)(geo.pool * geo.pool);
   const int K = p.topk;
   const float c = p.scale_log2;
 
-  const int32_t* trow = p.topk_idx + item * K;
+  const int32_t* trow = p.topk_idx + (win * geo.n_heads + h) * K;
   const int tr0 = lane < K ? trow[lane] : -1;
   const int tr1 = lane + 64 < K ? trow[lane + 64] : -1;
   const int n_chunks = (int)((K * geo.sb + 31) / 32);
@@ -195,16 +198,14 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
     f32x4 o[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    SelChunk<T> cur, nxt;
-    if (n_chunks > 0) load_chunk<T>(cur, p, h, 0, ql, g, tr0, tr1);
-    for (int ci = 0; ci < n_chunks; ++ci) {
-      if (ci + 1 < n_chunks) load_chunk<T>(nxt, p, h, ci + 1, ql, g, tr0, tr1);
-      f32x4 s0 = F::qk(cur.k[0], qf);
-      f32x4 s1 = F::qk(cur.k[1], qf);
+    // One chunk: scores of 32 key slots, online softmax, PV.
+    auto process = [&](const SelChunk<T>& ch) {
+      f32x4 s0 = F::qk(ch.k[0], qf);
+      f32x4 s1 = F::qk(ch.k[1], qf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bool v0 = cur.jv >= 0 && cur.kkv0 + e < s2;
-        const bool v1 = cur.jv >= 0 && cur.kkv0 + 4 + e < s2;
+        const bool v0 = ch.jv >= 0 && ch.kkv0 + e < s2;
+        const bool v1 = ch.jv >= 0 && ch.kkv0 + 4 + e < s2;
         if (!v0) s0[e] = -INFINITY;
         if (!v1) s1[e] = -INFINITY;
       }
@@ -229,9 +230,25 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
         ps += p0[e] + p1[e];
       }
       l_run += ps;
-      F::pv(cur.v, p0, p1, o);
-      if (ci + 1 < n_chunks) cur = nxt;
+      F::pv(ch.v, p0, p1, o);
+    };
+
+    // Two chunk buffers alternate so that two chunks of gathers are always in
+    // flight; no register copies (a copy would wait for its loads).
+    SelChunk<T> A, B;
+    load_chunk<T>(A, p, h, 0, ql, g, tr0, tr1);
+    load_chunk<T>(B, p, h, 1, ql, g, tr0, tr1);
+    int ci = 0;
+    for (; ci + 3 < n_chunks; ci += 2) {
+      process(A);
+      load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1);
+      process(B);
+      load_chunk<T>(B, p, h, ci + 3, ql, g, tr0, tr1);
     }
+    process(A);
+    if (ci + 2 < n_chunks) load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1);
+    if (ci + 1 < n_chunks) process(B);
+    if (ci + 2 < n_chunks) process(A);
 
     float l = l_run + xor_lane(l_run, 16);
     l = l + xor_lane(l, 32);
