@@ -365,3 +365,20 @@ def test_clustered_recipe_windows_share_a_centroid():
     spread = K[wt].std(axis=1)  # within-window spread = the 0.1 noise
     assert 0.06 < spread.mean() < 0.14
     assert K[special_token_ids(sh)].std() > 0.7
+
+
+def test_guide_scores_are_the_raw_dot_products():
+    """S_ij = Q_comp_i . K_comp_j, unscaled (section "压缩分支", guide-score equation);
+    integer-valued pooled rows make the products exact, so equality is exact."""
+    sh = shape(head_dim=8, topk=5)
+    qc, kc, _ = _int_pooled(sh, 9)
+    wins = np.array([0, 3, sh.n_windows - 1])
+    idx = np.array([[[1, 0, 7, -1, 5]] * sh.n_heads] * 3, np.int32)
+    got = oracle.guide_scores(sh, qc, kc, wins, idx)
+    for a, i in enumerate(wins):
+        for h in range(sh.n_heads):
+            for t, j in enumerate(idx[a, h]):
+                if j < 0:
+                    assert np.isnan(got[a, h, t])
+                else:
+                    assert got[a, h, t] == float(qc[i, h].astype(np.int64) @ kc[j, h].astype(np.int64))
