@@ -223,20 +223,19 @@ struct TileLoader {
   static_assert(NV >= 1 && NV * NT == kKT * VPR, "tile must split evenly over the workgroup");
   uint4 kr[NV], vr[NV];
 
+  // Rows past the end of the range re-read the last row: their scores are
+  // masked to -inf and their probabilities are exactly 0, so the values never
+  // count.  Keeping every load unconditional lets the compiler count the loads
+  // in flight and wait only for the oldest tile, not drain the queue.
   __device__ void load(const T* K, const T* V, int64_t stride, int64_t hoff, int64_t key0,
                        int64_t kend, int tid) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int idx = tid + i * NT;
       int key = idx / VPR, c = idx % VPR;
-      int64_t kk = key0 + key;
-      if (kk < kend) {
-        kr[i] = ld16(K + kk * stride + hoff + c * VE);
-        vr[i] = ld16(V + kk * stride + hoff + c * VE);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int64_t kk = key0 + key < kend ? key0 + key : kend - 1;
+      kr[i] = ld16(K + kk * stride + hoff + c * VE);
+      vr[i] = ld16(V + kk * stride + hoff + c * VE);
     }
   }
   __device__ void store(T* kt, T* vt, int tid) const {
