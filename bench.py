@@ -154,6 +154,7 @@ def main():
     osel = torch.empty((sh.m_img, H, d), dtype=torch.float32, device=dev)
     ws_spec = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_SPECIAL)), dtype=torch.uint8, device=dev)
     ws_sel = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_SELECT)), dtype=torch.uint8, device=dev)
+    ws_cmp = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_COMPRESSED)), dtype=torch.uint8, device=dev)
     o2 = torch.empty_like(dq)
 
     def timed(fn, reps):
@@ -170,7 +171,7 @@ def main():
     reps = max(2, args.steps)
     st = {}
     st["pool"] = timed(lambda: gsa.gsa_pool(cfg, dq, dk, dv, qc, kc, vc, stream=stream), reps)
-    st["compressed_topk"] = timed(lambda: gsa.gsa_compressed_attn_topk(cfg, qc, kc, vc, oc, idx, stream=stream), reps)
+    st["compressed_topk"] = timed(lambda: gsa.gsa_compressed_attn_topk(cfg, qc, kc, vc, oc, idx, None, ws_cmp, stream=stream), reps)
     st["special"] = timed(lambda: gsa.gsa_special_attn(cfg, dq, dk, dv, o2, ws_spec, stream=stream), reps)
     st["select_standalone"] = timed(lambda: gsa.gsa_select_attn(cfg, dq, dk, dv, idx, osel, ws_sel, stream=stream), reps)
     st["gate_combine"] = timed(lambda: gsa.gsa_gate_combine(cfg, dq, dwg, None, oc, osel, o2, stream=stream), reps)
@@ -204,7 +205,7 @@ def main():
         "wall_s_timed_region": round(t_wall, 3),
         "input_gen_s": round(t_gen, 1),
     }
-    del ws_spec, ws_sel, o2, osel
+    del ws_spec, ws_sel, ws_cmp, o2, osel
 
     # ---- dense comparator at the same shape --------------------------------------
     if not args.no_dense:

@@ -65,7 +65,8 @@ typedef enum {
   GSA_OP_FORWARD = 0, /* gsa_forward */
   GSA_OP_SPECIAL = 1, /* gsa_special_attn */
   GSA_OP_SELECT = 2,  /* gsa_select_attn */
-  GSA_OP_DENSE = 3    /* gsa_dense_attn */
+  GSA_OP_DENSE = 3,   /* gsa_dense_attn */
+  GSA_OP_COMPRESSED = 4 /* gsa_compressed_attn_topk */
 } gsa_op;
 
 #define GSA_MAX_CTX_FRAMES 16
@@ -99,19 +100,22 @@ gsa_status gsa_pool(const gsa_config* cfg, const void* q, const void* k, const v
                     void* kc, void* vc, void* stream);
 
 /*
- * Compressed attention fused with a streaming top-k over the guide scores
- * (section "压缩分支": O'_comp = Attention(Q_comp, K_comp, V_comp) and
- * S_guide = Q_comp K_comp^T; section "选择分支": TopKSelect of the most
- * relevant windows; section "高效 Triton Kernel 实现": top-k kept while the
- * score tiles are on chip, the score matrix is never stored).  Softmax over
- * all M' windows with the config scale; top-k over the raw scores of the
- * candidate windows (all windows, minus the context frames' windows when
- * ctx_exclude_from_topk is set), per head.  Writes oc, topk_idx and, if not
- * NULL, topk_score.
+ * Compressed attention and the top-k over the guide scores (section "压缩分支":
+ * O'_comp = Attention(Q_comp, K_comp, V_comp) and S_guide = Q_comp K_comp^T;
+ * section "选择分支": TopKSelect of the most relevant windows; section
+ * "高效 Triton Kernel 实现": the top-k is found from score tiles on chip, the
+ * M' x M' score matrix is never stored).  Softmax over all M' windows with
+ * the config scale; top-k over the raw scores of the candidate windows (all
+ * windows, minus the context frames' windows when ctx_exclude_from_topk is
+ * set), per head.  Writes oc, topk_idx and, if not NULL, topk_score.
+ * The attention sweep also records a lower bound of the best score in each
+ * group of key tiles; a score-only sweep then keeps the keys that reach the
+ * k-th best bound and ranks them (exact; a block whose candidates do not fit
+ * is redone with streaming heaps).  Workspace: GSA_OP_COMPRESSED bytes.
  */
 gsa_status gsa_compressed_attn_topk(const gsa_config* cfg, const void* qc, const void* kc,
                                     const void* vc, float* oc, int32_t* topk_idx,
-                                    float* topk_score, void* stream);
+                                    float* topk_score, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Selection-branch attention (section "选择分支": each image query attends the

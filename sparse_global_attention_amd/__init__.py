@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 GSA_OK, GSA_ERR_INVALID_ARG, GSA_ERR_SHAPE, GSA_ERR_UNSUPPORTED, GSA_ERR_WORKSPACE, GSA_ERR_HIP = range(6)
 GSA_BF16, GSA_F32 = 0, 1
-GSA_OP_FORWARD, GSA_OP_SPECIAL, GSA_OP_SELECT, GSA_OP_DENSE = range(4)
+GSA_OP_FORWARD, GSA_OP_SPECIAL, GSA_OP_SELECT, GSA_OP_DENSE, GSA_OP_COMPRESSED = range(5)
 GSA_MAX_CTX_FRAMES = 16
 
 EXPORTS = ("gsa_workspace_size", "gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn",
@@ -77,7 +77,7 @@ _CFG = ctypes.POINTER(GSAConfig)
 _sig = {
     "gsa_workspace_size": [_CFG, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
     "gsa_pool": [_CFG, _P, _P, _P, _P, _P, _P, _P],
-    "gsa_compressed_attn_topk": [_CFG, _P, _P, _P, _P, _P, _P, _P],
+    "gsa_compressed_attn_topk": [_CFG, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_select_attn": [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_special_attn": [_CFG, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_gate_combine": [_CFG, _P, _P, _P, _P, _P, _P, _P],
@@ -132,9 +132,10 @@ def gsa_pool(cfg, q, k, v, qc, kc, vc, stream=None):
                          _stream(stream)), "gsa_pool")
 
 
-def gsa_compressed_attn_topk(cfg, qc, kc, vc, oc, topk_idx, topk_score=None, stream=None):
+def gsa_compressed_attn_topk(cfg, qc, kc, vc, oc, topk_idx, topk_score, ws, ws_bytes=None, stream=None):
+    wsb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(_lib.gsa_compressed_attn_topk(ctypes.byref(cfg), _ptr(qc), _ptr(kc), _ptr(vc), _ptr(oc),
-                                         _ptr(topk_idx), _ptr(topk_score), _stream(stream)),
+                                         _ptr(topk_idx), _ptr(topk_score), _ptr(ws), wsb, _stream(stream)),
            "gsa_compressed_attn_topk")
 
 

@@ -37,6 +37,8 @@
 // every tile.
 #include <math.h>
 
+#include <type_traits>
+
 #include "gsa_device.h"
 #include "gsa_kernels.h"
 
@@ -238,6 +240,27 @@ struct TileLoader {
       vr[i] = ld16(V + kk * stride + hoff + c * VE);
     }
   }
+  // K only (score-only sweep)
+  __device__ void load_k(const T* K, int64_t stride, int64_t hoff, int64_t key0, int64_t kend, int tid) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int idx = tid + i * NT;
+      int key = idx / VPR, c = idx % VPR;
+      const int64_t kk = key0 + key < kend ? key0 + key : kend - 1;
+      kr[i] = ld16(K + kk * stride + hoff + c * VE);
+    }
+  }
+  __device__ void store_k(T* kt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int idx = tid + i * NT;
+      int key = idx / VPR, c = idx % VPR;
+      if constexpr (sizeof(T) == 2)
+        st16(kt + TL::chunk(key, c), kr[i]);
+      else
+        st16(kt + key * TL::KSTRIDE + c * VE, kr[i]);
+    }
+  }
   __device__ void store(T* kt, T* vt, int tid) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -352,6 +375,19 @@ __device__ __forceinline__ bool excluded_window(const FlashParams& p, int64_t ke
   return false;
 }
 
+// Excluded keys of the 32-key tile starting at key0, as a bit mask (bit i =
+// key key0 + i).  Uniform across the wave.
+template <typename P>
+__device__ __forceinline__ uint32_t excluded_mask(const P& p, int64_t key0) {
+  uint32_t m = 0;
+  for (int x = 0; x < p.n_excl; ++x) {
+    const int64_t b = (int64_t)p.excl_frames[x] * p.wins_per_frame, e = b + p.wins_per_frame;
+    const int64_t lo = b > key0 ? b - key0 : 0, hi = e < key0 + kKT ? e - key0 : kKT;
+    if (lo < hi) m |= (uint32_t)((hi - lo == 32 ? 0xffffffffull : ((1ull << (hi - lo)) - 1)) << lo);
+  }
+  return m;
+}
+
 // ---- the kernel ---------------------------------------------------------------
 template <typename T, int WAVES, int MODE>
 __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
@@ -388,6 +424,7 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
   float m_run = -INFINITY, l_run = 0.0f;
   bool first = true;
   const float c = p.scale_log2;
+  const float rc = 1.0f / c;
 
   TopkState tk;
   if constexpr (MODE == kFlashTopk) {
@@ -400,12 +437,18 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
     tk.tau_u = -INFINITY;
   }
 
+  // kFlashBound: running max over the current group of fl(tile max u + m),
+  // the largest |m| seen in the group, the group's last tile and its index
+  float gb = -INFINITY, gm_abs = 0.0f;
+  int gend = p.group_tiles - 1, gi = 0;
+
   // Key tiles of this split: tile t covers keys kb + 32t .. kb + 32t + 31.
   // Prefetches past the last tile re-read the last tile (never used), so the
   // load/store pattern has no branches and the compiler can keep two tiles of
   // loads in flight across the barriers.
   const int64_t kb = p.kbeg[split], ke = p.kend[split];
   const int n_tiles = (int)((ke - kb + kKT - 1) / kKT);
+  if (gend > n_tiles - 1) gend = n_tiles - 1;
   auto tile_key = [&](int t) { return kb + (int64_t)(t < n_tiles ? t : n_tiles - 1) * kKT; };
   TileLoader<T, WAVES * 64> sa, sb;
   sa.load(K, V, p.row_stride, hoff, tile_key(0), ke, tid);
@@ -485,6 +528,33 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
       mu = max3(max3(m0, m1, m2), max3(m3, m4, u[15]), u[15]);
     }
     mu = fmaxf(mu, xor_lane(mu, 32));
+    if constexpr (MODE == kFlashBound) {
+      // Lower bound of the tile's best candidate score, recovered from u and
+      // the running max before any rescale: |fl(fl(u + m) / c) - s| stays
+      // below 2^-22 |s| + 2^-24 |m / c|, so subtracting 2^-20 (|a| + |m / c|)
+      // gives a true lower bound.  Windows of excluded frames do not count.
+      float mt = mu;
+      const uint32_t em = p.n_excl ? excluded_mask(p, cur0) : 0u;
+      if (em) {
+        float x = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (!((em >> (8 * (i / 4) + 4 * hf + (i % 4))) & 1u)) x = fmaxf(x, u[i]);
+        mt = fmaxf(x, xor_lane(x, 32));
+      }
+      gb = fmaxf(gb, mt + m_run);
+      gm_abs = fmaxf(gm_abs, fabsf(m_run));
+      if (t == gend) {
+        if (hf == 0 && qvalid) {
+          const float a = gb * rc;
+          p.gbound[((int64_t)h * p.n_groups + gi) * p.n_q + qrow] = a - ldexpf(fabsf(a) + gm_abs * rc, -20);
+        }
+        gb = -INFINITY;
+        gm_abs = 0.0f;
+        gend = min(gend + p.group_tiles, n_tiles - 1);
+        ++gi;
+      }
+    }
     // lazy rescale: only when the max has grown by more than 2^kLazyRescale
     const bool need = mu > kLazyRescale;
     if (wave_any(need)) {
@@ -577,6 +647,360 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
   }
 }
 
+// ---- exact top-k from the group bounds ---------------------------------------
+// Order-preserving map of floats to unsigned keys and back.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// The next float above x (x finite or -inf): "y > x" is "y >= next_up(x)".
+// (both zeros map to +0 first, so the result is the smallest positive value)
+__device__ __forceinline__ float next_up(float x) { return key_value(order_key(x == 0.0f ? 0.0f : x) + 1u); }
+
+
+// theta = the k-th largest of the query's group bounds.  Each group bound is
+// at most the score of one distinct candidate key, so the k-th best candidate
+// score is >= theta, and every top-k key scores >= theta.  Radix select over
+// the order keys, bit by bit from the top; the two lanes of a query hold the
+// even and the odd groups (n_groups <= 2 * kMaxGroupsPerLane).  Returns -inf
+// when there are fewer than k finite bounds (then every candidate qualifies).
+constexpr int kMaxGroupsPerLane = 64;
+__device__ float kth_bound(const RefineParams& p, int64_t qrow, int h, int hf, bool qvalid) {
+  const int NG = p.n_groups;
+  const int per = (NG - hf + 1) / 2;
+  const float* src = p.gbound + (int64_t)h * NG * p.n_q + (qvalid ? qrow : 0);
+  uint32_t kv[kMaxGroupsPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxGroupsPerLane; ++i) {
+    // clamped, unconditional loads; out-of-range slots become key 0, which no
+    // candidate key below reaches (every candidate key has a bit set)
+    const int g = min(2 * i + hf, NG - 1);
+    const float x = src[(int64_t)g * p.n_q];
+    kv[i] = (qvalid && i < per) ? order_key(x) : 0u;
+  }
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxGroupsPerLane; ++i) cnt += kv[i] >= cand ? 1 : 0;
+    cnt += xor_lane(cnt, 32);
+    if (cnt >= p.topk) T = cand;
+  }
+  return T > order_key(-INFINITY) ? key_value(T) : -INFINITY;
+}
+
+__device__ __forceinline__ bool cand_better(Cand a, Cand b) { return a.s > b.s || (a.s == b.s && a.j < b.j); }
+
+// Candidate slots of one wave in LDS: slot i of query r at buf[i * 32 + r],
+// kRefineSlots slots per query.  The even lane of a query fills slots upwards
+// from 0 (its entries are [0, lo)), the odd lane downwards from the top (its
+// entries are (hi, kRefineSlots)); the slots between are free.  Within each
+// lane's range the entries are in ascending key order.
+struct CandSlots {
+  Cand* buf;
+  int r, hf;
+  int lo, hi;  // this lane's fill pointer; the partner's is fetched when needed
+  __device__ int count() const { return hf ? kRefineSlots - 1 - hi : lo; }
+  __device__ int slot(int i) const { return hf ? kRefineSlots - 1 - i : i; }  // i-th own entry
+};
+
+// Keep only the k best candidates (score desc, index asc) of every query of the
+// wave; returns the k-th best score (-inf if fewer than k).  Radix select on the
+// order keys of the scores; ties at the cut are decided by the lowest indices
+// with a second select on the index bits.  Entries move only inside their own
+// lane's range (a lane reads slot i before writing slot <= i), so the
+// compaction is done in place.  Every lane of the wave must call it.
+__device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
+  const int c = cs.count();
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int cnt = 0;
+    for (int i = 0; i < c; ++i) cnt += order_key(cs.buf[cs.slot(i) * 32 + cs.r].s) >= cand ? 1 : 0;
+    cnt += xor_lane(cnt, 32);
+    if (cnt >= K) T = cand;
+  }
+  // entries strictly above the cut score, and those equal to it
+  int gt = 0, eq = 0;
+  for (int i = 0; i < c; ++i) {
+    const uint32_t k = order_key(cs.buf[cs.slot(i) * 32 + cs.r].s);
+    gt += k > T ? 1 : 0;
+    eq += k == T ? 1 : 0;
+  }
+  gt += xor_lane(gt, 32);
+  eq += xor_lane(eq, 32);
+  // among the entries equal to the cut score keep the (K - gt) lowest indices:
+  // J = the largest index kept (smallest J with #{equal, index <= J} >= K - gt)
+  uint32_t J = 0xffffffffu;
+  const bool straddle = gt < K && gt + eq > K;
+  if (wave_any(straddle)) {
+    uint32_t lowJ = 0;  // build the answer from the top bit: count(index < lowJ + bit) < need -> set bit
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t probe = lowJ | (1u << b);
+      int cnt = 0;
+      for (int i = 0; i < c; ++i) {
+        const Cand x = cs.buf[cs.slot(i) * 32 + cs.r];
+        cnt += (order_key(x.s) == T && (uint32_t)x.j < probe) ? 1 : 0;
+      }
+      cnt += xor_lane(cnt, 32);
+      if (cnt < K - gt) lowJ = probe;
+    }
+    if (straddle) J = lowJ;
+  }
+  // squeeze the kept entries of this lane's range towards its end
+  int w = 0;
+  for (int i = 0; i < c; ++i) {
+    const Cand x = cs.buf[cs.slot(i) * 32 + cs.r];
+    const uint32_t k = order_key(x.s);
+    if (k > T || (k == T && (uint32_t)x.j <= J)) {
+      cs.buf[cs.slot(w) * 32 + cs.r] = x;
+      ++w;
+    }
+  }
+  if (cs.hf) cs.hi = kRefineSlots - 1 - w; else cs.lo = w;
+  cut = gt + eq >= K;
+  return cut ? key_value(T) : -INFINITY;
+}
+
+// One workgroup: WAVES x 32 queries of one head against all M' keys.  Key
+// tiles are staged in LDS as in flash_kernel (RSUB tiles of 32 keys per
+// barrier), but only S^T = K Q^T is formed.  Keys with score >= theta are
+// appended to the query's LDS slots; when the slots run low, the query keeps
+// only its current k best (so the slots never overflow) and from then on a key
+// must beat the k-th best score strictly (an equal score loses: it has a
+// higher index than every kept key).  At the end the candidates are ranked and
+// the first k written, sorted.  Requires k <= kRefineSlots / 2.
+constexpr int RSUB = 2;
+template <typename T, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
+  using TL = Tile<T>;
+  using F = Frag32<T>;
+  using Loader = TileLoader<T, WAVES * 64>;
+  constexpr int KBYTES = TL::K_ELEMS * (int)sizeof(T);
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // two stage buffers of RSUB key tiles each
+  auto tile_buf = [&](int stage, int j) { return reinterpret_cast<T*>(smem + (stage * RSUB + j) * KBYTES); };
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 31, hf = lane >> 5;
+  CandSlots cs;
+  cs.buf = reinterpret_cast<Cand*>(smem + 2 * RSUB * KBYTES) + wv * kRefineSlots * 32;
+  cs.r = r;
+  cs.hf = hf;
+  cs.lo = 0;
+  cs.hi = kRefineSlots - 1;
+  constexpr int QW = WAVES * 32;
+  const int64_t n_qt = (p.n_q + QW - 1) / QW;
+  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t qt = w % n_qt;
+  const int h = (int)(w / n_qt);
+  const int64_t qrow = qt * QW + wv * 32 + r;
+  const bool qvalid = qrow < p.n_q;
+  const int64_t hoff = (int64_t)h * kHeadDim;
+  const int Kk = p.topk;
+  const T* K = static_cast<const T*>(p.k);
+  typename F::Q qf = F::load_q(qvalid ? static_cast<const T*>(p.q) + qrow * p.row_stride + hoff : nullptr, hf);
+  // a key is a candidate when its score is >= tlo: theta at first, then just
+  // above the k-th best kept score (an equal score loses to the kept keys,
+  // which all have lower indices)
+  float tlo = kth_bound(p, qrow, h, hf, qvalid);
+  if (!qvalid) tlo = INFINITY;
+  int ntot = 0;  // candidates held for this lane's query (both lanes)
+  __builtin_amdgcn_s_waitcnt(0);
+  // compare raw scores as integers when every threshold of the wave is
+  // positive (order-preserving on the bit patterns then), else as floats;
+  // thresholds only grow, so the choice stays valid
+  const bool as_int = !wave_any(!(tlo > 0.0f));
+
+  const int64_t nk = p.n_q;
+  const int n_tiles = (int)((nk + kKT - 1) / kKT);
+  const int n_steps = (n_tiles + RSUB - 1) / RSUB;
+  auto tile_key = [&](int t) { return (int64_t)(t < n_tiles ? t : n_tiles - 1) * kKT; };
+  struct Stage {
+    Loader l[RSUB];
+  };
+  auto stage_load = [&](Stage& st, int u) {
+#pragma unroll
+    for (int j = 0; j < RSUB; ++j) st.l[j].load_k(K, p.row_stride, hoff, tile_key(u * RSUB + j), nk, tid);
+  };
+  auto stage_store = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int j = 0; j < RSUB; ++j) st.l[j].store_k(tile_buf(buf, j), tid);
+  };
+  Stage sa, sb;
+  stage_load(sa, 0);
+  stage_load(sb, 1);
+  stage_store(sa, 0);
+  stage_load(sa, 2);
+  lds_barrier();
+
+  // The sweep, compiled once for integer and once for float comparisons.
+  auto sweep = [&](auto int_tag) {
+    constexpr bool AS_INT = decltype(int_tag)::value;
+    // one 32-key tile t from LDS
+    auto tile = [&](int t, const T* kt) {
+      const int64_t cur0 = (int64_t)t * kKT;
+      f32x16 s = F::qk(kt, r, hf, qf);
+      if (cur0 + kKT > nk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (cur0 + 8 * (i / 4) + 4 * hf + (i % 4) >= nk) s[i] = -INFINITY;
+      }
+      // a score passes when >= tlo (and is not -inf: keys past the end)
+      const int tlo_bits = __float_as_int(tlo);
+      auto pass = [&](float x) {
+        if constexpr (AS_INT) return __float_as_int(x) >= tlo_bits;
+        else return x >= tlo && x != -INFINITY;
+      };
+      // 4-key group maxima first (the exact per-key test follows)
+      bool g[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        if constexpr (AS_INT) {
+          const int m = max(max(__float_as_int(s[4 * a]), __float_as_int(s[4 * a + 1])),
+                            max(__float_as_int(s[4 * a + 2]), __float_as_int(s[4 * a + 3])));
+          g[a] = m >= tlo_bits;
+        } else {
+          const float m = fmaxf(fmaxf(s[4 * a], s[4 * a + 1]), fmaxf(s[4 * a + 2], s[4 * a + 3]));
+          g[a] = m >= tlo && m != -INFINITY;
+        }
+      }
+      if (!wave_any(g[0] || g[1] || g[2] || g[3])) return;
+      // excluded keys of the tile, as this lane's bits (bit 4a+e = key 8a+4hf+e)
+      unsigned ex = 0;
+      if (p.n_excl) {
+        const uint32_t em = excluded_mask(p, cur0);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) ex |= ((em >> (8 * a + 4 * hf)) & 15u) << (4 * a);
+      }
+      // exact tests: bit 4a+e of km = key 8a+4hf+e is a candidate
+      auto keep_mask = [&]() {
+        unsigned km = 0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          if (wave_any(g[a])) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) km |= (pass(s[4 * a + e]) ? 1u : 0u) << (4 * a + e);
+          }
+        }
+        return km & ~ex;
+      };
+      unsigned km = keep_mask();
+      int need = __builtin_popcount(km);
+      int need_p = xor_lane(need, 32);  // outside any condition: every lane takes part
+      // 8 spare slots let whole groups be written (below)
+      if (wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
+        // keep the k best; afterwards the new candidates fit unless a tile
+        // brings more than kRefineSlots - k - 8 of them (exact path below)
+        bool cut;
+        const float kth = compact_slots(cs, Kk, cut);
+        if (cut) {
+          tlo = next_up(kth);
+          ntot = Kk;
+        }
+        km = keep_mask();
+        need = __builtin_popcount(km);
+        need_p = xor_lane(need, 32);
+      }
+      auto key_of = [&](int a, int e) { return (int)(cur0 + 8 * a + 4 * hf + e); };
+      if (!wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
+        // Whole groups: every lane writes the group's 4 keys, its kept keys
+        // compacted at its fill pointer and the others at pointer + e.  A kept
+        // key's slot is at most its own e, so a later kept key may overwrite
+        // an earlier dropped one but never the reverse; the dropped keys land
+        // in free slots (>= 8 are free, so the two ends never meet).
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          if (wave_any(g[a])) {
+            const unsigned gm = (km >> (4 * a)) & 15u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int off = ((gm >> e) & 1u) ? __builtin_popcount(gm & ((1u << e) - 1u)) : e;
+              const int sl = hf ? cs.hi - off : cs.lo + off;
+              cs.buf[sl * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
+            }
+            const int nkp = __builtin_popcount(gm);
+            cs.lo += hf ? 0 : nkp;
+            cs.hi -= hf ? nkp : 0;
+          }
+        }
+      } else {
+        // exact: one key at a time
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          if (wave_any((km >> (4 * a)) & 15u)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if ((km >> (4 * a + e)) & 1u) cs.buf[(hf ? cs.hi : cs.lo) * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
+              const int d = (km >> (4 * a + e)) & 1u;
+              cs.lo += hf ? 0 : d;
+              cs.hi -= hf ? d : 0;
+            }
+          }
+        }
+      }
+      ntot += need + need_p;
+    };
+
+    // one barrier step: RSUB tiles from stage buffer u%2, then move stage u+1
+    // from registers into the other buffer and reuse `nxt` for stage u+3
+    auto step = [&](int u, Stage& nxt) {
+#pragma unroll
+      for (int j = 0; j < RSUB; ++j) tile(u * RSUB + j, tile_buf(u & 1, j));
+      stage_store(nxt, (u + 1) & 1);
+      stage_load(nxt, u + 3);
+      lds_barrier();
+    };
+    for (int u = 0; u < n_steps; u += 2) {
+      step(u, sb);
+      step(u + 1, sa);
+    }
+  };
+  if (as_int)
+    sweep(std::integral_constant<bool, true>{});
+  else
+    sweep(std::integral_constant<bool, false>{});
+
+  // rank this lane's candidates against all of the query's and write the first k
+  const int c_me = cs.count(), c_ot = xor_lane(c_me, 32);
+  const int n = c_me + c_ot;
+  if (qvalid) {
+    int32_t* di = p.topk_idx + (qrow * p.n_heads + h) * Kk;
+    float* ds = p.topk_score ? p.topk_score + (qrow * p.n_heads + h) * Kk : nullptr;
+    const int lo0 = hf ? c_ot : c_me;  // the even lane's entries are slots [0, lo0)
+    for (int i0 = 0; i0 < c_me; i0 += 16) {
+      Cand x[16];
+      int rk[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        x[j] = i0 + j < c_me ? cs.buf[cs.slot(i0 + j) * 32 + r] : Cand{-INFINITY, 0x7fffffff};
+        rk[j] = 0;
+      }
+      for (int y = 0; y < n; ++y) {
+        const int sl = y < lo0 ? y : kRefineSlots - 1 - (y - lo0);
+        const Cand cy = cs.buf[sl * 32 + r];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) rk[j] += cand_better(cy, x[j]) ? 1 : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (i0 + j < c_me && rk[j] < Kk) {
+          di[rk[j]] = x[j].j;
+          if (ds) ds[rk[j]] = x[j].s;
+        }
+      }
+    }
+    for (int t = n + hf; t < Kk; t += 2) {
+      di[t] = -1;
+      if (ds) ds[t] = -INFINITY;
+    }
+  }
+}
+
 // Combine split partials: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
 template <typename T>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
@@ -622,6 +1046,7 @@ template <typename T>
 static hipError_t launch_flash_dt(int mode, const FlashParams& p, hipStream_t stream) {
   if (mode == kFlashFinal) return launch_flash_t<T, 4, kFlashFinal>(p, stream);
   if (mode == kFlashPartial) return launch_flash_t<T, 4, kFlashPartial>(p, stream);
+  if (mode == kFlashBound) return launch_flash_t<T, 4, kFlashBound>(p, stream);
   // top-k heaps take WAVES * k * 256 bytes of LDS: fewer waves for larger k
   if (p.topk <= 32) return launch_flash_t<T, 4, kFlashTopk>(p, stream);
   if (p.topk <= 64) return launch_flash_t<T, 2, kFlashTopk>(p, stream);
@@ -630,6 +1055,20 @@ static hipError_t launch_flash_dt(int mode, const FlashParams& p, hipStream_t st
 
 hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t stream) {
   return dtype == kBF16 ? launch_flash_dt<__bf16>(mode, p, stream) : launch_flash_dt<float>(mode, p, stream);
+}
+
+template <typename T>
+static hipError_t launch_refine_t(const RefineParams& p, hipStream_t stream) {
+  constexpr int WAVES = 4;
+  const int64_t blocks = (p.n_q + WAVES * 32 - 1) / (WAVES * 32) * p.n_heads;
+  if (blocks == 0) return hipSuccess;
+  const size_t lds = 2 * RSUB * (size_t)Tile<T>::K_ELEMS * sizeof(T) + (size_t)WAVES * kRefineSlots * 32 * sizeof(Cand);
+  hipLaunchKernelGGL((refine_kernel<T, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_refine(int dtype, const RefineParams& p, hipStream_t stream) {
+  return dtype == kBF16 ? launch_refine_t<__bf16>(p, stream) : launch_refine_t<float>(p, stream);
 }
 
 hipError_t launch_merge(int dtype, const MergeParams& p, hipStream_t stream) {

@@ -83,7 +83,26 @@ bool ptr_ok(const void* p) { return p != nullptr && ((uintptr_t)p & 15) == 0; }
 struct Plan {
   int n_split;  // special-attention key splits
   int64_t qc, kc, vc, oc, topk, kblk, vblk, spec_o, spec_lse, ctx_o, ctx_lse, total;
+  int n_groups, group_tiles;  // compressed step: key-tile groups of the score bounds
+  int64_t gbound;
 };
+
+// The compressed step's top-k: for k <= kRefineSlots / 2 the attention sweep
+// writes score bounds and refine_kernel finds the top-k; larger k use the
+// streaming-heap kernel.
+bool use_refine(const Call& c) { return c.topk <= kRefineSlots / 2; }
+
+// Groups of key tiles for the score bounds: at most 128 groups (a lane of the
+// refine kernel holds 64 of them), so that the k-th best group bound sits
+// close to the k-th best score and few keys pass it.
+void bound_groups(const Call& c, int* n_groups, int* group_tiles) {
+  const int64_t tiles = (c.g.n_windows + 31) / 32;
+  const int64_t target = 128;
+  int64_t gt = (tiles + target - 1) / target;
+  if (gt < 1) gt = 1;
+  *group_tiles = (int)gt;
+  *n_groups = (int)((tiles + gt - 1) / gt);
+}
 
 int special_splits(const Call& c) {
   const Geometry& g = c.g;
@@ -101,6 +120,7 @@ Plan make_plan(const Call& c, gsa_op op) {
   Plan p;
   memset(&p, 0, sizeof(p));
   p.n_split = special_splits(c);
+  bound_groups(c, &p.n_groups, &p.group_tiles);
   const int64_t pooled = g.n_windows * g.n_heads * kHeadDim * c.esz;
   const int64_t blk = g.n_windows * g.n_heads * g.sb * kHeadDim * c.esz;
   const int64_t spec_o = (int64_t)p.n_split * g.m_spec * g.n_heads * kHeadDim * 4;
@@ -120,6 +140,8 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.oc = take(g.n_windows * g.n_heads * kHeadDim * 4);
     p.topk = take(g.n_windows * g.n_heads * (int64_t)c.topk * 4);
   }
+  if ((op == GSA_OP_FORWARD || op == GSA_OP_COMPRESSED) && use_refine(c))
+    p.gbound = take((int64_t)p.n_groups * g.n_heads * g.n_windows * 4);
   if (op == GSA_OP_FORWARD || op == GSA_OP_SELECT) {
     p.kblk = take(blk);
     p.vblk = take(blk);
@@ -200,9 +222,15 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
   return launch_merge(c.dtype, m, st);
 }
 
-hipError_t run_compressed(const Call& c, const void* qc, const void* kc, const void* vc, float* oc, int32_t* idx,
-                          float* score, hipStream_t st) {
+// Compressed attention + exact top-k.  k <= kRefineSlots / 2: two launches,
+//  1. flash attention over all M' windows, also writing per-group score bounds;
+//  2. refine_kernel: theta from the bounds, score-only sweep collecting the
+//     keys >= theta, ranking -> topk.
+// Larger k: one launch of the streaming-heap kernel.
+hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const void* kc, const void* vc, float* oc,
+                          int32_t* idx, float* score, void* ws, hipStream_t st) {
   const Geometry& g = c.g;
+  if (g.n_windows == 0) return hipSuccess;
   FlashParams f = flash_base(c, qc, kc, vc);
   set_rows_identity(f, g.n_windows);
   f.n_splits = 1;
@@ -215,7 +243,29 @@ hipError_t run_compressed(const Call& c, const void* qc, const void* kc, const v
   f.wins_per_frame = g.wpf;
   f.n_excl = c.exclude ? c.n_ctx : 0;
   for (int i = 0; i < f.n_excl; ++i) f.excl_frames[i] = c.ctx[i];
-  return launch_flash(c.dtype, kFlashTopk, f, st);
+  if (!use_refine(c)) return launch_flash(c.dtype, kFlashTopk, f, st);
+  f.gbound = reinterpret_cast<float*>(at(ws, pl.gbound));
+  f.n_groups = pl.n_groups;
+  f.group_tiles = pl.group_tiles;
+  hipError_t e = launch_flash(c.dtype, kFlashBound, f, st);
+  if (e != hipSuccess) return e;
+
+  RefineParams r;
+  memset(&r, 0, sizeof(r));
+  r.q = qc;
+  r.k = kc;
+  r.row_stride = f.row_stride;
+  r.n_heads = f.n_heads;
+  r.n_q = g.n_windows;
+  r.gbound = f.gbound;
+  r.n_groups = pl.n_groups;
+  r.topk = c.topk;
+  r.wins_per_frame = g.wpf;
+  r.n_excl = f.n_excl;
+  for (int i = 0; i < f.n_excl; ++i) r.excl_frames[i] = f.excl_frames[i];
+  r.topk_idx = idx;
+  r.topk_score = score;
+  return launch_refine(c.dtype, r, st);
 }
 
 // Context frames' part of the selection softmax: image queries over all T_f tokens of each context frame.
@@ -284,7 +334,7 @@ gsa_status gsa_workspace_size(const gsa_config* cfg, gsa_op op, size_t* bytes) {
   gsa_status s = check_cfg(cfg, &c);
   if (s != GSA_OK) return s;
   if (!bytes) return GSA_ERR_INVALID_ARG;
-  if (op < GSA_OP_FORWARD || op > GSA_OP_DENSE) return GSA_ERR_INVALID_ARG;
+  if (op < GSA_OP_FORWARD || op > GSA_OP_COMPRESSED) return GSA_ERR_INVALID_ARG;
   *bytes = (size_t)make_plan(c, op).total;
   return GSA_OK;
 }
@@ -307,13 +357,15 @@ gsa_status gsa_pool(const gsa_config* cfg, const void* q, const void* k, const v
 }
 
 gsa_status gsa_compressed_attn_topk(const gsa_config* cfg, const void* qc, const void* kc, const void* vc, float* oc,
-                                    int32_t* topk_idx, float* topk_score, void* stream) {
+                                    int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes, void* stream) {
   Call c;
   gsa_status s = check_cfg(cfg, &c);
   if (s != GSA_OK) return s;
   if (!ptr_ok(qc) || !ptr_ok(kc) || !ptr_ok(vc) || !ptr_ok(oc) || !ptr_ok(topk_idx)) return GSA_ERR_INVALID_ARG;
   if (topk_score && !ptr_ok(topk_score)) return GSA_ERR_INVALID_ARG;
-  return hip_status(run_compressed(c, qc, kc, vc, oc, topk_idx, topk_score, static_cast<hipStream_t>(stream)));
+  Plan pl = make_plan(c, GSA_OP_COMPRESSED);
+  if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
+  return hip_status(run_compressed(c, pl, qc, kc, vc, oc, topk_idx, topk_score, ws, static_cast<hipStream_t>(stream)));
 }
 
 gsa_status gsa_select_attn(const gsa_config* cfg, const void* q, const void* k, const void* v,
@@ -399,7 +451,7 @@ gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, cons
   // 3. compressed attention + top-k
   float* oc = reinterpret_cast<float*>(at(ws, pl.oc));
   int32_t* idx = reinterpret_cast<int32_t*>(at(ws, pl.topk));
-  if (e == hipSuccess) e = run_compressed(c, pp.dst[0], pp.dst[1], pp.dst[2], oc, idx, nullptr, st);
+  if (e == hipSuccess) e = run_compressed(c, pl, pp.dst[0], pp.dst[1], pp.dst[2], oc, idx, nullptr, ws, st);
   // 4. fixed-context partial
   if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
   // 5. selection + upsample + gate

@@ -51,7 +51,12 @@ hipError_t launch_pool(int dtype, const PoolParams& p, int n_tensors, hipStream_
 // ---- tiled flash attention (special / dense / context / compressed+top-k) ----
 constexpr int kMaxRanges = 64;
 constexpr int kMaxExcl = 16;
-enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashTopk = 2 };
+// kFlashBound: compressed attention that also records, per group of key
+// tiles, a lower bound of the group's best candidate score (input of
+// refine_kernel, used for k <= kRefineSlots / 2).  kFlashTopk: compressed
+// attention with an exact streaming top-k in LDS heaps (larger k).
+enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashTopk = 2, kFlashBound = 3 };
+constexpr int kRefineSlots = 64;  // refine_kernel: LDS candidate slots per query
 
 struct FlashParams {
   const void* q;
@@ -78,8 +83,32 @@ struct FlashParams {
   int64_t wins_per_frame;
   int n_excl;                 // frames whose windows are not top-k candidates
   int excl_frames[kMaxExcl];
+  // kFlashBound: gbound [H][n_groups][n_q]; group g covers key tiles
+  // [g*group_tiles, (g+1)*group_tiles) of the single key range
+  float* gbound;
+  int n_groups, group_tiles;
 };
 hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t stream);
+
+// Exact top-k from the group bounds: theta = k-th best bound per query; a
+// score-only sweep keeps the candidate keys with score >= theta in LDS
+// (compacting to the current k best when the slots run low) and ranks them.
+struct RefineParams {
+  const void* q;
+  const void* k;
+  int64_t row_stride;
+  int n_heads;
+  int64_t n_q;      // queries = keys = M'
+  const float* gbound;
+  int n_groups;
+  int topk;
+  int64_t wins_per_frame;
+  int n_excl;
+  int excl_frames[kMaxExcl];
+  int32_t* topk_idx;
+  float* topk_score;
+};
+hipError_t launch_refine(int dtype, const RefineParams& p, hipStream_t stream);
 
 // Combine split partials into the final rows of o (input dtype).
 struct MergeParams {

@@ -72,7 +72,8 @@ class Case:
         oc = torch.empty((sh.n_windows, sh.n_heads, sh.head_dim), dtype=torch.float32, device=DEV)
         idx = torch.empty((sh.n_windows, sh.n_heads, sh.topk), dtype=torch.int32, device=DEV)
         sc = torch.empty((sh.n_windows, sh.n_heads, sh.topk), dtype=torch.float32, device=DEV) if with_scores else None
-        gsa.gsa_compressed_attn_topk(self.cfg, qc, kc, vc, oc, idx, sc)
+        ws = workspace(self.cfg, gsa.GSA_OP_COMPRESSED)
+        gsa.gsa_compressed_attn_topk(self.cfg, qc, kc, vc, oc, idx, sc, ws)
         return oc, idx, sc
 
     def select(self, idx):

@@ -97,8 +97,8 @@ def test_pointer_validation(lib):
     c = ctypes.byref(cfg(lib))
     assert lib.call_status("gsa_pool", c, None, A, A, A, A, A, None) == 1
     assert lib.call_status("gsa_pool", c, MISALIGNED, A, A, A, A, A, None) == 1
-    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, A, None, None, None) == 1
-    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, A, A, MISALIGNED, None) == 1
+    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, A, None, None, A, 1 << 30, None) == 1
+    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, A, A, MISALIGNED, A, 1 << 30, None) == 1
     assert lib.call_status("gsa_gate_combine", c, A, None, None, A, A, A + 64, None) == 1  # no wg and no gate
     assert lib.call_status("gsa_forward", c, A, A, A, A, A, A, 1 << 30, None) == 1  # o aliases q
     assert lib.call_status("gsa_special_attn", c, A, A, A, A, A, 1 << 30, None) == 1  # o aliases q
@@ -117,6 +117,10 @@ def test_workspace_validation(lib):
     assert lib.call_status("gsa_select_attn", c, A, A, A, A, o, A, need - 256, None) == 4
     need = lib.gsa_workspace_size(cc, lib.GSA_OP_SPECIAL)
     assert lib.call_status("gsa_special_attn", c, A, A, A, o, A, need - 1, None) == 4
+    need = lib.gsa_workspace_size(cc, lib.GSA_OP_COMPRESSED)
+    assert need > 0
+    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, o, o + 4096, None, A, need - 1, None) == 4
+    assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, o, o + 4096, None, None, need, None) == 1
 
 
 def test_binding_raises_gsa_error(lib):

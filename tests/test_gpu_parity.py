@@ -187,6 +187,27 @@ def test_topk_ties_go_to_lower_window():
     assert np.all(idx.cpu().numpy() == np.array([0, 1, 2], np.int32))
 
 
+def test_topk_ties_beyond_the_candidate_slots():
+    """Head 0: every key window identical, so each query's guide scores all tie
+    and every key reaches the threshold, far more than the candidate slots
+    hold; the slots are cut back to the k best (ties to the lower window), so
+    the answer is the k lowest windows.  Head 1 keeps its seeded keys and must
+    match the oracle."""
+    sh = GSAShape("ties-many 16f-16x16-h2-s4-k8", 16, 1, 16, 16, 2, 64, 4, 8, BF16, seed=41)
+    c = Case(sh)
+    qc, kc, vc = c.pool()
+    kc[:, 0] = kc[5, 0].clone()
+    oc, idx, sc = c.compressed(qc, kc, vc)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    assert np.all(gi[:, 0] == np.arange(sh.topk, dtype=np.int32))
+    wins = np.arange(sh.n_windows)
+    q64, k64, v64 = (to_host(x).astype(np.float32) for x in (qc, kc, vc))  # the oracle takes float32 pooled values
+    roc, ridx, rsc, amax = oracle.compressed(sh, q64, k64, v64, wins)
+    assert_close(to_host(oc), roc, sh.dtype, "ties-many O'_comp")
+    check_topk(sh, gi, ridx, rsc, amax, oracle.guide_scores(sh, q64, k64, wins, gi))
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "odd_f32"])
 def test_dense_comparator_rows(name):
     sh = SHAPES[name]
