@@ -225,30 +225,41 @@ struct TileLoader {
   static_assert(NV >= 1 && NV * NT == kKT * VPR, "tile must split evenly over the workgroup");
   uint4 kr[NV], vr[NV];
 
-  // Rows past the end of the range re-read the last row: their scores are
-  // masked to -inf and their probabilities are exactly 0, so the values never
-  // count.  Keeping every load unconditional lets the compiler count the loads
-  // in flight and wait only for the oldest tile, not drain the queue.
+  // A tile is rows key0 .. key0+31 of one head, read with buffer loads whose
+  // (scalar) base is the tile's first row: the per-thread byte offsets are the
+  // same for every tile, and rows at or past kend lie beyond the buffer's byte
+  // limit, which the hardware returns as zeros (those keys are masked: -inf
+  // scores, weight 0).  The loads are unconditional, so the compiler can count
+  // the loads in flight and wait only for the oldest tile.
+  static __device__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* X, int64_t stride, int64_t hoff, int64_t key0,
+                                                     int64_t kend) {
+    const int64_t bytes = (kend - key0) * stride * (int64_t)sizeof(T);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X + key0 * stride + hoff), (short)0,
+                                             (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+  }
+  static __device__ int chunk_offset(int64_t stride, int idx) {
+    const int key = idx / VPR, c = idx % VPR;
+    return (int)(((int64_t)key * stride + c * VE) * (int64_t)sizeof(T));
+  }
+  static __device__ uint4 buf16(__amdgpu_buffer_rsrc_t rs, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
   __device__ void load(const T* K, const T* V, int64_t stride, int64_t hoff, int64_t key0,
                        int64_t kend, int tid) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, stride, hoff, key0, kend);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V, stride, hoff, key0, kend);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      int idx = tid + i * NT;
-      int key = idx / VPR, c = idx % VPR;
-      const int64_t kk = key0 + key < kend ? key0 + key : kend - 1;
-      kr[i] = ld16(K + kk * stride + hoff + c * VE);
-      vr[i] = ld16(V + kk * stride + hoff + c * VE);
+      const int off = chunk_offset(stride, tid + i * NT);
+      kr[i] = buf16(rk, off);
+      vr[i] = buf16(rv, off);
     }
   }
   // K only (score-only sweep)
   __device__ void load_k(const T* K, int64_t stride, int64_t hoff, int64_t key0, int64_t kend, int tid) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, stride, hoff, key0, kend);
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int idx = tid + i * NT;
-      int key = idx / VPR, c = idx % VPR;
-      const int64_t kk = key0 + key < kend ? key0 + key : kend - 1;
-      kr[i] = ld16(K + kk * stride + hoff + c * VE);
-    }
+    for (int i = 0; i < NV; ++i) kr[i] = buf16(rk, chunk_offset(stride, tid + i * NT));
   }
   __device__ void store_k(T* kt, int tid) const {
 #pragma unroll
