@@ -881,6 +881,9 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
         }
       }
       if (!wave_any(g[0] || g[1] || g[2] || g[3])) return;
+      // groups with a passing key in some lane of the wave (uniform)
+      const unsigned gany = (wave_any(g[0]) ? 1u : 0u) | (wave_any(g[1]) ? 2u : 0u) |
+                            (wave_any(g[2]) ? 4u : 0u) | (wave_any(g[3]) ? 8u : 0u);
       // excluded keys of the tile, as this lane's bits (bit 4a+e = key 8a+4hf+e)
       unsigned ex = 0;
       if (p.n_excl) {
@@ -888,22 +891,56 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) ex |= ((em >> (8 * a + 4 * hf)) & 15u) << (4 * a);
       }
-      // exact tests: bit 4a+e of km = key 8a+4hf+e is a candidate
+      auto key_of = [&](int a, int e) { return (int)(cur0 + 8 * a + 4 * hf + e); };
+      // exact tests of group a: bit e = key 8a+4hf+e is a candidate
+      auto group_keep = [&](int a) {
+        unsigned gm = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gm |= (pass(s[4 * a + e]) ? 1u : 0u) << e;
+        return gm & ~(ex >> (4 * a)) & 15u;
+      };
+      // Whole group: every lane writes the group's 4 keys, its kept keys
+      // compacted at its fill pointer and the others at pointer + e.  A kept
+      // key's slot is at most its own e, so a later kept key may overwrite an
+      // earlier dropped one but never the reverse; the dropped keys land in
+      // free slots (needs >= 8 free, so the two ends never meet).
+      auto append_group = [&](int a, unsigned gm) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int off = ((gm >> e) & 1u) ? __builtin_popcount(gm & ((1u << e) - 1u)) : e;
+          const int sl = hf ? cs.hi - off : cs.lo + off;
+          cs.buf[sl * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
+        }
+        const int nkp = __builtin_popcount(gm);
+        cs.lo += hf ? 0 : nkp;
+        cs.hi -= hf ? nkp : 0;
+      };
+      // a passing group adds at most 8 candidates to a query (4 per lane)
+      if (!wave_any(ntot + 8 * __builtin_popcount(gany) + 8 > kRefineSlots)) {
+        // common case: room for whole groups, test and append in one pass
+        int need = 0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          if ((gany >> a) & 1u) {
+            const unsigned gm = group_keep(a);
+            append_group(a, gm);
+            need += __builtin_popcount(gm);
+          }
+        }
+        ntot += need + xor_lane(need, 32);  // outside any condition: every lane takes part
+        return;
+      }
+      // slots running low: count exactly, keep the k best if needed, append
       auto keep_mask = [&]() {
         unsigned km = 0;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if (wave_any(g[a])) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) km |= (pass(s[4 * a + e]) ? 1u : 0u) << (4 * a + e);
-          }
-        }
-        return km & ~ex;
+        for (int a = 0; a < 4; ++a)
+          if ((gany >> a) & 1u) km |= group_keep(a) << (4 * a);
+        return km;
       };
       unsigned km = keep_mask();
       int need = __builtin_popcount(km);
-      int need_p = xor_lane(need, 32);  // outside any condition: every lane takes part
-      // 8 spare slots let whole groups be written (below)
+      int need_p = xor_lane(need, 32);
       if (wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
         // keep the k best; afterwards the new candidates fit unless a tile
         // brings more than kRefineSlots - k - 8 of them (exact path below)
@@ -917,28 +954,10 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
         need = __builtin_popcount(km);
         need_p = xor_lane(need, 32);
       }
-      auto key_of = [&](int a, int e) { return (int)(cur0 + 8 * a + 4 * hf + e); };
       if (!wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
-        // Whole groups: every lane writes the group's 4 keys, its kept keys
-        // compacted at its fill pointer and the others at pointer + e.  A kept
-        // key's slot is at most its own e, so a later kept key may overwrite
-        // an earlier dropped one but never the reverse; the dropped keys land
-        // in free slots (>= 8 are free, so the two ends never meet).
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if (wave_any(g[a])) {
-            const unsigned gm = (km >> (4 * a)) & 15u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int off = ((gm >> e) & 1u) ? __builtin_popcount(gm & ((1u << e) - 1u)) : e;
-              const int sl = hf ? cs.hi - off : cs.lo + off;
-              cs.buf[sl * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
-            }
-            const int nkp = __builtin_popcount(gm);
-            cs.lo += hf ? 0 : nkp;
-            cs.hi -= hf ? nkp : 0;
-          }
-        }
+        for (int a = 0; a < 4; ++a)
+          if ((gany >> a) & 1u) append_group(a, (km >> (4 * a)) & 15u);
       } else {
         // exact: one key at a time
 #pragma unroll
