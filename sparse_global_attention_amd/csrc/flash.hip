@@ -784,8 +784,11 @@ __device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
 // only its current k best (so the slots never overflow) and from then on a key
 // must beat the k-th best score strictly (an equal score loses: it has a
 // higher index than every kept key).  At the end the candidates are ranked and
-// the first k written, sorted.  Requires k <= kRefineSlots / 2.
-constexpr int RSUB = 2;
+// the first k written, sorted.  Requires k <= kRefineMaxK.
+#ifndef GSA_RSUB
+#define GSA_RSUB 2
+#endif
+constexpr int RSUB = GSA_RSUB;  // 32-key tiles per barrier step
 template <typename T, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   using TL = Tile<T>;
@@ -930,50 +933,28 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
         ntot += need + xor_lane(need, 32);  // outside any condition: every lane takes part
         return;
       }
-      // slots running low: count exactly, keep the k best if needed, append
-      auto keep_mask = [&]() {
-        unsigned km = 0;
+      // slots running low: one group at a time, keeping the k best first when
+      // the group might not fit (a group adds at most 8; k + 8 + 8 <= slots)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          if ((gany >> a) & 1u) km |= group_keep(a) << (4 * a);
-        return km;
-      };
-      unsigned km = keep_mask();
-      int need = __builtin_popcount(km);
-      int need_p = xor_lane(need, 32);
-      if (wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
-        // keep the k best; afterwards the new candidates fit unless a tile
-        // brings more than kRefineSlots - k - 8 of them (exact path below)
-        bool cut;
-        const float kth = compact_slots(cs, Kk, cut);
-        if (cut) {
-          tlo = next_up(kth);
-          ntot = Kk;
-        }
-        km = keep_mask();
-        need = __builtin_popcount(km);
-        need_p = xor_lane(need, 32);
-      }
-      if (!wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          if ((gany >> a) & 1u) append_group(a, (km >> (4 * a)) & 15u);
-      } else {
-        // exact: one key at a time
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if (wave_any((km >> (4 * a)) & 15u)) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if ((km >> (4 * a + e)) & 1u) cs.buf[(hf ? cs.hi : cs.lo) * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
-              const int d = (km >> (4 * a + e)) & 1u;
-              cs.lo += hf ? 0 : d;
-              cs.hi -= hf ? d : 0;
+      for (int a = 0; a < 4; ++a) {
+        if ((gany >> a) & 1u) {
+          unsigned gm = group_keep(a);
+          int need = __builtin_popcount(gm), need_p = xor_lane(need, 32);
+          if (wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
+            bool cut;
+            const float kth = compact_slots(cs, Kk, cut);
+            if (cut) {
+              tlo = next_up(kth);
+              ntot = Kk;
             }
+            gm = group_keep(a);
+            need = __builtin_popcount(gm);
+            need_p = xor_lane(need, 32);
           }
+          append_group(a, gm);
+          ntot += need + need_p;
         }
       }
-      ntot += need + need_p;
     };
 
     // one barrier step: RSUB tiles from stage buffer u%2, then move stage u+1

@@ -87,10 +87,10 @@ struct Plan {
   int64_t gbound;
 };
 
-// The compressed step's top-k: for k <= kRefineSlots / 2 the attention sweep
+// The compressed step's top-k: for k <= kRefineMaxK the attention sweep
 // writes score bounds and refine_kernel finds the top-k; larger k use the
 // streaming-heap kernel.
-bool use_refine(const Call& c) { return c.topk <= kRefineSlots / 2; }
+bool use_refine(const Call& c) { return c.topk <= kRefineMaxK; }
 
 // Groups of key tiles for the score bounds: at most 128 groups (a lane of the
 // refine kernel holds 64 of them), so that the k-th best group bound sits
@@ -222,7 +222,7 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
   return launch_merge(c.dtype, m, st);
 }
 
-// Compressed attention + exact top-k.  k <= kRefineSlots / 2: two launches,
+// Compressed attention + exact top-k.  k <= kRefineMaxK: two launches,
 //  1. flash attention over all M' windows, also writing per-group score bounds;
 //  2. refine_kernel: theta from the bounds, score-only sweep collecting the
 //     keys >= theta, ranking -> topk.

@@ -53,10 +53,14 @@ constexpr int kMaxRanges = 64;
 constexpr int kMaxExcl = 16;
 // kFlashBound: compressed attention that also records, per group of key
 // tiles, a lower bound of the group's best candidate score (input of
-// refine_kernel, used for k <= kRefineSlots / 2).  kFlashTopk: compressed
+// refine_kernel, used for k <= kRefineMaxK).  kFlashTopk: compressed
 // attention with an exact streaming top-k in LDS heaps (larger k).
 enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashTopk = 2, kFlashBound = 3 };
-constexpr int kRefineSlots = 64;  // refine_kernel: LDS candidate slots per query
+#ifndef GSA_REFINE_SLOTS
+#define GSA_REFINE_SLOTS 64
+#endif
+constexpr int kRefineSlots = GSA_REFINE_SLOTS;  // refine_kernel: LDS candidate slots per query
+constexpr int kRefineMaxK = kRefineSlots - 16;   // the k best + one group (8) + 8 spare slots
 
 struct FlashParams {
   const void* q;

@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, element by
 element, on seeded inputs small enough for the whole oracle: the tiny fp32
 workload, the 32-frame bf16 workload, and edge shapes (ragged tails, s in
-{1, 2, 4, 8}, P = 0, fixed context, k beyond the candidate count, k = 64/128).
+{1, 2, 4, 8}, P = 0, fixed context, k beyond the candidate count, k = 40/64/128).
 """
 import numpy as np
 import pytest
@@ -27,6 +27,7 @@ SHAPES = {
     "ctx": GSAShape("ctx 6f-8x8-h2-s4-k3+ctx{0,3}", 6, 2, 8, 8, 2, 64, 4, 3, BF16, ctx_frames=(0, 3), seed=27),
     "ctx_f32": GSAShape("ctx 5f-8x8-h1-s2-k6+ctx{4}", 5, 1, 8, 8, 1, 64, 2, 6, F32, ctx_frames=(4,), seed=28),
     "k_clamp": GSAShape("kclamp 2f-8x8-h2-s4-k64", 2, 1, 8, 8, 2, 64, 4, 64, BF16, seed=29),
+    "k40": GSAShape("k40 10f-16x16-h2-s4-k40", 10, 1, 16, 16, 2, 64, 4, 40, BF16, seed=32),
     "k64": GSAShape("k64 10f-16x16-h2-s4-k64", 10, 1, 16, 16, 2, 64, 4, 64, BF16, seed=30),
     "k128": GSAShape("k128 10f-16x16-h1-s4-k128", 10, 1, 16, 16, 1, 64, 4, 128, BF16, seed=31),
 }
