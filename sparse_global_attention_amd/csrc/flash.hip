@@ -400,8 +400,10 @@ __device__ __forceinline__ uint32_t excluded_mask(const P& p, int64_t key0) {
 }
 
 // ---- the kernel ---------------------------------------------------------------
+// The bf16 bound mode asks for four workgroups per CU (at most 128 VGPRs),
+// the occupancy of the plain attention modes.
 template <typename T, int WAVES, int MODE>
-__global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
+__global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ? 4 : 1) void flash_kernel(FlashParams p) {
   using TL = Tile<T>;
   using F = Frag32<T>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -449,9 +451,16 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
   }
 
   // kFlashBound: running max over the current group of fl(tile max u + m),
-  // the largest |m| seen in the group, the group's last tile and its index
+  // the largest |m| seen in the group, the group's last tile and its index.
+  // The bounds of this head are written with buffer stores: scalar base (the
+  // head's slab) and group offset, one per-lane offset (the query row).
   float gb = -INFINITY, gm_abs = 0.0f;
   int gend = p.group_tiles - 1, gi = 0;
+  const int64_t slab = MODE == kFlashBound ? (int64_t)p.n_groups * p.n_q * 4 : 0;
+  const __amdgpu_buffer_rsrc_t gbr = __builtin_amdgcn_make_buffer_rsrc(
+      MODE == kFlashBound ? p.gbound + (int64_t)h * p.n_groups * p.n_q : nullptr, (short)0,
+      (int)(slab < 0x7fffffff ? slab : 0x7fffffff), 0x00020000);
+  const int gb_off = (int)(qrow * 4);
 
   // Key tiles of this split: tile t covers keys kb + 32t .. kb + 32t + 31.
   // Prefetches past the last tile re-read the last tile (never used), so the
@@ -558,7 +567,8 @@ __global__ __launch_bounds__(WAVES * 64) void flash_kernel(FlashParams p) {
       if (t == gend) {
         if (hf == 0 && qvalid) {
           const float a = gb * rc;
-          p.gbound[((int64_t)h * p.n_groups + gi) * p.n_q + qrow] = a - ldexpf(fabsf(a) + gm_abs * rc, -20);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a - ldexpf(fabsf(a) + gm_abs * rc, -20)), gbr, gb_off,
+                                                (int)((int64_t)gi * p.n_q * 4), 0);
         }
         gb = -INFINITY;
         gm_abs = 0.0f;
