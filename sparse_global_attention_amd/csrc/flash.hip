@@ -49,9 +49,12 @@ constexpr float kLazyRescale = 8.0f; // rescale only when the max grows by > 2^8
 
 // LDS tile of 32 keys.
 // bf16: K and V are stored row-major (one 128-byte row per key) with the
-// 16-byte chunks of row r permuted as c -> c ^ (r % 8): reads of the same
-// chunk by 8 consecutive rows then hit 8 different bank groups, with no
-// padding.  V is read transposed by ds_read_b64_tr_b16.
+// 16-byte chunks of row r permuted as c -> c ^ swz(r), no padding.  Two rows
+// share one 256-byte line of the 64 LDS banks (row parity picks the half), so
+// swz(r) = bit-reverse of (r >> 1) % 8: the same chunk read by 16 consecutive
+// rows (the K operand) lands on 16 different 16-byte bank groups, and the
+// transposing V reads (4 rows x 4 chunks per 32 lanes) see rows r and r + 2
+// in different 64-byte halves.
 // fp32: K rows padded by 16 bytes; V stored transposed (channel rows) since
 // there is no transposing read for 32-bit data.
 template <typename T>
@@ -64,7 +67,11 @@ struct Tile<__bf16> {
   static constexpr int V_ELEMS = kKT * kHeadDim;
   static constexpr int BYTES = (K_ELEMS + V_ELEMS) * 2;
   // element offset of 16-byte chunk c of key row `key`
-  __device__ static int chunk(int key, int c) { return key * kHeadDim + ((c ^ (key & 7)) << 3); }
+  __device__ static int swz(int key) {
+    const int x = (key >> 1) & 7;
+    return ((x & 1) << 2) | (x & 2) | (x >> 2);
+  }
+  __device__ static int chunk(int key, int c) { return key * kHeadDim + ((c ^ swz(key)) << 3); }
 };
 
 template <>
@@ -148,15 +155,18 @@ struct Frag32<__bf16> {
     const int G = lane >> 4, j = lane & 15;
     const int krow = 4 * (G >> 1) + (j >> 2);      // + 16m + 8c
     const int dv = 16 * (G & 1) + 4 * (j & 3);     // + 32n
-    const int sw = krow & 7;                       // chunk swizzle of every row this lane reads
+    // chunk swizzles of the rows this lane reads (16m + 8c + krow: 16m keeps
+    // swz, +8 flips its low bit)
+    const int sw_lo = TL::swz(krow), sw_hi = TL::swz(krow + 8);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const int off = (((4 * n + (dv >> 3)) ^ sw) << 3) + (dv & 7);
-        const __bf16* q0 = vt + (16 * m + krow) * kHeadDim + off;
-        bf16x4 lo = lds_read_tr16(q0);
-        bf16x4 hi = lds_read_tr16(q0 + 8 * kHeadDim);
+        const int off_lo = (((4 * n + (dv >> 3)) ^ sw_lo) << 3) + (dv & 7);
+        const int off_hi = (((4 * n + (dv >> 3)) ^ sw_hi) << 3) + (dv & 7);
+        const __bf16* q0 = vt + (16 * m + krow) * kHeadDim;
+        bf16x4 lo = lds_read_tr16(q0 + off_lo);
+        bf16x4 hi = lds_read_tr16(q0 + 8 * kHeadDim + off_hi);
         bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[n] = mfma32(a, p.v[m], o[n]);
       }
