@@ -557,12 +557,17 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       const float m3 = max3(u[9], u[10], u[11]), m4 = max3(u[12], u[13], u[14]);
       mu = max3(max3(m0, m1, m2), max3(m3, m4, u[15]), u[15]);
     }
-    mu = fmaxf(mu, xor_lane(mu, 32));
+    // mu is this lane's max over its 16 keys; the query's other 16 keys are in
+    // lane l^32.  The hot path needs no cross-lane step: whether any query of
+    // the wave must rescale is the same test on either half, and only the
+    // (cold) rescale combines the halves.
+    if constexpr (MODE == kFlashTopk) mu = fmaxf(mu, xor_lane(mu, 32));
     if constexpr (MODE == kFlashBound) {
       // Lower bound of the tile's best candidate score, recovered from u and
       // the running max before any rescale: |fl(fl(u + m) / c) - s| stays
       // below 2^-22 |s| + 2^-24 |m / c|, so subtracting 2^-20 (|a| + |m / c|)
       // gives a true lower bound.  Windows of excluded frames do not count.
+      // gb runs per lane; the halves are combined when the group is written.
       float mt = mu;
       const uint32_t em = p.n_excl ? excluded_mask(p, cur0) : 0u;
       if (em) {
@@ -570,13 +575,14 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (!((em >> (8 * (i / 4) + 4 * hf + (i % 4))) & 1u)) x = fmaxf(x, u[i]);
-        mt = fmaxf(x, xor_lane(x, 32));
+        mt = x;
       }
       gb = fmaxf(gb, mt + m_run);
       gm_abs = fmaxf(gm_abs, fabsf(m_run));
       if (t == gend) {
+        const float gq = fmaxf(gb, xor_lane(gb, 32));  // uniform branch: every lane takes part
         if (hf == 0 && qvalid) {
-          const float a = gb * rc;
+          const float a = gq * rc;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a - ldexpf(fabsf(a) + gm_abs * rc, -20)), gbr, gb_off,
                                                 (int)((int64_t)gi * p.n_q * 4), 0);
         }
@@ -587,9 +593,9 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       }
     }
     // lazy rescale: only when the max has grown by more than 2^kLazyRescale
-    const bool need = mu > kLazyRescale;
-    if (wave_any(need)) {
-      if (need) {
+    if (wave_any(mu > kLazyRescale)) {
+      if constexpr (MODE != kFlashTopk) mu = fmaxf(mu, xor_lane(mu, 32));
+      if (mu > kLazyRescale) {
         const float alpha = fast_exp2(-mu);
         m_run += mu;
         l_run *= alpha;
