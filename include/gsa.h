@@ -53,7 +53,8 @@ extern "C" {
 typedef enum {
   GSA_OK = 0,
   GSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad k, bad context frame, aliasing */
-  GSA_ERR_SHAPE = 2,       /* h or w not divisible by s, non-positive sizes, size overflow */
+  GSA_ERR_SHAPE = 2,       /* h or w not divisible by s, non-positive sizes, size overflow
+                              (M' > 2^31 - 1 windows, M >= 2^31 - 64 tokens, M*H*d > 2^40) */
   GSA_ERR_UNSUPPORTED = 3, /* d != 64, s > 8, k > 128, unknown dtype */
   GSA_ERR_WORKSPACE = 4,   /* workspace smaller than gsa_workspace_size() */
   GSA_ERR_HIP = 5          /* a HIP launch failed */

@@ -237,15 +237,15 @@ struct TileLoader {
 
   // A tile is rows key0 .. key0+31 of one head, read with buffer loads whose
   // (scalar) base is the tile's first row: the per-thread byte offsets are the
-  // same for every tile, and rows at or past kend lie beyond the buffer's byte
-  // limit, which the hardware returns as zeros (those keys are masked: -inf
-  // scores, weight 0).  The loads are unconditional, so the compiler can count
-  // the loads in flight and wait only for the oldest tile.
+  // same for every tile, and rows from `valid` (0..32) on lie beyond the
+  // buffer's byte limit, which the hardware returns as zeros (those keys are
+  // masked: -inf scores, weight 0).  The loads are unconditional, so the
+  // compiler can count the loads in flight and wait only for the oldest tile.
+  // The limit is 32-bit scalar arithmetic (32 rows of a token row stride).
   static __device__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* X, int64_t stride, int64_t hoff, int64_t key0,
-                                                     int64_t kend) {
-    const int64_t bytes = (kend - key0) * stride * (int64_t)sizeof(T);
+                                                     int valid) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X + key0 * stride + hoff), (short)0,
-                                             (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+                                             valid * (int)(stride * (int64_t)sizeof(T)), 0x00020000);
   }
   static __device__ int chunk_offset(int64_t stride, int idx) {
     const int key = idx / VPR, c = idx % VPR;
@@ -254,10 +254,10 @@ struct TileLoader {
   static __device__ uint4 buf16(__amdgpu_buffer_rsrc_t rs, int off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
   }
-  __device__ void load(const T* K, const T* V, int64_t stride, int64_t hoff, int64_t key0,
-                       int64_t kend, int tid) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, stride, hoff, key0, kend);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V, stride, hoff, key0, kend);
+  __device__ void load(const T* K, const T* V, int64_t stride, int64_t hoff, int64_t key0, int valid,
+                       int tid) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, stride, hoff, key0, valid);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V, stride, hoff, key0, valid);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int off = chunk_offset(stride, tid + i * NT);
@@ -266,8 +266,8 @@ struct TileLoader {
     }
   }
   // K only (score-only sweep)
-  __device__ void load_k(const T* K, int64_t stride, int64_t hoff, int64_t key0, int64_t kend, int tid) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, stride, hoff, key0, kend);
+  __device__ void load_k(const T* K, int64_t stride, int64_t hoff, int64_t key0, int valid, int tid) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, stride, hoff, key0, valid);
 #pragma unroll
     for (int i = 0; i < NV; ++i) kr[i] = buf16(rk, chunk_offset(stride, tid + i * NT));
   }
@@ -476,15 +476,22 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   // Prefetches past the last tile re-read the last tile (never used), so the
   // load/store pattern has no branches and the compiler can keep two tiles of
   // loads in flight across the barriers.
-  const int64_t kb = p.kbeg[split], ke = p.kend[split];
-  const int n_tiles = (int)((ke - kb + kKT - 1) / kKT);
+  // Positions inside the range are int32 (the host keeps token counts below
+  // 2^31 - 64), so the per-tile bookkeeping is scalar 32-bit arithmetic.
+  const int64_t kb = p.kbeg[split];
+  const int nk = (int)(p.kend[split] - kb);
+  const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
   if (gend > n_tiles - 1) gend = n_tiles - 1;
-  auto tile_key = [&](int t) { return kb + (int64_t)(t < n_tiles ? t : n_tiles - 1) * kKT; };
+  auto tile_rel = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
+  auto load_tile = [&](TileLoader<T, WAVES * 64>& ld, int t) {
+    const int rel = tile_rel(t);
+    ld.load(K, V, p.row_stride, hoff, kb + rel, min(nk - rel, kKT), tid);
+  };
   TileLoader<T, WAVES * 64> sa, sb;
-  sa.load(K, V, p.row_stride, hoff, tile_key(0), ke, tid);
-  sb.load(K, V, p.row_stride, hoff, tile_key(1), ke, tid);
+  load_tile(sa, 0);
+  load_tile(sb, 1);
   sa.store(kbuf0, kbuf0 + TL::K_ELEMS, tid);
-  sa.load(K, V, p.row_stride, hoff, tile_key(2), ke, tid);
+  load_tile(sa, 2);
   lds_barrier();
 
   // One tile: compute tile t from LDS, then move tile t+1 from register stage
@@ -493,16 +500,15 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   // (a copy would wait for the in-flight loads).
   auto step = [&](int t, TileLoader<T, WAVES * 64>& nxt) {
     // a step past the last tile (odd tile count) sees only masked keys
-    const int64_t cur0 = kb + (int64_t)t * kKT, cur_end = ke;
+    const int64_t cur0 = kb + (int64_t)t * kKT;
     const T* kt = (t & 1) ? kbuf1 : kbuf0;
     const T* vt = kt + TL::K_ELEMS;
     f32x16 s = F::qk(kt, r, hf, qf);
-    if (cur0 + kKT > cur_end) {
+    if (t >= n_full) {
+      const int lim = nk - t * kKT - 4 * hf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        int64_t key = cur0 + 8 * (i / 4) + 4 * hf + (i % 4);
-        if (key >= cur_end) s[i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i / 4) + (i % 4) >= lim) s[i] = -INFINITY;
     }
     if (first) {
       // the running max starts at the first tile's max (every tile holds a valid key)
@@ -617,7 +623,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
 
     T* kn = (t & 1) ? kbuf0 : kbuf1;
     nxt.store(kn, kn + TL::K_ELEMS, tid);
-    nxt.load(K, V, p.row_stride, hoff, tile_key(t + 3), ke, tid);
+    load_tile(nxt, t + 3);
     lds_barrier();
   };
   for (int t = 0; t < n_tiles; t += 2) {
@@ -856,16 +862,19 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   // thresholds only grow, so the choice stays valid
   const bool as_int = !wave_any(!(tlo > 0.0f));
 
-  const int64_t nk = p.n_q;
-  const int n_tiles = (int)((nk + kKT - 1) / kKT);
+  const int nk = (int)p.n_q;  // window counts are int32 (checked on the host)
+  const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
   const int n_steps = (n_tiles + RSUB - 1) / RSUB;
-  auto tile_key = [&](int t) { return (int64_t)(t < n_tiles ? t : n_tiles - 1) * kKT; };
+  auto tile_key = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
   struct Stage {
     Loader l[RSUB];
   };
   auto stage_load = [&](Stage& st, int u) {
 #pragma unroll
-    for (int j = 0; j < RSUB; ++j) st.l[j].load_k(K, p.row_stride, hoff, tile_key(u * RSUB + j), nk, tid);
+    for (int j = 0; j < RSUB; ++j) {
+      const int key0 = tile_key(u * RSUB + j);
+      st.l[j].load_k(K, p.row_stride, hoff, key0, min(nk - key0, kKT), tid);
+    }
   };
   auto stage_store = [&](const Stage& st, int buf) {
 #pragma unroll
@@ -883,12 +892,13 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
     constexpr bool AS_INT = decltype(int_tag)::value;
     // one 32-key tile t from LDS
     auto tile = [&](int t, const T* kt) {
-      const int64_t cur0 = (int64_t)t * kKT;
+      const int cur0 = t * kKT;
       f32x16 s = F::qk(kt, r, hf, qf);
-      if (cur0 + kKT > nk) {
+      if (t >= n_full) {
+        const int lim = nk - cur0 - 4 * hf;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (cur0 + 8 * (i / 4) + 4 * hf + (i % 4) >= nk) s[i] = -INFINITY;
+          if (8 * (i / 4) + (i % 4) >= lim) s[i] = -INFINITY;
       }
       // a score passes when >= tlo (and is not -inf: keys past the end)
       const int tlo_bits = __float_as_int(tlo);

@@ -64,8 +64,11 @@ gsa_status check_cfg(const gsa_config* c, Call* out) {
   g.wpf = (g.grid_h / g.pool) * g.wx;
   g.n_windows = g.n_frames * g.wpf;
   g.sb = (g.pool * g.pool + 7) / 8 * 8;
-  // window ids are int32 in topk_idx; keep every element count well inside int64
-  if (g.n_windows > INT32_MAX || g.m_tokens > ((int64_t)1 << 40) / (g.n_heads * kHeadDim)) return GSA_ERR_SHAPE;
+  // window ids are int32 in topk_idx, key positions inside a kernel's key range
+  // are int32, and every element count stays well inside int64
+  if (g.n_windows > INT32_MAX || g.m_tokens > INT32_MAX - 64 ||
+      g.m_tokens > ((int64_t)1 << 40) / (g.n_heads * kHeadDim))
+    return GSA_ERR_SHAPE;
 
   out->dtype = c->dtype;
   out->esz = c->dtype == GSA_BF16 ? 2 : 4;
