@@ -59,6 +59,9 @@ def cfg(lib, **kw):
     (dict(head_dim=128), 3), (dict(pool=16, grid_h=16, grid_w=16), 3), (dict(topk=129), 3), (dict(dtype=7), 3),
     (dict(topk=0), 1), (dict(ctx_frames=(4,)), 1), (dict(ctx_frames=(1, 1)), 1), (dict(scale=-1.0), 1),
     (dict(scale=float("nan")), 1), (dict(ctx_exclude_from_topk=2), 1),
+    # key positions are int32 inside the kernels: M = 64 N tokens must stay below 2^31 - 64
+    (dict(n_frames=(2**31 - 64) // 64, n_special=0, n_heads=1), 2),
+    (dict(n_frames=(2**31 - 64) // 64 - 1, n_special=0, n_heads=1), 0),
 ])
 def test_config_validation(lib, kw, status):
     size = ctypes.c_size_t()
