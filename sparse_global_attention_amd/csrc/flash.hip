@@ -730,7 +730,7 @@ __device__ float kth_bound(const RefineParams& p, int64_t qrow, int h, int hf, b
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < kMaxGroupsPerLane; ++i) cnt += kv[i] >= cand ? 1 : 0;
-    cnt += xor_lane(cnt, 32);
+    cnt = sum_halves(cnt);
     if (cnt >= p.topk) T = cand;
   }
   return T > order_key(-INFINITY) ? key_value(T) : -INFINITY;
@@ -764,7 +764,7 @@ __device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
     const uint32_t cand = T | (1u << b);
     int cnt = 0;
     for (int i = 0; i < c; ++i) cnt += order_key(cs.buf[cs.slot(i) * 32 + cs.r].s) >= cand ? 1 : 0;
-    cnt += xor_lane(cnt, 32);
+    cnt = sum_halves(cnt);
     if (cnt >= K) T = cand;
   }
   // entries strictly above the cut score, and those equal to it
@@ -774,8 +774,8 @@ __device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
     gt += k > T ? 1 : 0;
     eq += k == T ? 1 : 0;
   }
-  gt += xor_lane(gt, 32);
-  eq += xor_lane(eq, 32);
+  gt = sum_halves(gt);
+  eq = sum_halves(eq);
   // among the entries equal to the cut score keep the (K - gt) lowest indices:
   // J = the largest index kept (smallest J with #{equal, index <= J} >= K - gt)
   uint32_t J = 0xffffffffu;
@@ -789,7 +789,7 @@ __device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
         const Cand x = cs.buf[cs.slot(i) * 32 + cs.r];
         cnt += (order_key(x.s) == T && (uint32_t)x.j < probe) ? 1 : 0;
       }
-      cnt += xor_lane(cnt, 32);
+      cnt = sum_halves(cnt);
       if (cnt < K - gt) lowJ = probe;
     }
     if (straddle) J = lowJ;
@@ -966,7 +966,7 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
             need += __builtin_popcount(gm);
           }
         }
-        ntot += need + xor_lane(need, 32);  // outside any condition: every lane takes part
+        ntot += sum_halves(need);  // outside any condition: every lane takes part
         return;
       }
       // slots running low: one group at a time, keeping the k best first when
@@ -975,8 +975,8 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
       for (int a = 0; a < 4; ++a) {
         if ((gany >> a) & 1u) {
           unsigned gm = group_keep(a);
-          int need = __builtin_popcount(gm), need_p = xor_lane(need, 32);
-          if (wave_any(ntot + need + need_p + 8 > kRefineSlots)) {
+          int need = sum_halves(__builtin_popcount(gm));  // the query's new candidates
+          if (wave_any(ntot + need + 8 > kRefineSlots)) {
             bool cut;
             const float kth = compact_slots(cs, Kk, cut);
             if (cut) {
@@ -984,11 +984,10 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
               ntot = Kk;
             }
             gm = group_keep(a);
-            need = __builtin_popcount(gm);
-            need_p = xor_lane(need, 32);
+            need = sum_halves(__builtin_popcount(gm));
           }
           append_group(a, gm);
-          ntot += need + need_p;
+          ntot += need;
         }
       }
     };

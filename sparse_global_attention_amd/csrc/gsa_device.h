@@ -29,6 +29,15 @@ __device__ __forceinline__ int xor_lane(int x, int mask) {
   return __builtin_amdgcn_ds_bpermute(src, x);
 }
 
+// x + (x of lane l ^ 32), through v_permlane32_swap: a VALU lane exchange
+// between the two halves of the wave, no LDS round trip.  Each lane ends up
+// with its own value and its partner's (in some order), so the sum does not
+// depend on which is which.  Every lane of the wave must be active.
+__device__ __forceinline__ int sum_halves(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return (int)(r[0] + r[1]);
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
