@@ -124,8 +124,12 @@ struct Frag32<__bf16> {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(kt + TL::chunk(r, 4 * hf + ks));
     f32x16 s = {};
+    // raised wave priority while the matrix-core ops issue, so a wave that has
+    // them ready goes first and the others' VALU work fills in behind
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) s = mfma32(a[ks], q.v[ks], s);
+    __builtin_amdgcn_s_setprio(0);
     return s;
   }
   // P operand: the bf16 values of the lane's S^T elements; the row sum adds
@@ -152,6 +156,7 @@ struct Frag32<__bf16> {
   // channels 32n + 16(G%2) + 4(j%4) .. +3; the transposing read then hands
   // lane l exactly V[16m + 8c + 4hf + e'][32n + l%32] for e' = 0..3.
   __device__ static void pv(const __bf16* vt, int lane, const P& p, f32x16 o[2]) {
+    __builtin_amdgcn_s_setprio(1);
     const int G = lane >> 4, j = lane & 15;
     const int krow = 4 * (G >> 1) + (j >> 2);      // + 16m + 8c
     const int dv = 16 * (G & 1) + 4 * (j & 3);     // + 32n
@@ -171,6 +176,7 @@ struct Frag32<__bf16> {
         o[n] = mfma32(a, p.v[m], o[n]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 };
 

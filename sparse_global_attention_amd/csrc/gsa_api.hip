@@ -15,7 +15,9 @@ using namespace gsa;
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int64_t kSplitTargetBlocks = 4096;  // special attention: aim for >> 256 CUs of work
+// Workgroups of the attention kernels resident at once on a gfx950 part:
+// 256 compute units, four 256-thread workgroups each.
+constexpr int64_t kWorkgroupSlots = 256 * 4;
 
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -107,15 +109,27 @@ void bound_groups(const Call& c, int* n_groups, int* group_tiles) {
   *n_groups = (int)((tiles + gt - 1) / gt);
 }
 
+// Key splits of the special-token attention.  Every workgroup of a split
+// sweeps 1/n of the keys, so with W = per_split * n workgroups running
+// kWorkgroupSlots at a time the sweep takes about ceil(W / slots) / n of the
+// unsplit time: n is chosen to minimise that (the smallest such n), i.e. to
+// fill the last round of workgroups, with at least 4 key tiles per split.
 int special_splits(const Call& c) {
   const Geometry& g = c.g;
   if (g.m_spec == 0) return 1;
   const int64_t per_split = g.n_heads * ((g.m_spec + 127) / 128);
-  int64_t n = (kSplitTargetBlocks + per_split - 1) / per_split;
-  const int64_t max_by_keys = (g.m_tokens + 4 * 32 - 1) / (4 * 32);  // >= 4 key tiles per split
-  if (n > max_by_keys) n = max_by_keys;
-  if (n > kMaxRanges) n = kMaxRanges;
-  return n < 1 ? 1 : (int)n;
+  int64_t max_n = (g.m_tokens + 4 * 32 - 1) / (4 * 32);
+  if (max_n > kMaxRanges) max_n = kMaxRanges;
+  int best = 1;
+  double best_t = 0.0;
+  for (int64_t n = 1; n <= max_n; ++n) {
+    const double t = (double)((per_split * n + kWorkgroupSlots - 1) / kWorkgroupSlots) / (double)n;
+    if (n == 1 || t < best_t * (1.0 - 1e-9)) {
+      best = (int)n;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 Plan make_plan(const Call& c, gsa_op op) {
