@@ -896,10 +896,9 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   // The sweep, compiled once for integer and once for float comparisons.
   auto sweep = [&](auto int_tag) {
     constexpr bool AS_INT = decltype(int_tag)::value;
-    // one 32-key tile t from LDS
-    auto tile = [&](int t, const T* kt) {
+    // candidates of one 32-key tile t, from its scores s (S^T)
+    auto tile = [&](int t, f32x16 s) {
       const int cur0 = t * kKT;
-      f32x16 s = F::qk(kt, r, hf, qf);
       if (t >= n_full) {
         const int lim = nk - cur0 - 4 * hf;
 #pragma unroll
@@ -1001,8 +1000,13 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
     // one barrier step: RSUB tiles from stage buffer u%2, then move stage u+1
     // from registers into the other buffer and reuse `nxt` for stage u+3
     auto step = [&](int u, Stage& nxt) {
+      // all scores of the step first: the later tiles' matrix-core work runs
+      // while the earlier tiles are tested
+      f32x16 sc[RSUB];
 #pragma unroll
-      for (int j = 0; j < RSUB; ++j) tile(u * RSUB + j, tile_buf(u & 1, j));
+      for (int j = 0; j < RSUB; ++j) sc[j] = F::qk(tile_buf(u & 1, j), r, hf, qf);
+#pragma unroll
+      for (int j = 0; j < RSUB; ++j) tile(u * RSUB + j, sc[j]);
       stage_store(nxt, (u + 1) & 1);
       stage_load(nxt, u + 3);
       lds_barrier();
