@@ -752,8 +752,9 @@ __device__ __forceinline__ bool cand_better(Cand a, Cand b) { return a.s > b.s |
 struct CandSlots {
   Cand* buf;
   int r, hf;
-  int lo, hi;  // this lane's fill pointer; the partner's is fetched when needed
-  __device__ int count() const { return hf ? kRefineSlots - 1 - hi : lo; }
+  int fp;   // this lane's next free slot (even lane: lo, odd lane: hi)
+  int dir;  // +1 for the even lane, -1 for the odd lane
+  __device__ int count() const { return hf ? kRefineSlots - 1 - fp : fp; }
   __device__ int slot(int i) const { return hf ? kRefineSlots - 1 - i : i; }  // i-th own entry
 };
 
@@ -810,7 +811,7 @@ __device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
       ++w;
     }
   }
-  if (cs.hf) cs.hi = kRefineSlots - 1 - w; else cs.lo = w;
+  cs.fp = cs.slot(w);
   cut = gt + eq >= K;
   return cut ? key_value(T) : -INFINITY;
 }
@@ -843,8 +844,8 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   cs.buf = reinterpret_cast<Cand*>(smem + 2 * RSUB * KBYTES) + wv * kRefineSlots * 32;
   cs.r = r;
   cs.hf = hf;
-  cs.lo = 0;
-  cs.hi = kRefineSlots - 1;
+  cs.fp = hf ? kRefineSlots - 1 : 0;
+  cs.dir = hf ? -1 : 1;
   constexpr int QW = WAVES * 32;
   const int64_t n_qt = (p.n_q + QW - 1) / QW;
   const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
@@ -949,15 +950,14 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
       // earlier dropped one but never the reverse; the dropped keys land in
       // free slots (needs >= 8 free, so the two ends never meet).
       auto append_group = [&](int a, unsigned gm) {
+        int kb = 0;  // kept keys of the group so far
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int off = ((gm >> e) & 1u) ? __builtin_popcount(gm & ((1u << e) - 1u)) : e;
-          const int sl = hf ? cs.hi - off : cs.lo + off;
-          cs.buf[sl * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
+          const bool kept = (gm >> e) & 1u;
+          cs.buf[(cs.fp + cs.dir * (kept ? kb : e)) * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
+          kb += kept ? 1 : 0;
         }
-        const int nkp = __builtin_popcount(gm);
-        cs.lo += hf ? 0 : nkp;
-        cs.hi -= hf ? nkp : 0;
+        cs.fp += cs.dir * kb;
       };
       // a passing group adds at most 8 candidates to a query (4 per lane)
       if (!wave_any(ntot + 8 * __builtin_popcount(gany) + 8 > kRefineSlots)) {
