@@ -416,6 +416,13 @@ __device__ __forceinline__ uint32_t excluded_mask(const P& p, int64_t key0) {
 }
 
 // ---- the kernel ---------------------------------------------------------------
+// The ring of bf16 K/V tile buffers (three separate arrays, so the compiler
+// can tell which buffer a global-to-LDS load writes and wait only for that).
+// Only the kernels that use them get them allocated.
+__shared__ __attribute__((aligned(16))) __bf16 ring0[kKT * kHeadDim * 2];
+__shared__ __attribute__((aligned(16))) __bf16 ring1[kKT * kHeadDim * 2];
+__shared__ __attribute__((aligned(16))) __bf16 ring2[kKT * kHeadDim * 2];
+
 // The bf16 bound mode asks for four workgroups per CU (at most 128 VGPRs),
 // the occupancy of the plain attention modes.
 template <typename T, int WAVES, int MODE>
@@ -423,9 +430,12 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   using TL = Tile<T>;
   using F = Frag32<T>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // two K/V tile buffers: tile t is read from buffer t%2 while tile t+1 is stored into the other
-  T* const kbuf0 = reinterpret_cast<T*>(smem);
-  T* const kbuf1 = reinterpret_cast<T*>(smem + TL::BYTES);
+  // bf16 key tiles go from global memory straight into LDS (a ring of three
+  // static buffers, below); fp32 tiles are staged through registers into two
+  // buffers at the start of the dynamic LDS.  The streaming top-k heaps
+  // follow the tile buffers in the dynamic LDS.
+  constexpr bool DMA = sizeof(T) == 2;
+  char* const heap_lds = DMA ? smem : smem + 2 * TL::BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
@@ -457,7 +467,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
 
   TopkState tk;
   if constexpr (MODE == kFlashTopk) {
-    Cand* base = reinterpret_cast<Cand*>(smem + 2 * TL::BYTES);
+    Cand* base = reinterpret_cast<Cand*>(heap_lds);
     tk.heap = base + wv * p.topk * 32;
     tk.buf = base + WAVES * p.topk * 32 + wv * kBufCap * 64;
     tk.hsize = 0;
@@ -489,25 +499,11 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
   if (gend > n_tiles - 1) gend = n_tiles - 1;
   auto tile_rel = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
-  auto load_tile = [&](TileLoader<T, WAVES * 64>& ld, int t) {
-    const int rel = tile_rel(t);
-    ld.load(K, V, p.row_stride, hoff, kb + rel, min(nk - rel, kKT), tid);
-  };
-  TileLoader<T, WAVES * 64> sa, sb;
-  load_tile(sa, 0);
-  load_tile(sb, 1);
-  sa.store(kbuf0, kbuf0 + TL::K_ELEMS, tid);
-  load_tile(sa, 2);
-  lds_barrier();
 
-  // One tile: compute tile t from LDS, then move tile t+1 from register stage
-  // `nxt` into the other LDS buffer and reuse `nxt` for tile t+3.  The loop
-  // below is unrolled by two so the stages swap roles without register copies
-  // (a copy would wait for the in-flight loads).
-  auto step = [&](int t, TileLoader<T, WAVES * 64>& nxt) {
-    // a step past the last tile (odd tile count) sees only masked keys
+  // One tile t from the K/V tile at kt (V follows K).  A step past the last
+  // tile (the loops below run in whole unrolled rounds) sees only masked keys.
+  auto compute = [&](int t, const T* kt) {
     const int64_t cur0 = kb + (int64_t)t * kKT;
-    const T* kt = (t & 1) ? kbuf1 : kbuf0;
     const T* vt = kt + TL::K_ELEMS;
     f32x16 s = F::qk(kt, r, hf, qf);
     if (t >= n_full) {
@@ -625,16 +621,93 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     for (int i = 0; i < 16; ++i) pw[i] = fast_exp2(u[i]);
     const typename F::P pp = F::to_p(pw, l_run);
     F::pv(vt, lane, pp, o);
-
-
-    T* kn = (t & 1) ? kbuf0 : kbuf1;
-    nxt.store(kn, kn + TL::K_ELEMS, tid);
-    load_tile(nxt, t + 3);
-    lds_barrier();
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, sb);
-    step(t + 1, sa);
+
+  if constexpr (DMA) {
+    // Ring of three tile buffers.  Step t issues the loads of tile t+2 into
+    // the buffer tile t-1 used (every wave left it at the last barrier),
+    // computes tile t, waits for its own loads of tile t+1 (only tile t+2's
+    // stay in flight: loads complete in order) and meets the other waves at
+    // a barrier, after which tile t+1 is complete in LDS.
+    // A tile is 256 16-byte chunks per operand; this wave loads NDMA of them
+    // per operand, lane l into LDS chunk 64 (WAVES j + wave) + l, which holds
+    // chunk c' of key row (chunk / 8), i.e. global chunk c' ^ swz(row).
+    constexpr int NDMA = (kKT * kHeadDim / 8) / (WAVES * 64);
+    static_assert(NDMA >= 1 && NDMA * WAVES * 64 == kKT * kHeadDim / 8, "tile must split evenly over the waves");
+    const int wu = __builtin_amdgcn_readfirstlane(wv);
+    int goff[NDMA];
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int ch = 64 * (WAVES * j + wu) + lane, row = ch >> 3;
+      goff[j] = (int)(row * p.row_stride * 2 + (((ch & 7) ^ TL::swz(row)) << 4));
+    }
+    auto dma_tile = [&](__bf16* buf, int t) {
+      const int rel = tile_rel(t), valid = min(nk - rel, kKT);
+      const __amdgpu_buffer_rsrc_t rk = TileLoader<T, WAVES * 64>::tile_rsrc(K, p.row_stride, hoff, kb + rel, valid);
+      const __amdgpu_buffer_rsrc_t rv = TileLoader<T, WAVES * 64>::tile_rsrc(V, p.row_stride, hoff, kb + rel, valid);
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int at = 512 * (WAVES * j + wu);  // this wave's 1 KB of the operand, in elements
+        lds_load16(rk, buf + at, goff[j]);
+        lds_load16(rv, buf + TL::K_ELEMS + at, goff[j]);
+      }
+    };
+    // Wait until at most the 2 NDMA loads of the newest tile are in flight
+    // and every LDS read has returned, then meet at the barrier.  No memory
+    // fence: a workgroup release fence would also wait for the newest tile's
+    // loads.  The compiler barriers keep every memory access on its side.
+    auto ring_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x70 | (2 * NDMA));  // vmcnt(2 NDMA) lgkmcnt(0), expcnt untouched
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    dma_tile(ring0, 0);
+    dma_tile(ring1, 1);
+    ring_barrier();
+    auto step = [&](int t, const __bf16* cur, __bf16* fill) {
+      dma_tile(fill, t + 2);
+      compute(t, cur);
+      ring_barrier();
+    };
+    for (int t = 0; t < n_tiles; t += 3) {
+      step(t, ring0, ring2);
+      step(t + 1, ring1, ring0);
+      step(t + 2, ring2, ring1);
+    }
+    // the last prefetches (re-reads of the last tile) must land before the
+    // workgroup's LDS can be handed to another workgroup
+    __builtin_amdgcn_s_waitcnt(0x70);  // vmcnt(0) lgkmcnt(0)
+  } else {
+    // two LDS buffers fed from two register stages: compute tile t from
+    // buffer t%2, move tile t+1 from stage `nxt` into the other buffer and
+    // reuse `nxt` for tile t+3 (unrolled by two so the stages swap roles
+    // without register copies, which would wait for the loads in flight)
+    T* const kbuf0 = reinterpret_cast<T*>(smem);
+    T* const kbuf1 = reinterpret_cast<T*>(smem + TL::BYTES);
+    auto load_tile = [&](TileLoader<T, WAVES * 64>& ld, int t) {
+      const int rel = tile_rel(t);
+      ld.load(K, V, p.row_stride, hoff, kb + rel, min(nk - rel, kKT), tid);
+    };
+    TileLoader<T, WAVES * 64> sa, sb;
+    load_tile(sa, 0);
+    load_tile(sb, 1);
+    sa.store(kbuf0, kbuf0 + TL::K_ELEMS, tid);
+    load_tile(sa, 2);
+    lds_barrier();
+    auto step = [&](int t, TileLoader<T, WAVES * 64>& nxt) {
+      compute(t, (t & 1) ? kbuf1 : kbuf0);
+      T* kn = (t & 1) ? kbuf0 : kbuf1;
+      nxt.store(kn, kn + TL::K_ELEMS, tid);
+      load_tile(nxt, t + 3);
+      lds_barrier();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, sb);
+      step(t + 1, sa);
+    }
   }
 
   // ---- epilogue ----
@@ -1089,7 +1162,7 @@ static hipError_t launch_flash_t(const FlashParams& p, hipStream_t stream) {
   const int64_t n_qt = (p.n_q + WAVES * 32 - 1) / (WAVES * 32);
   const int64_t blocks = n_qt * p.n_heads * p.n_splits;
   if (blocks == 0) return hipSuccess;
-  size_t lds = 2 * (size_t)Tile<T>::BYTES;
+  size_t lds = sizeof(T) == 2 ? 0 : 2 * (size_t)Tile<T>::BYTES;  // bf16 tiles live in static LDS
   if (MODE == kFlashTopk) lds += (size_t)WAVES * ((size_t)p.topk * 32 + kBufCap * 64) * sizeof(Cand);
   const void* fn = reinterpret_cast<const void*>(&flash_kernel<T, WAVES, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -40,6 +40,14 @@ __device__ __forceinline__ int sum_halves(int x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Global-to-LDS load of 16 bytes per lane (buffer load with the LDS flag):
+// lane l's bytes at byte offset `voff` of the buffer land at lds + 16 l;
+// lanes past the buffer's byte limit write zeros.  `lds` must be the same
+// for the whole wave.  Completion is counted by vmcnt like other loads.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // fences global memory, which makes every wave wait for its in-flight global
 // loads (the tile prefetch) at the barrier; this one does not.
