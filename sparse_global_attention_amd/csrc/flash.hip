@@ -46,6 +46,9 @@ namespace gsa {
 
 constexpr int kKT = 32;              // keys per tile
 constexpr float kLazyRescale = 8.0f; // rescale only when the max grows by > 2^8
+// Attention modes without a per-tile max: a tile is redone after a rescale
+// only when its weights against the running reference sum to 2^64 or more.
+constexpr float kSumLimit = 0x1p64f;
 
 // LDS tile of 32 keys.
 // bf16: K and V are stored row-major (one 128-byte row per key) with the
@@ -232,6 +235,18 @@ struct Frag32<float> {
 };
 
 // ---- cooperative K/V tile staging ------------------------------------------
+// A tile is rows key0 .. key0+31 of one head, read with buffer loads whose
+// (scalar) base is the tile's first row: the per-thread byte offsets are the
+// same for every tile, and rows from `valid` (0..32) on lie beyond the
+// buffer's byte limit, which the hardware returns as zeros (those keys are
+// masked: -inf scores, weight 0).  The limit is 32-bit scalar arithmetic
+// (32 rows of a token row stride).
+template <typename T>
+__device__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* X, int64_t stride, int64_t hoff, int64_t key0, int valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X + key0 * stride + hoff), (short)0,
+                                           valid * (int)(stride * (int64_t)sizeof(T)), 0x00020000);
+}
+
 template <typename T, int NT>
 struct TileLoader {
   using TL = Tile<T>;
@@ -241,18 +256,8 @@ struct TileLoader {
   static_assert(NV >= 1 && NV * NT == kKT * VPR, "tile must split evenly over the workgroup");
   uint4 kr[NV], vr[NV];
 
-  // A tile is rows key0 .. key0+31 of one head, read with buffer loads whose
-  // (scalar) base is the tile's first row: the per-thread byte offsets are the
-  // same for every tile, and rows from `valid` (0..32) on lie beyond the
-  // buffer's byte limit, which the hardware returns as zeros (those keys are
-  // masked: -inf scores, weight 0).  The loads are unconditional, so the
-  // compiler can count the loads in flight and wait only for the oldest tile.
-  // The limit is 32-bit scalar arithmetic (32 rows of a token row stride).
-  static __device__ __amdgpu_buffer_rsrc_t tile_rsrc(const T* X, int64_t stride, int64_t hoff, int64_t key0,
-                                                     int valid) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X + key0 * stride + hoff), (short)0,
-                                             valid * (int)(stride * (int64_t)sizeof(T)), 0x00020000);
-  }
+  // The loads are unconditional, so the compiler can count the loads in
+  // flight and wait only for the oldest tile.
   static __device__ int chunk_offset(int64_t stride, int idx) {
     const int key = idx / VPR, c = idx % VPR;
     return (int)(((int64_t)key * stride + c * VE) * (int64_t)sizeof(T));
@@ -526,6 +531,42 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     f32x16 u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) u[i] = fmaf(s[i], c, -m_run);
+    if constexpr (MODE == kFlashFinal || MODE == kFlashPartial) {
+      // No per-tile max.  The weights are formed against the running
+      // reference m_run (the first tile's max, raised only here) and summed;
+      // only a tile whose weights sum to 2^64 or more (or overflow) is redone,
+      // after moving the reference to the tile's max.  Below that every
+      // weight, the row sum (at most 2^31 keys) and the products with V stay
+      // finite, and since the reference never exceeds the true max, no weight
+      // that matters underflows: the result is the same softmax.
+      f32x16 pw;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pw[i] = fast_exp2(u[i]);
+      float ts = 0.0f;
+      typename F::P pp = F::to_p(pw, ts);
+      if (wave_any(!(ts < kSumLimit))) {
+        const float m0 = max3(u[0], u[1], u[2]), m1 = max3(u[3], u[4], u[5]), m2 = max3(u[6], u[7], u[8]);
+        const float m3 = max3(u[9], u[10], u[11]), m4 = max3(u[12], u[13], u[14]);
+        float mt = max3(max3(m0, m1, m2), max3(m3, m4, u[15]), u[15]);
+        // both halves of the query, and never downwards (a fully masked
+        // tile's max is -inf)
+        mt = fmaxf(fmaxf(mt, xor_lane(mt, 32)), 0.0f);
+        const float alpha = fast_exp2(-mt);
+        m_run += mt;
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[n][i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pw[i] = fast_exp2(u[i] - mt);
+        ts = 0.0f;
+        pp = F::to_p(pw, ts);
+      }
+      l_run += ts;
+      F::pv(vt, lane, pp, o);
+      return;
+    }
     float mu;
     if constexpr (MODE == kFlashTopk) {
       // 4-key group maxima, shared by the top-k filter and the softmax.  u is a
@@ -629,35 +670,35 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     // computes tile t, waits for its own loads of tile t+1 (only tile t+2's
     // stay in flight: loads complete in order) and meets the other waves at
     // a barrier, after which tile t+1 is complete in LDS.
-    // A tile is 256 16-byte chunks per operand; this wave loads NDMA of them
-    // per operand, lane l into LDS chunk 64 (WAVES j + wave) + l, which holds
-    // chunk c' of key row (chunk / 8), i.e. global chunk c' ^ swz(row).
-    constexpr int NDMA = (kKT * kHeadDim / 8) / (WAVES * 64);
-    static_assert(NDMA >= 1 && NDMA * WAVES * 64 == kKT * kHeadDim / 8, "tile must split evenly over the waves");
+    // A tile is 512 16-byte chunks: K chunks 0..255, then V.  This wave
+    // loads NDMA of them, lane l chunk 64 (WAVES j + wave) + l into the same
+    // LDS chunk, which holds chunk c' of key row (chunk % 256) / 8 of its
+    // operand, i.e. that row's global chunk c' ^ swz(row).
+    constexpr int NDMA = (2 * kKT * kHeadDim / 8) / (WAVES * 64);
+    static_assert(NDMA >= 1 && NDMA * WAVES * 64 == 2 * kKT * kHeadDim / 8, "tile must split evenly over the waves");
     const int wu = __builtin_amdgcn_readfirstlane(wv);
     int goff[NDMA];
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int ch = 64 * (WAVES * j + wu) + lane, row = ch >> 3;
+      const int ch = (64 * (WAVES * j + wu) + lane) & 255, row = ch >> 3;
       goff[j] = (int)(row * p.row_stride * 2 + (((ch & 7) ^ TL::swz(row)) << 4));
     }
     auto dma_tile = [&](__bf16* buf, int t) {
       const int rel = tile_rel(t), valid = min(nk - rel, kKT);
-      const __amdgpu_buffer_rsrc_t rk = TileLoader<T, WAVES * 64>::tile_rsrc(K, p.row_stride, hoff, kb + rel, valid);
-      const __amdgpu_buffer_rsrc_t rv = TileLoader<T, WAVES * 64>::tile_rsrc(V, p.row_stride, hoff, kb + rel, valid);
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, p.row_stride, hoff, kb + rel, valid);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V, p.row_stride, hoff, kb + rel, valid);
 #pragma unroll
       for (int j = 0; j < NDMA; ++j) {
-        const int at = 512 * (WAVES * j + wu);  // this wave's 1 KB of the operand, in elements
-        lds_load16(rk, buf + at, goff[j]);
-        lds_load16(rv, buf + TL::K_ELEMS + at, goff[j]);
+        const int c0 = 64 * (WAVES * j + wu);  // first chunk of this wave's load (the operand is uniform)
+        lds_load16(c0 < 256 ? rk : rv, buf + 8 * c0, goff[j]);
       }
     };
-    // Wait until at most the 2 NDMA loads of the newest tile are in flight
+    // Wait until at most the NDMA loads of the newest tile are in flight
     // and every LDS read has returned, then meet at the barrier.  No memory
     // fence: a workgroup release fence would also wait for the newest tile's
     // loads.  The compiler barriers keep every memory access on its side.
     auto ring_barrier = [&]() {
-      __builtin_amdgcn_s_waitcnt(0x70 | (2 * NDMA));  // vmcnt(2 NDMA) lgkmcnt(0), expcnt untouched
+      __builtin_amdgcn_s_waitcnt(0x70 | NDMA);  // vmcnt(NDMA) lgkmcnt(0), expcnt untouched
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();

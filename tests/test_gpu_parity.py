@@ -225,3 +225,54 @@ def test_dense_comparator_rows(name):
         w = np.exp(s - s.max(1, keepdims=True))
         ref[:, h] = (w / w.sum(1, keepdims=True)) @ V[:, h]
     assert_close(out[rows], ref, sh.dtype, f"{name} dense rows")
+
+
+def _growing_keys(sh, seed_case, slope):
+    """K of the seeded workload scaled by 1 + slope * j / M at token j (the
+    seeded representation of the workload's dtype)."""
+    k32 = gen.to_f32(seed_case.k, sh.dtype).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    f = 1.0 + slope * np.arange(sh.m_tokens, dtype=np.float64) / sh.m_tokens
+    k32 = (k32 * f[:, None, None]).astype(np.float32).reshape(sh.qkv_shape)
+    if sh.dtype == BF16:
+        return torch.from_numpy(k32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return k32
+
+
+def test_scores_growing_along_the_keys():
+    """Key norms grow 150-fold along the sequence, so inside every key split
+    and every sweep the scores rise far above the first tile's (by hundreds
+    of log2 units): the attention kernels must move their softmax reference
+    many times (the special-token and dense sweeps redo a tile whose weights
+    reach 2^64; the compressed sweep rescales lazily).  Everything is checked
+    against the oracle as usual.  bf16 only: with scores in the thousands,
+    fp32 rounding of the scores alone is beyond the fp32 tolerance (the
+    rescaling code is the same template for both)."""
+    sh = GSAShape("grow 8f-8x8-h2-s2-k4", 8, 2, 8, 8, 2, 64, 2, 4, BF16, seed=42)
+    c = Case(sh, k=_growing_keys(sh, Case(sh), 150.0))
+    wins = np.arange(sh.n_windows)
+    gqc, gkc, gvc = c.pool()
+    goc, gidx, gsc = c.compressed(gqc, gkc, gvc)
+    gspec = c.special()
+    gout = c.forward()
+    gdense = to_host(c.dense()).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    torch.cuda.synchronize()
+    qc, kc, vc = (oracle.pool(sh, x) for x in (c.q, c.k, c.v))
+    oc, idx, sc, amax = oracle.compressed(sh, qc, kc, vc, wins)
+    assert_close(to_host(goc), oc, sh.dtype, "grow O'_comp")
+    gi = gidx.cpu().numpy()
+    check_topk(sh, gi, idx, sc, amax, oracle.guide_scores(sh, qc, kc, wins, gi))
+    spec = oracle.special(sh, c.q, c.k, c.v, np.arange(sh.m_spec))
+    got = to_host(gspec).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    assert_close(got[special_token_ids(sh)], spec, sh.dtype, "grow O_spec")
+    osel = oracle.select(sh, c.q, c.k, c.v, wins, gi)
+    oimg = oracle.gate_combine(sh, c.q, c.wg, wins, oc, osel)
+    got = to_host(gout).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    assert_close(got[window_token_ids(sh)], oimg, sh.dtype, "grow O_img")
+    # dense comparator (the attention kernel's plain mode) on every row
+    Q, K, V = (gen.to_f32(x, sh.dtype).astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+               for x in (c.q, c.k, c.v))
+    for h in range(sh.n_heads):
+        s = Q[:, h] @ K[:, h].T / 8.0
+        w = np.exp(s - s.max(1, keepdims=True))
+        ref = (w / w.sum(1, keepdims=True)) @ V[:, h]
+        assert_close(gdense[:, h], ref, sh.dtype, f"grow dense head {h}")
