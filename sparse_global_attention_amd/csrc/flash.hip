@@ -931,17 +931,20 @@ __device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
 }
 
 // One workgroup: WAVES x 32 queries of one head against all M' keys.  Key
-// tiles are staged in LDS as in flash_kernel (RSUB tiles of 32 keys per
-// barrier), but only S^T = K Q^T is formed.  Keys with score >= theta are
+// tiles are staged in LDS, RSUB tiles of 32 keys at a time, and only
+// S^T = K Q^T is formed.  Keys with score >= theta are
 // appended to the query's LDS slots; when the slots run low, the query keeps
 // only its current k best (so the slots never overflow) and from then on a key
 // must beat the k-th best score strictly (an equal score loses: it has a
 // higher index than every kept key).  At the end the candidates are ranked and
 // the first k written, sorted.  Requires k <= kRefineMaxK.
-#ifndef GSA_RSUB
-#define GSA_RSUB 2
-#endif
-constexpr int RSUB = GSA_RSUB;  // 32-key tiles per barrier step
+// One LDS stage of RSUB key tiles: the waves test all RSUB tiles, meet at a
+// barrier, store the next stage (loaded into registers during the tests) and
+// meet again.  A wave's candidate work varies from tile to tile, and every
+// wave waits for the slowest at a barrier; four tiles per test phase average
+// that out better than two tiles per barrier with two stages (which LDS
+// allows only up to two tiles: the candidate slots take 64 KB).
+constexpr int RSUB = 4;
 template <typename T, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   using TL = Tile<T>;
@@ -949,13 +952,13 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   using Loader = TileLoader<T, WAVES * 64>;
   constexpr int KBYTES = TL::K_ELEMS * (int)sizeof(T);
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // two stage buffers of RSUB key tiles each
-  auto tile_buf = [&](int stage, int j) { return reinterpret_cast<T*>(smem + (stage * RSUB + j) * KBYTES); };
+  // the stage buffer: RSUB key tiles, then the candidate slots
+  auto tile_buf = [&](int j) { return reinterpret_cast<T*>(smem + j * KBYTES); };
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
   CandSlots cs;
-  cs.buf = reinterpret_cast<Cand*>(smem + 2 * RSUB * KBYTES) + wv * kRefineSlots * 32;
+  cs.buf = reinterpret_cast<Cand*>(smem + RSUB * KBYTES) + wv * kRefineSlots * 32;
   cs.r = r;
   cs.hf = hf;
   cs.fp = hf ? kRefineSlots - 1 : 0;
@@ -997,15 +1000,14 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
       st.l[j].load_k(K, p.row_stride, hoff, key0, min(nk - key0, kKT), tid);
     }
   };
-  auto stage_store = [&](const Stage& st, int buf) {
+  auto stage_store = [&](const Stage& st) {
 #pragma unroll
-    for (int j = 0; j < RSUB; ++j) st.l[j].store_k(tile_buf(buf, j), tid);
+    for (int j = 0; j < RSUB; ++j) st.l[j].store_k(tile_buf(j), tid);
   };
-  Stage sa, sb;
-  stage_load(sa, 0);
-  stage_load(sb, 1);
-  stage_store(sa, 0);
-  stage_load(sa, 2);
+  Stage st;
+  stage_load(st, 0);
+  stage_store(st);
+  stage_load(st, 1);
   lds_barrier();
 
   // The sweep, compiled once for integer and once for float comparisons.
@@ -1111,23 +1113,20 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
       }
     };
 
-    // one barrier step: RSUB tiles from stage buffer u%2, then move stage u+1
-    // from registers into the other buffer and reuse `nxt` for stage u+3
-    auto step = [&](int u, Stage& nxt) {
-      // all scores of the step first: the later tiles' matrix-core work runs
-      // while the earlier tiles are tested
-      f32x16 sc[RSUB];
+    // stage u: scores two tiles at a time (the second tile's matrix-core
+    // work runs while the first is tested), then the stage swap
+    for (int u = 0; u < n_steps; ++u) {
 #pragma unroll
-      for (int j = 0; j < RSUB; ++j) sc[j] = F::qk(tile_buf(u & 1, j), r, hf, qf);
-#pragma unroll
-      for (int j = 0; j < RSUB; ++j) tile(u * RSUB + j, sc[j]);
-      stage_store(nxt, (u + 1) & 1);
-      stage_load(nxt, u + 3);
+      for (int j = 0; j < RSUB; j += 2) {
+        const f32x16 s0 = F::qk(tile_buf(j), r, hf, qf);
+        const f32x16 s1 = F::qk(tile_buf(j + 1), r, hf, qf);
+        tile(u * RSUB + j, s0);
+        tile(u * RSUB + j + 1, s1);
+      }
       lds_barrier();
-    };
-    for (int u = 0; u < n_steps; u += 2) {
-      step(u, sb);
-      step(u + 1, sa);
+      stage_store(st);
+      stage_load(st, u + 2);
+      lds_barrier();
     }
   };
   if (as_int)
@@ -1232,7 +1231,7 @@ static hipError_t launch_refine_t(const RefineParams& p, hipStream_t stream) {
   constexpr int WAVES = 4;
   const int64_t blocks = (p.n_q + WAVES * 32 - 1) / (WAVES * 32) * p.n_heads;
   if (blocks == 0) return hipSuccess;
-  const size_t lds = 2 * RSUB * (size_t)Tile<T>::K_ELEMS * sizeof(T) + (size_t)WAVES * kRefineSlots * 32 * sizeof(Cand);
+  const size_t lds = RSUB * (size_t)Tile<T>::K_ELEMS * sizeof(T) + (size_t)WAVES * kRefineSlots * 32 * sizeof(Cand);
   hipLaunchKernelGGL((refine_kernel<T, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
   return hipGetLastError();
 }
