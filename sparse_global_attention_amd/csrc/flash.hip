@@ -485,7 +485,9 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   // the largest |m| seen in the group, the group's last tile and its index.
   // The bounds of this head are written with buffer stores: scalar base (the
   // head's slab) and group offset, one per-lane offset (the query row).
-  float gb = -INFINITY, gm_abs = 0.0f;
+  // gbu: this lane's max of u since the reference m_run last changed (so
+  // fl(gbu + m_run) is the max of fl(u + m_run), adding m being monotonic)
+  float gb = -INFINITY, gbu = -INFINITY, gm_abs = 0.0f;
   int gend = p.group_tiles - 1, gi = 0;
   const int64_t slab = MODE == kFlashBound ? (int64_t)p.n_groups * p.n_q * 4 : 0;
   const __amdgpu_buffer_rsrc_t gbr = __builtin_amdgcn_make_buffer_rsrc(
@@ -507,7 +509,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
 
   // One tile t from the K/V tile at kt (V follows K).  A step past the last
   // tile (the loops below run in whole unrolled rounds) sees only masked keys.
-  auto compute = [&](int t, const T* kt) {
+  auto compute = [&](int t, const T* kt) __attribute__((always_inline)) {
     const int64_t cur0 = kb + (int64_t)t * kKT;
     const T* vt = kt + TL::K_ELEMS;
     f32x16 s = F::qk(kt, r, hf, qf);
@@ -617,6 +619,8 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       // below 2^-22 |s| + 2^-24 |m / c|, so subtracting 2^-20 (|a| + |m / c|)
       // gives a true lower bound.  Windows of excluded frames do not count.
       // gb runs per lane; the halves are combined when the group is written.
+      // The reference is added only when it changes (a rescale) and at the
+      // group's end, and so is |m| folded into gm_abs.
       float mt = mu;
       const uint32_t em = p.n_excl ? excluded_mask(p, cur0) : 0u;
       if (em) {
@@ -626,9 +630,10 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
           if (!((em >> (8 * (i / 4) + 4 * hf + (i % 4))) & 1u)) x = fmaxf(x, u[i]);
         mt = x;
       }
-      gb = fmaxf(gb, mt + m_run);
-      gm_abs = fmaxf(gm_abs, fabsf(m_run));
+      gbu = fmaxf(gbu, mt);
       if (t == gend) {
+        gb = fmaxf(gb, gbu + m_run);
+        gm_abs = fmaxf(gm_abs, fabsf(m_run));
         const float gq = fmaxf(gb, xor_lane(gb, 32));  // uniform branch: every lane takes part
         if (hf == 0 && qvalid) {
           const float a = gq * rc;
@@ -636,6 +641,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
                                                 (int)((int64_t)gi * p.n_q * 4), 0);
         }
         gb = -INFINITY;
+        gbu = -INFINITY;
         gm_abs = 0.0f;
         gend = min(gend + p.group_tiles, n_tiles - 1);
         ++gi;
@@ -645,6 +651,11 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     if (wave_any(mu > kLazyRescale)) {
       if constexpr (MODE != kFlashTopk) mu = fmaxf(mu, xor_lane(mu, 32));
       if (mu > kLazyRescale) {
+        if constexpr (MODE == kFlashBound) {
+          gb = fmaxf(gb, gbu + m_run);
+          gm_abs = fmaxf(gm_abs, fabsf(m_run));
+          gbu = -INFINITY;
+        }
         const float alpha = fast_exp2(-mu);
         m_run += mu;
         l_run *= alpha;
@@ -683,7 +694,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       const int ch = (64 * (WAVES * j + wu) + lane) & 255, row = ch >> 3;
       goff[j] = (int)(row * p.row_stride * 2 + (((ch & 7) ^ TL::swz(row)) << 4));
     }
-    auto dma_tile = [&](__bf16* buf, int t) {
+    auto dma_tile = [&](__bf16* buf, int t) __attribute__((always_inline)) {
       const int rel = tile_rel(t), valid = min(nk - rel, kKT);
       const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, p.row_stride, hoff, kb + rel, valid);
       const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V, p.row_stride, hoff, kb + rel, valid);
@@ -697,7 +708,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     // and every LDS read has returned, then meet at the barrier.  No memory
     // fence: a workgroup release fence would also wait for the newest tile's
     // loads.  The compiler barriers keep every memory access on its side.
-    auto ring_barrier = [&]() {
+    auto ring_barrier = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0x70 | NDMA);  // vmcnt(NDMA) lgkmcnt(0), expcnt untouched
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
@@ -708,7 +719,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     dma_tile(ring0, 0);
     dma_tile(ring1, 1);
     ring_barrier();
-    auto step = [&](int t, const __bf16* cur, __bf16* fill) {
+    auto step = [&](int t, const __bf16* cur, __bf16* fill) __attribute__((always_inline)) {
       dma_tile(fill, t + 2);
       compute(t, cur);
       ring_barrier();
@@ -738,7 +749,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     sa.store(kbuf0, kbuf0 + TL::K_ELEMS, tid);
     load_tile(sa, 2);
     lds_barrier();
-    auto step = [&](int t, TileLoader<T, WAVES * 64>& nxt) {
+    auto step = [&](int t, TileLoader<T, WAVES * 64>& nxt) __attribute__((always_inline)) {
       compute(t, (t & 1) ? kbuf1 : kbuf0);
       T* kn = (t & 1) ? kbuf0 : kbuf1;
       nxt.store(kn, kn + TL::K_ELEMS, tid);
