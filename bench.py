@@ -37,6 +37,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="pi3-long", help="workload name (see gen/configs.py)")
+    ap.add_argument("--topk", type=int, default=None, help="override the workload's k (test-time top-k)")
+    ap.add_argument("--pool", type=int, default=None, help="override the workload's window size s")
+    ap.add_argument("--special", type=int, default=None, help="override the special tokens per frame P")
+    ap.add_argument("--grid", type=int, nargs=2, default=None, metavar=("H", "W"), help="override the image grid")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-windows", type=int, default=64)
@@ -107,6 +111,14 @@ def main():
     from gen.configs import config_by_name
 
     sh = config_by_name(args.config)
+    over = {k: v for k, v in (("topk", args.topk), ("pool", args.pool), ("n_special", args.special)) if v is not None}
+    if args.grid:
+        over.update(grid_h=args.grid[0], grid_w=args.grid[1])
+    if over:
+        import dataclasses
+        sh = dataclasses.replace(sh, **over)
+        sh = dataclasses.replace(sh, name=f"{sh.name.split()[0]}-variant {sh.n_frames}f-{sh.grid_h}x{sh.grid_w}-"
+                                           f"h{sh.n_heads}-s{sh.pool}-k{sh.topk}-P{sh.n_special}")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 

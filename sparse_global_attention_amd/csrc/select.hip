@@ -170,15 +170,20 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
   const Geometry& geo = p.g;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int ql = lane & 15, g = lane >> 4;
+  // One wave per (head, window, block of 16 of the window's s^2 queries).
   // Head-major order: all waves in flight gather from the same head's K/V
   // blocks (M' x 4 KB), a working set the 256 MB Infinity Cache can hold a
-  // large part of, instead of all heads' blocks at once.
-  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
-  if (item >= geo.n_windows * geo.n_heads) return;
-  const int64_t h = item / geo.n_windows;
-  const int64_t win = item % geo.n_windows;
-  const int64_t H = geo.n_heads;
+  // large part of, instead of all heads' blocks at once.  The query blocks of
+  // a window are adjacent waves (mostly one workgroup), so their identical
+  // gathers meet in the caches instead of being repeated one after another.
   const int s2 = (int)(geo.pool * geo.pool);
+  const int n_sub = (s2 + 15) / 16;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+  if (item >= geo.n_windows * geo.n_heads * n_sub) return;
+  const int qs = (int)(item % n_sub);
+  const int64_t h = item / n_sub / geo.n_windows;
+  const int64_t win = item / n_sub % geo.n_windows;
+  const int64_t H = geo.n_heads;
   const int K = p.topk;
   const float c = p.scale_log2;
 
@@ -186,9 +191,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
   const int tr0 = lane < K ? trow[lane] : -1;
   const int tr1 = lane + 64 < K ? trow[lane + 64] : -1;
   const int n_chunks = (int)((K * geo.sb + 31) / 32);
-  const int n_sub = (s2 + 15) / 16;
 
-  for (int qs = 0; qs < n_sub; ++qs) {
+  {
     const int kq = qs * 16 + ql;  // window-local query index
     const bool qvalid = kq < s2;
     const int64_t tok = window_token(geo, win, qvalid ? kq : 0);
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }
 
 hipError_t launch_select(int dtype, const SelectParams& p, hipStream_t stream) {
-  const int64_t items = p.g.n_windows * p.g.n_heads;
+  const int64_t items = p.g.n_windows * p.g.n_heads * ((p.g.pool * p.g.pool + 15) / 16);
   if (items == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((items + 3) / 4);
   if (dtype == kBF16)
