@@ -38,6 +38,20 @@ __device__ __forceinline__ int sum_halves(int x) {
   return (int)(r[0] + r[1]);
 }
 
+// max(x, x of lane l ^ 32) and max(x, x of lane l ^ 16) with the VALU lane
+// swaps (v_permlane32_swap: the two 32-lane halves; v_permlane16_swap: the
+// odd and even 16-lane rows): each lane gets its own value and its partner's,
+// in some order, so the max does not depend on which is which.  Every lane of
+// the wave must be active.
+__device__ __forceinline__ float max_halves32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // Global-to-LDS load of 16 bytes per lane (buffer load with the LDS flag):

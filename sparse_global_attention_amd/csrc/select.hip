@@ -215,8 +215,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
       }
       float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                        fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-      mx = fmaxf(mx, xor_lane(mx, 16));
-      mx = fmaxf(mx, xor_lane(mx, 32));
+      mx = max_halves32(max_rows16(mx));  // the query's four lanes ql + 16 g
       const float mnew = mx * c;
       if (mnew > m_run) {  // few chunks per window: rescale eagerly
         const float alpha = fast_exp2(m_run - mnew);
