@@ -841,7 +841,7 @@ __device__ __forceinline__ float next_up(float x) { return key_value(order_key(x
 // the order keys, bit by bit from the top; the two lanes of a query hold the
 // even and the odd groups (n_groups <= 2 * kMaxGroupsPerLane).  Returns -inf
 // when there are fewer than k finite bounds (then every candidate qualifies).
-constexpr int kMaxGroupsPerLane = 64;
+template <int kMaxGroupsPerLane>
 __device__ float kth_bound(const RefineParams& p, int64_t qrow, int h, int hf, bool qvalid) {
   const int NG = p.n_groups;
   const int per = (NG - hf + 1) / 2;
@@ -877,10 +877,11 @@ __device__ __forceinline__ bool cand_better(Cand a, Cand b) { return a.s > b.s |
 struct CandSlots {
   Cand* buf;
   int r, hf;
-  int fp;   // this lane's next free slot (even lane: lo, odd lane: hi)
-  int dir;  // +1 for the even lane, -1 for the odd lane
-  __device__ int count() const { return hf ? kRefineSlots - 1 - fp : fp; }
-  __device__ int slot(int i) const { return hf ? kRefineSlots - 1 - i : i; }  // i-th own entry
+  int fp;      // this lane's next free slot (even lane: lo, odd lane: hi)
+  int dir;     // +1 for the even lane, -1 for the odd lane
+  int nslots;  // slots per query (a compile-time constant of the kernel)
+  __device__ __forceinline__ int count() const { return hf ? nslots - 1 - fp : fp; }
+  __device__ __forceinline__ int slot(int i) const { return hf ? nslots - 1 - i : i; }  // i-th own entry
 };
 
 // Keep only the k best candidates (score desc, index asc) of every query of the
@@ -956,8 +957,9 @@ __device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
 // that out better than two tiles per barrier with two stages (which LDS
 // allows only up to two tiles: the candidate slots take 64 KB).
 constexpr int RSUB = 4;
-template <typename T, int WAVES>
+template <typename T, int WAVES, int SLOTS>
 __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
+  constexpr int kRefineSlots = SLOTS;
   using TL = Tile<T>;
   using F = Frag32<T>;
   using Loader = TileLoader<T, WAVES * 64>;
@@ -972,6 +974,7 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   cs.buf = reinterpret_cast<Cand*>(smem + RSUB * KBYTES) + wv * kRefineSlots * 32;
   cs.r = r;
   cs.hf = hf;
+  cs.nslots = kRefineSlots;
   cs.fp = hf ? kRefineSlots - 1 : 0;
   cs.dir = hf ? -1 : 1;
   constexpr int QW = WAVES * 32;
@@ -988,7 +991,7 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   // a key is a candidate when its score is >= tlo: theta at first, then just
   // above the k-th best kept score (an equal score loses to the kept keys,
   // which all have lower indices)
-  float tlo = kth_bound(p, qrow, h, hf, qvalid);
+  float tlo = kth_bound<kRefineGroups(SLOTS) / 2>(p, qrow, h, hf, qvalid);
   if (!qvalid) tlo = INFINITY;
   int ntot = 0;  // candidates held for this lane's query (both lanes)
   __builtin_amdgcn_s_waitcnt(0);
@@ -1237,14 +1240,22 @@ hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t s
   return dtype == kBF16 ? launch_flash_dt<__bf16>(mode, p, stream) : launch_flash_dt<float>(mode, p, stream);
 }
 
-template <typename T>
-static hipError_t launch_refine_t(const RefineParams& p, hipStream_t stream) {
+template <typename T, int SLOTS>
+static hipError_t launch_refine_s(const RefineParams& p, hipStream_t stream) {
   constexpr int WAVES = 4;
   const int64_t blocks = (p.n_q + WAVES * 32 - 1) / (WAVES * 32) * p.n_heads;
   if (blocks == 0) return hipSuccess;
-  const size_t lds = RSUB * (size_t)Tile<T>::K_ELEMS * sizeof(T) + (size_t)WAVES * kRefineSlots * 32 * sizeof(Cand);
-  hipLaunchKernelGGL((refine_kernel<T, WAVES>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
+  const size_t lds = RSUB * (size_t)Tile<T>::K_ELEMS * sizeof(T) + (size_t)WAVES * SLOTS * 32 * sizeof(Cand);
+  const void* fn = reinterpret_cast<const void*>(&refine_kernel<T, WAVES, SLOTS>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((refine_kernel<T, WAVES, SLOTS>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
   return hipGetLastError();
+}
+template <typename T>
+static hipError_t launch_refine_t(const RefineParams& p, hipStream_t stream) {
+  if (p.topk <= kRefineSlotsSmall - 16) return launch_refine_s<T, kRefineSlotsSmall>(p, stream);
+  return launch_refine_s<T, kRefineSlotsLarge>(p, stream);
 }
 
 hipError_t launch_refine(int dtype, const RefineParams& p, hipStream_t stream) {

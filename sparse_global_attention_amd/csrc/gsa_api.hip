@@ -97,12 +97,13 @@ struct Plan {
 // streaming-heap kernel.
 bool use_refine(const Call& c) { return c.topk <= kRefineMaxK; }
 
-// Groups of key tiles for the score bounds: at most 128 groups (a lane of the
-// refine kernel holds 64 of them), so that the k-th best group bound sits
-// close to the k-th best score and few keys pass it.
+// Groups of key tiles for the score bounds: at most refine_groups_for_k(k)
+// groups (128 for k <= 48, 512 beyond; a lane of the refine kernel holds half
+// of them), so that the k-th best group bound sits close to the k-th best
+// score and few keys pass it.
 void bound_groups(const Call& c, int* n_groups, int* group_tiles) {
   const int64_t tiles = (c.g.n_windows + 31) / 32;
-  const int64_t target = 128;
+  const int64_t target = refine_groups_for_k(c.topk);
   int64_t gt = (tiles + target - 1) / target;
   if (gt < 1) gt = 1;
   *group_tiles = (int)gt;

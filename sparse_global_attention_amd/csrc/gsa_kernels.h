@@ -56,11 +56,18 @@ constexpr int kMaxExcl = 16;
 // refine_kernel, used for k <= kRefineMaxK).  kFlashTopk: compressed
 // attention with an exact streaming top-k in LDS heaps (larger k).
 enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashTopk = 2, kFlashBound = 3 };
-#ifndef GSA_REFINE_SLOTS
-#define GSA_REFINE_SLOTS 64
-#endif
-constexpr int kRefineSlots = GSA_REFINE_SLOTS;  // refine_kernel: LDS candidate slots per query
-constexpr int kRefineMaxK = kRefineSlots - 16;   // the k best + one group (8) + 8 spare slots
+// refine_kernel: LDS candidate slots per query.  64 slots (80 KB per
+// workgroup, two per CU) serve k <= 48; 144 slots (the whole 160 KB, one
+// workgroup per CU) serve k <= 128.  A query needs its k best + one 4-key
+// group of each lane (8) + 8 spare slots for whole-group writes.
+constexpr int kRefineSlotsSmall = 64;
+constexpr int kRefineSlotsLarge = 144;
+constexpr int kRefineMaxK = kRefineSlotsLarge - 16;
+// Groups of key tiles for the score bounds (at most; fewer when there are
+// fewer tiles).  The threshold is the k-th largest group bound, so it needs
+// groups well beyond k: 128 for k <= 48, 512 for larger k.
+constexpr int kRefineGroups(int slots) { return slots == kRefineSlotsSmall ? 128 : 512; }
+inline int refine_groups_for_k(int k) { return kRefineGroups(k <= kRefineSlotsSmall - 16 ? kRefineSlotsSmall : kRefineSlotsLarge); }
 
 struct FlashParams {
   const void* q;

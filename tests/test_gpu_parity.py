@@ -188,13 +188,14 @@ def test_topk_ties_go_to_lower_window():
     assert np.all(idx.cpu().numpy() == np.array([0, 1, 2], np.int32))
 
 
-def test_topk_ties_beyond_the_candidate_slots():
+@pytest.mark.parametrize("k", [8, 100])
+def test_topk_ties_beyond_the_candidate_slots(k):
     """Head 0: every key window identical, so each query's guide scores all tie
     and every key reaches the threshold, far more than the candidate slots
     hold; the slots are cut back to the k best (ties to the lower window), so
     the answer is the k lowest windows.  Head 1 keeps its seeded keys and must
-    match the oracle."""
-    sh = GSAShape("ties-many 16f-16x16-h2-s4-k8", 16, 1, 16, 16, 2, 64, 4, 8, BF16, seed=41)
+    match the oracle.  k = 8 runs with the 64 slots per query, k = 100 with 144."""
+    sh = GSAShape(f"ties-many 16f-16x16-h2-s4-k{k}", 16, 1, 16, 16, 2, 64, 4, k, BF16, seed=41)
     c = Case(sh)
     qc, kc, vc = c.pool()
     kc[:, 0] = kc[5, 0].clone()
