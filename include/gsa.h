@@ -111,8 +111,9 @@ gsa_status gsa_pool(const gsa_config* cfg, const void* q, const void* k, const v
  * set), per head.  Writes oc, topk_idx and, if not NULL, topk_score.
  * The attention sweep also records a lower bound of the best score in each
  * group of key tiles; a score-only sweep then keeps the keys that reach the
- * k-th best bound and ranks them (exact; a block whose candidates do not fit
- * is redone with streaming heaps).  Workspace: GSA_OP_COMPRESSED bytes.
+ * k-th best bound and ranks them (exact for any input: a query whose
+ * candidate slots fill up keeps its k best so far and raises its threshold).
+ * Workspace: GSA_OP_COMPRESSED bytes.
  */
 gsa_status gsa_compressed_attn_topk(const gsa_config* cfg, const void* qc, const void* kc,
                                     const void* vc, float* oc, int32_t* topk_idx,

@@ -8,11 +8,11 @@
 //                   Reconstruction Models", section "全局稀疏注意力（GSA）核心设计"
 //                   (M_spec queries over all M keys), and the fixed-context
 //                   part of the selection branch (section "Speed3R-VGGT 适配");
-//  * kFlashTopk     compressed attention over the pooled windows fused with a
-//                   streaming top-k over the raw guide scores S = Qc Kc^T
-//                   (section "压缩分支" and section "选择分支"; the fused
-//                   top-k-in-the-attention-sweep idea of section
-//                   "高效 Triton Kernel 实现").  S is never written out.
+//  * kFlashBound     compressed attention over the pooled windows (section
+//                   "压缩分支") that also leaves, per group of key tiles, a
+//                   lower bound of each query's best raw guide score
+//                   S = Qc Kc^T; refine_kernel below turns them into the exact
+//                   top-k (section "选择分支").  S is never written out.
 //
 // Work decomposition: a workgroup of WAVES wavefronts owns 32*WAVES query
 // rows of one head and one key split; each wavefront owns 32 query rows.  Key
@@ -25,16 +25,6 @@
 // Lane l holds query l%32 and 16 of the tile's keys; the other 16 keys of the
 // same query sit in lane l^32.
 //
-// Streaming top-k (kFlashTopk): per query a min-heap of the k best
-// (score, window) pairs lives in LDS, ordered by (score desc, index asc), so
-// its root is the current k-th best.  Keys are swept in ascending index order,
-// so a new key that ties the root's score loses the tie: a score can only
-// enter if it is strictly above the root score tau.  Each tile first compares
-// 4-key group maxima with tau (the maxima are needed for the softmax anyway);
-// only then are single scores tested and appended to a small per-lane buffer
-// in LDS.  Buffers are flushed into the heaps in batches (the two lanes of a
-// query take turns), which keeps the rare insertions from stalling the wave on
-// every tile.
 #include <math.h>
 
 #include <type_traits>
@@ -311,101 +301,11 @@ struct TileLoader {
   }
 };
 
-// ---- streaming top-k helpers ------------------------------------------------
+// ---- candidates of the exact top-k ------------------------------------------
 struct Cand {
   float s;
   int j;
 };
-// a ranks below b in the order (score desc, index asc)
-__device__ __forceinline__ bool worse(Cand a, Cand b) { return a.s < b.s || (a.s == b.s && a.j > b.j); }
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Heap element i of query r lives at hp[i*32 + r] (queries interleaved so the
-// lanes of a wave touch consecutive words).  Root = worst of the kept set.
-__device__ void sift_down(Cand* hp, int r, int i, int n, Cand x) {
-  while (true) {
-    int ci = 2 * i + 1;
-    if (ci >= n) break;
-    Cand cc = hp[ci * 32 + r];
-    if (ci + 1 < n) {
-      Cand c2 = hp[(ci + 1) * 32 + r];
-      if (worse(c2, cc)) {
-        cc = c2;
-        ++ci;
-      }
-    }
-    if (worse(cc, x)) {
-      hp[i * 32 + r] = cc;
-      i = ci;
-    } else {
-      break;
-    }
-  }
-  hp[i * 32 + r] = x;
-}
-
-__device__ void heap_insert(Cand* hp, int r, int& n, int K, Cand x) {
-  if (n < K) {
-    int i = n++;
-    while (i > 0) {
-      int pi = (i - 1) >> 1;
-      Cand pc = hp[pi * 32 + r];
-      if (worse(x, pc)) {
-        hp[i * 32 + r] = pc;
-        i = pi;
-      } else {
-        break;
-      }
-    }
-    hp[i * 32 + r] = x;
-  } else if (worse(hp[r], x)) {
-    sift_down(hp, r, 0, K, x);
-  }
-}
-
-constexpr int kBufCap = 16;  // per-lane buffered candidates
-
-__device__ __forceinline__ bool excluded_window(const FlashParams& p, int64_t key);
-
-struct TopkState {
-  Cand* heap;    // this wave's heaps: [K][32]
-  Cand* buf;     // this wave's candidate buffers: [kBufCap][64]
-  int hsize;     // entries in this lane's query heap (same in both lanes of the query)
-  int cnt;       // candidates in this lane's buffer
-  float tau;     // current k-th best score of the query (-inf until the heap is full)
-  float tau_u;   // tau in the shifted exponent units fma(tau, c, -m) of the running max m
-
-  // Move every buffered candidate into the heaps.  The two lanes of a query
-  // take turns because they share its heap.
-  __device__ void flush(const FlashParams& p, int lane, int r, int hf, int K) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (hf == half) {
-        for (int b = 0; b < cnt; ++b) {
-          const Cand x = buf[b * 64 + lane];
-          if (!excluded_window(p, x.j)) heap_insert(heap, r, hsize, K, x);
-        }
-      }
-      wave_sync();
-      int other = xor_lane(hsize, 32);
-      if (hf != half) hsize = other;
-    }
-    cnt = 0;
-    tau = hsize >= K ? heap[r].s : -INFINITY;
-  }
-};
-
-__device__ __forceinline__ bool excluded_window(const FlashParams& p, int64_t key) {
-  if (p.n_excl == 0) return false;
-  int64_t f = key / p.wins_per_frame;
-  for (int x = 0; x < p.n_excl; ++x)
-    if (f == p.excl_frames[x]) return true;
-  return false;
-}
 
 // Excluded keys of the 32-key tile starting at key0, as a bit mask (bit i =
 // key key0 + i).  Uniform across the wave.
@@ -437,10 +337,8 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // bf16 key tiles go from global memory straight into LDS (a ring of three
   // static buffers, below); fp32 tiles are staged through registers into two
-  // buffers at the start of the dynamic LDS.  The streaming top-k heaps
-  // follow the tile buffers in the dynamic LDS.
+  // buffers in the dynamic LDS.
   constexpr bool DMA = sizeof(T) == 2;
-  char* const heap_lds = DMA ? smem : smem + 2 * TL::BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 31, hf = lane >> 5;
@@ -469,17 +367,6 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   bool first = true;
   const float c = p.scale_log2;
   const float rc = 1.0f / c;
-
-  TopkState tk;
-  if constexpr (MODE == kFlashTopk) {
-    Cand* base = reinterpret_cast<Cand*>(heap_lds);
-    tk.heap = base + wv * p.topk * 32;
-    tk.buf = base + WAVES * p.topk * 32 + wv * kBufCap * 64;
-    tk.hsize = 0;
-    tk.cnt = 0;
-    tk.tau = -INFINITY;
-    tk.tau_u = -INFINITY;
-  }
 
   // kFlashBound: running max over the current group of fl(tile max u + m),
   // the largest |m| seen in the group, the group's last tile and its index.
@@ -570,40 +457,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       return;
     }
     float mu;
-    if constexpr (MODE == kFlashTopk) {
-      // 4-key group maxima, shared by the top-k filter and the softmax.  u is a
-      // non-decreasing function of the raw score, so "group max >= tau_u" keeps
-      // every group holding a score above tau; exact tests run on raw scores.
-      float g[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) g[a] = max3(fmaxf(u[4 * a], u[4 * a + 1]), u[4 * a + 2], u[4 * a + 3]);
-      mu = max3(fmaxf(g[0], g[1]), g[2], g[3]);
-      if (wave_any(mu >= tk.tau_u)) {
-        // a passing group adds at most 4 entries: flush first if any lane could overflow
-        int need = 0;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) need += g[a] >= tk.tau_u ? 4 : 0;
-        if (wave_any(tk.cnt + need > kBufCap)) {
-          tk.flush(p, lane, r, hf, p.topk);
-          tk.tau_u = fmaf(tk.tau, c, -m_run);
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const bool take = g[a] >= tk.tau_u;
-          if (wave_any(take)) {
-            if (take) {
-              // write every score of the group, keep those strictly above the raw
-              // root score (a tie loses: the root holds an earlier, lower index)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                tk.buf[tk.cnt * 64 + lane] = Cand{s[4 * a + e], (int)(cur0 + 8 * a + 4 * hf + e)};
-                tk.cnt += s[4 * a + e] > tk.tau ? 1 : 0;
-              }
-            }
-          }
-        }
-      }
-    } else {
+    {
       const float m0 = max3(u[0], u[1], u[2]), m1 = max3(u[3], u[4], u[5]), m2 = max3(u[6], u[7], u[8]);
       const float m3 = max3(u[9], u[10], u[11]), m4 = max3(u[12], u[13], u[14]);
       mu = max3(max3(m0, m1, m2), max3(m3, m4, u[15]), u[15]);
@@ -612,7 +466,6 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     // lane l^32.  The hot path needs no cross-lane step: whether any query of
     // the wave must rescale is the same test on either half, and only the
     // (cold) rescale combines the halves.
-    if constexpr (MODE == kFlashTopk) mu = fmaxf(mu, xor_lane(mu, 32));
     if constexpr (MODE == kFlashBound) {
       // Lower bound of the tile's best candidate score, recovered from u and
       // the running max before any rescale: |fl(fl(u + m) / c) - s| stays
@@ -649,7 +502,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     }
     // lazy rescale: only when the max has grown by more than 2^kLazyRescale
     if (wave_any(mu > kLazyRescale)) {
-      if constexpr (MODE != kFlashTopk) mu = fmaxf(mu, xor_lane(mu, 32));
+      mu = fmaxf(mu, xor_lane(mu, 32));
       if (mu > kLazyRescale) {
         if constexpr (MODE == kFlashBound) {
           gb = fmaxf(gb, gbu + m_run);
@@ -666,7 +519,6 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
 #pragma unroll
         for (int i = 0; i < 16; ++i) u[i] -= mu;
       }
-      if constexpr (MODE == kFlashTopk) tk.tau_u = fmaf(tk.tau, c, -m_run);
     }
     f32x16 pw;
 #pragma unroll
@@ -795,30 +647,6 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     }
   }
 
-  if constexpr (MODE == kFlashTopk) {
-    tk.flush(p, lane, r, hf, p.topk);
-    const int K = p.topk;
-    if (hf == 0) {
-      // heapsort: repeatedly move the worst kept entry to the back
-      for (int end = tk.hsize - 1; end > 0; --end) {
-        Cand top = tk.heap[r];
-        Cand last = tk.heap[end * 32 + r];
-        tk.heap[end * 32 + r] = top;
-        sift_down(tk.heap, r, 0, end, last);
-      }
-    }
-    wave_sync();
-    if (qvalid) {
-      int32_t* di = p.topk_idx + (qrow * p.n_heads + h) * K;
-      float* ds = p.topk_score ? p.topk_score + (qrow * p.n_heads + h) * K : nullptr;
-      for (int t = hf; t < K; t += 2) {
-        const bool have = t < tk.hsize;
-        const Cand x = have ? tk.heap[t * 32 + r] : Cand{-INFINITY, -1};
-        di[t] = have ? x.j : -1;
-        if (ds) ds[t] = have ? x.s : -INFINITY;
-      }
-    }
-  }
 }
 
 // ---- exact top-k from the group bounds ---------------------------------------
@@ -1217,7 +1045,6 @@ static hipError_t launch_flash_t(const FlashParams& p, hipStream_t stream) {
   const int64_t blocks = n_qt * p.n_heads * p.n_splits;
   if (blocks == 0) return hipSuccess;
   size_t lds = sizeof(T) == 2 ? 0 : 2 * (size_t)Tile<T>::BYTES;  // bf16 tiles live in static LDS
-  if (MODE == kFlashTopk) lds += (size_t)WAVES * ((size_t)p.topk * 32 + kBufCap * 64) * sizeof(Cand);
   const void* fn = reinterpret_cast<const void*>(&flash_kernel<T, WAVES, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -1230,10 +1057,7 @@ static hipError_t launch_flash_dt(int mode, const FlashParams& p, hipStream_t st
   if (mode == kFlashFinal) return launch_flash_t<T, 4, kFlashFinal>(p, stream);
   if (mode == kFlashPartial) return launch_flash_t<T, 4, kFlashPartial>(p, stream);
   if (mode == kFlashBound) return launch_flash_t<T, 4, kFlashBound>(p, stream);
-  // top-k heaps take WAVES * k * 256 bytes of LDS: fewer waves for larger k
-  if (p.topk <= 32) return launch_flash_t<T, 4, kFlashTopk>(p, stream);
-  if (p.topk <= 64) return launch_flash_t<T, 2, kFlashTopk>(p, stream);
-  return launch_flash_t<T, 1, kFlashTopk>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t stream) {

@@ -92,11 +92,6 @@ struct Plan {
   int64_t gbound;
 };
 
-// The compressed step's top-k: for k <= kRefineMaxK the attention sweep
-// writes score bounds and refine_kernel finds the top-k; larger k use the
-// streaming-heap kernel.
-bool use_refine(const Call& c) { return c.topk <= kRefineMaxK; }
-
 // Groups of key tiles for the score bounds: at most refine_groups_for_k(k)
 // groups (128 for k <= 48, 512 beyond; a lane of the refine kernel holds half
 // of them), so that the k-th best group bound sits close to the k-th best
@@ -158,7 +153,7 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.oc = take(g.n_windows * g.n_heads * kHeadDim * 4);
     p.topk = take(g.n_windows * g.n_heads * (int64_t)c.topk * 4);
   }
-  if ((op == GSA_OP_FORWARD || op == GSA_OP_COMPRESSED) && use_refine(c))
+  if (op == GSA_OP_FORWARD || op == GSA_OP_COMPRESSED)
     p.gbound = take((int64_t)p.n_groups * g.n_heads * g.n_windows * 4);
   if (op == GSA_OP_FORWARD || op == GSA_OP_SELECT) {
     p.kblk = take(blk);
@@ -240,11 +235,10 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
   return launch_merge(c.dtype, m, st);
 }
 
-// Compressed attention + exact top-k.  k <= kRefineMaxK: two launches,
+// Compressed attention + exact top-k (k <= kRefineMaxK = 128), two launches:
 //  1. flash attention over all M' windows, also writing per-group score bounds;
 //  2. refine_kernel: theta from the bounds, score-only sweep collecting the
 //     keys >= theta, ranking -> topk.
-// Larger k: one launch of the streaming-heap kernel.
 hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const void* kc, const void* vc, float* oc,
                           int32_t* idx, float* score, void* ws, hipStream_t st) {
   const Geometry& g = c.g;
@@ -255,13 +249,9 @@ hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const v
   f.kbeg[0] = 0;
   f.kend[0] = g.n_windows;
   f.oc = oc;
-  f.topk_idx = idx;
-  f.topk_score = score;
-  f.topk = c.topk;
   f.wins_per_frame = g.wpf;
   f.n_excl = c.exclude ? c.n_ctx : 0;
   for (int i = 0; i < f.n_excl; ++i) f.excl_frames[i] = c.ctx[i];
-  if (!use_refine(c)) return launch_flash(c.dtype, kFlashTopk, f, st);
   f.gbound = reinterpret_cast<float*>(at(ws, pl.gbound));
   f.n_groups = pl.n_groups;
   f.group_tiles = pl.group_tiles;

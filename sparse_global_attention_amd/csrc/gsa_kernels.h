@@ -53,9 +53,8 @@ constexpr int kMaxRanges = 64;
 constexpr int kMaxExcl = 16;
 // kFlashBound: compressed attention that also records, per group of key
 // tiles, a lower bound of the group's best candidate score (input of
-// refine_kernel, used for k <= kRefineMaxK).  kFlashTopk: compressed
-// attention with an exact streaming top-k in LDS heaps (larger k).
-enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashTopk = 2, kFlashBound = 3 };
+// refine_kernel, which turns them into the exact top-k, k <= kRefineMaxK).
+enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashBound = 3 };
 // refine_kernel: LDS candidate slots per query.  64 slots (80 KB per
 // workgroup, two per CU) serve k <= 48; 144 slots (the whole 160 KB, one
 // workgroup per CU) serve k <= 128.  A query needs its k best + one 4-key
@@ -86,11 +85,8 @@ struct FlashParams {
   // kFlashPartial: part_o [split][n_q][H][d] (normalised), part_lse [split][n_q][H] (natural log)
   float* part_o;
   float* part_lse;
-  // kFlashTopk: oc [n_q][H][d] fp32, topk_idx/topk_score [n_q][H][topk]
+  // kFlashBound: oc [n_q][H][d] fp32
   float* oc;
-  int32_t* topk_idx;
-  float* topk_score;
-  int topk;
   int64_t wins_per_frame;
   int n_excl;                 // frames whose windows are not top-k candidates
   int excl_frames[kMaxExcl];
