@@ -164,25 +164,25 @@ __device__ __forceinline__ void load_chunk(SelChunk<T>& ch, const SelectParams& 
     for (int x = 0; x < C::VV; ++x) ch.v[m][x] = ld16(vb + (16 * m + ql) * sb + x * C::VE);
 }
 
-template <typename T>
+template <typename T, int QB>
 __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
   using F = Frag16<T>;
   const Geometry& geo = p.g;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int ql = lane & 15, g = lane >> 4;
-  // One wave per (head, window, block of 16 of the window's s^2 queries).
+  // One wave per (head, window, group of QB blocks of 16 of the window's s^2
+  // queries); every gathered chunk serves the QB blocks from registers, so a
+  // window's K/V is gathered once (QB = the number of blocks, 1 for s <= 4).
   // Head-major order: all waves in flight gather from the same head's K/V
   // blocks (M' x 4 KB), a working set the 256 MB Infinity Cache can hold a
-  // large part of, instead of all heads' blocks at once.  The query blocks of
-  // a window are adjacent waves (mostly one workgroup), so their identical
-  // gathers meet in the caches instead of being repeated one after another.
+  // large part of, instead of all heads' blocks at once.
   const int s2 = (int)(geo.pool * geo.pool);
-  const int n_sub = (s2 + 15) / 16;
+  const int n_grp = ((s2 + 15) / 16 + QB - 1) / QB;
   const int64_t item = (int64_t)blockIdx.x * 4 + wv;
-  if (item >= geo.n_windows * geo.n_heads * n_sub) return;
-  const int qs = (int)(item % n_sub);
-  const int64_t h = item / n_sub / geo.n_windows;
-  const int64_t win = item / n_sub % geo.n_windows;
+  if (item >= geo.n_windows * geo.n_heads * n_grp) return;
+  const int qg = (int)(item % n_grp);
+  const int64_t h = item / n_grp / geo.n_windows;
+  const int64_t win = item / n_grp % geo.n_windows;
   const int64_t H = geo.n_heads;
   const int K = p.topk;
   const float c = p.scale_log2;
@@ -193,17 +193,30 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
   const int n_chunks = (int)((K * geo.sb + 31) / 32);
 
   {
-    const int kq = qs * 16 + ql;  // window-local query index
-    const bool qvalid = kq < s2;
-    const int64_t tok = window_token(geo, win, qvalid ? kq : 0);
-    const T* qrow = static_cast<const T*>(p.q) + (tok * H + h) * kHeadDim;
-    typename F::Q qf = F::load_q(qvalid ? qrow : nullptr, g);
+    // block b: window-local queries (QB qg + b) * 16 + ql
+    typename F::Q qfs[QB];
+    f32x4 os[QB][4];
+    float m_runs[QB], l_runs[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int kq = (QB * qg + b) * 16 + ql;
+      const bool qvalid = kq < s2;
+      const int64_t tok = window_token(geo, win, qvalid ? kq : 0);
+      qfs[b] = F::load_q(qvalid ? static_cast<const T*>(p.q) + (tok * H + h) * kHeadDim : nullptr, g);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) os[b][m] = f32x4{0, 0, 0, 0};
+      m_runs[b] = -INFINITY;
+      l_runs[b] = 0.0f;
+    }
 
-    f32x4 o[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    // One chunk: scores of 32 key slots, online softmax, PV.
-    auto process = [&](const SelChunk<T>& ch) {
+    // One chunk: scores of 32 key slots, online softmax, PV, for each block.
+    auto process = [&](const SelChunk<T>& ch) __attribute__((always_inline)) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+      const typename F::Q& qf = qfs[b];
+      f32x4 (&o)[4] = os[b];
+      float& m_run = m_runs[b];
+      float& l_run = l_runs[b];
       f32x4 s0 = F::qk(ch.k[0], qf);
       f32x4 s1 = F::qk(ch.k[1], qf);
 #pragma unroll
@@ -234,6 +247,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
       }
       l_run += ps;
       F::pv(ch.v, p0, p1, o);
+      }
     };
 
     // Two chunk buffers alternate so that two chunks of gathers are always in
@@ -253,6 +267,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
     if (ci + 1 < n_chunks) process(B);
     if (ci + 2 < n_chunks) process(A);
 
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+    if ((QB * qg + b) * 16 >= s2) continue;  // a block past the window's queries (uniform)
+    const int kq = (QB * qg + b) * 16 + ql;
+    const bool qvalid = kq < s2;
+    const int64_t tok = window_token(geo, win, qvalid ? kq : 0);
+    const typename F::Q& qf = qfs[b];
+    const f32x4 (&o)[4] = os[b];
+    const float m_run = m_runs[b], l_run = l_runs[b];
     float l = l_run + xor_lane(l_run, 16);
     l = l + xor_lane(l, 32);
 
@@ -305,6 +328,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
       for (int m = 0; m < 4; ++m)
         *reinterpret_cast<f32x4*>(p.osel + (u * H + h) * kHeadDim + 16 * m + 4 * g) = res[m];
     }
+    }
   }
 }
 
@@ -346,13 +370,23 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }
 
 hipError_t launch_select(int dtype, const SelectParams& p, hipStream_t stream) {
-  const int64_t items = p.g.n_windows * p.g.n_heads * ((p.g.pool * p.g.pool + 15) / 16);
+  // one wave per (window, head) serves all of the window's blocks of 16
+  // queries (s <= 8: at most 4 blocks)
+  const int n_sub = (int)((p.g.pool * p.g.pool + 15) / 16);
+  const int64_t items = p.g.n_windows * p.g.n_heads;
   if (items == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((items + 3) / 4);
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(select_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(select_kernel<float>, dim3(blocks), dim3(256), 0, stream, p);
+  if (dtype == kBF16) {
+    if (n_sub == 1) hipLaunchKernelGGL((select_kernel<__bf16, 1>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (n_sub == 2) hipLaunchKernelGGL((select_kernel<__bf16, 2>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (n_sub == 3) hipLaunchKernelGGL((select_kernel<__bf16, 3>), dim3(blocks), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((select_kernel<__bf16, 4>), dim3(blocks), dim3(256), 0, stream, p);
+  } else {
+    if (n_sub == 1) hipLaunchKernelGGL((select_kernel<float, 1>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (n_sub == 2) hipLaunchKernelGGL((select_kernel<float, 2>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (n_sub == 3) hipLaunchKernelGGL((select_kernel<float, 3>), dim3(blocks), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((select_kernel<float, 4>), dim3(blocks), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

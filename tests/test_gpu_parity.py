@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, element by
 element, on seeded inputs small enough for the whole oracle: the tiny fp32
 workload, the 32-frame bf16 workload, and edge shapes (ragged tails, s in
-{1, 2, 4, 8}, P = 0, fixed context, k beyond the candidate count, k = 40/64/128).
+{1, 2, 4, 5, 6, 8}, P = 0, fixed context, k beyond the candidate count, k = 40/64/128).
 """
 import numpy as np
 import pytest
@@ -22,6 +22,8 @@ SHAPES = {
     "odd_f32": GSAShape("odd 3f-12x8-h3-s4-k5 fp32", 3, 2, 12, 8, 3, 64, 4, 5, F32, seed=22),
     "s8": GSAShape("s8 3f-16x16-h2-s8-k3", 3, 1, 16, 16, 2, 64, 8, 3, BF16, seed=23),
     "s1": GSAShape("s1 2f-6x5-h2-s1-k7", 2, 1, 6, 5, 2, 64, 1, 7, BF16, seed=24),
+    "s5": GSAShape("s5 2f-10x10-h2-s5-k3", 2, 2, 10, 10, 2, 64, 5, 3, BF16, seed=33),
+    "s6": GSAShape("s6 3f-12x12-h2-s6-k3", 3, 1, 12, 12, 2, 64, 6, 3, BF16, seed=34),
     "s2_bf16": GSAShape("s2 4f-8x8-h2-s2-k4", 4, 3, 8, 8, 2, 64, 2, 4, BF16, seed=25),
     "p0": GSAShape("p0 4f-8x12-h2-s4-k3", 4, 0, 8, 12, 2, 64, 4, 3, BF16, seed=26),
     "ctx": GSAShape("ctx 6f-8x8-h2-s4-k3+ctx{0,3}", 6, 2, 8, 8, 2, 64, 4, 3, BF16, ctx_frames=(0, 3), seed=27),
