@@ -65,8 +65,8 @@ def copy_probe(mib: int):
 KERNEL_SOURCES = {
     "flash_kernel<bf16,4,partial>": ("flash.hip", "gsa_device.h", "gsa_kernels.h"),
     "flash_kernel<bf16,4,bound>": ("flash.hip", "gsa_device.h", "gsa_kernels.h"),
-    "refine_kernel<bf16,4>": ("flash.hip", "gsa_device.h", "gsa_kernels.h"),
-    "select_kernel<bf16>": ("select.hip", "gsa_device.h", "gsa_kernels.h"),
+    "refine_kernel<bf16,4,64>": ("flash.hip", "gsa_device.h", "gsa_kernels.h"),
+    "select_kernel<bf16,1>": ("select.hip", "gsa_device.h", "gsa_kernels.h"),
     "pool_kernel<bf16>": ("pool.hip", "gsa_device.h", "gsa_kernels.h"),
 }
 
@@ -215,7 +215,7 @@ def main():
         "pool_hbm_gbs": round(pool_bytes / (st["pool"] * 1e-3) / 1e9, 1),
         "pool_frac_hbm": round(pool_bytes / (st["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "select_gather_bytes": gather_bytes,
-        "compressed_step": {"kernels": ["flash_kernel<bf16,4,bound>", "refine_kernel<bf16,4>"],
+        "compressed_step": {"kernels": ["flash_kernel<bf16,4,bound>", "refine_kernel<bf16,4,64>"],
                             "ms": round(st["compressed_topk"], 4),
                             "flop": fl["compressed"] * 1.5,  # attention sweep + score-only sweep
                             "tflops": round((fl["compressed"] * 1.5) / (st["compressed_topk"] * 1e-3) / 1e12, 2)},
