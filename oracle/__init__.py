@@ -4,7 +4,8 @@ Thin ctypes wrapper over ``gsa_oracle.c``: a plain, double-precision,
 step-by-step CPU implementation of the Global Sparse Attention forward pass
 (Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models",
 sections "全局稀疏注意力（GSA）核心设计", "压缩分支", "选择分支", "门控聚合",
-"Speed3R-VGGT 适配").  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+"Speed3R-VGGT 适配"), and the frame attention it alternates with (section
+"整体框架").  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 bench's CPU-baseline leg use it.  It shares no code with the HIP library and
 imports nothing from it.
 
@@ -53,13 +54,14 @@ def _load():
         cfgp = ctypes.POINTER(OrcCfg)
         lib.orc_pool.argtypes = [cfgp, P, P]
         lib.orc_special.argtypes = [cfgp, P, P, P, P, I64, P]
+        lib.orc_frame.argtypes = [cfgp, P, P, P, P, I64, P]
         lib.orc_compressed.argtypes = [cfgp, P, P, P, P, I64, P, P, P, P]
         lib.orc_guide_scores.argtypes = [cfgp, P, P, P, I64, P, ctypes.c_int, P]
         lib.orc_select.argtypes = [cfgp, P, P, P, P, I64, P, ctypes.c_int, P]
         lib.orc_gate_combine.argtypes = [cfgp, P, P, P, P, I64, P, P, P]
         lib.orc_window_token.argtypes = [cfgp, I64, ctypes.c_int]
         lib.orc_window_token.restype = I64
-        for f in ("orc_pool", "orc_special", "orc_compressed", "orc_guide_scores", "orc_select",
+        for f in ("orc_pool", "orc_special", "orc_frame", "orc_compressed", "orc_guide_scores", "orc_select",
                   "orc_gate_combine"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -97,6 +99,15 @@ def special(sh, q, k, v, rows: np.ndarray) -> np.ndarray:
     rows = np.ascontiguousarray(rows, np.int64)
     out = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
     _load().orc_special(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(rows), rows.size, _p(out))
+    return out
+
+
+def frame(sh, q, k, v, rows: np.ndarray) -> np.ndarray:
+    """Frame attention (each token over the T_f tokens of its own frame) of the listed
+    token rows -> [n][H][d] float64."""
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
+    _load().orc_frame(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(rows), rows.size, _p(out))
     return out
 
 

@@ -6,7 +6,8 @@
  * Reconstruction Models" (CVPR 2026, arXiv 2603.08055), as described on the
  * Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models"
  * (sections "全局稀疏注意力（GSA）核心设计", "压缩分支", "选择分支",
- * "门控聚合", "Speed3R-VGGT 适配").  Only the tests, the package smoke check
+ * "门控聚合", "Speed3R-VGGT 适配"), and of the frame attention that
+ * alternates with it (section "整体框架").  Only the tests, the package smoke check
  * and the benchmark's CPU-baseline leg may call it; the HIP library never
  * does, and the two share no code.
  *
@@ -374,6 +375,37 @@ void orc_gate_combine(const orc_cfg* c, const void* q, const void* wg, const dou
         }
       }
     }
+}
+
+/* ======================================================================== */
+/* Frame attention: the local step that alternates with GSA in the
+ * aggregation transformer (Paper-Notes page, section "整体框架": blocks
+ * alternate intra-frame attention and global sparse attention).  Each token
+ * attends, in one softmax with the config scale, to every token of its own
+ * frame (special and image, T_f keys); frames do not see each other.
+ * rows[i] is a token id t in [0, M); out: [n][H][d]. */
+void orc_frame(const orc_cfg* c, const void* q, const void* k, const void* v,
+               const int64_t* rows, int64_t n, double* out) {
+  const int H = c->n_heads, d = c->head_dim;
+  const int64_t tf = tokens_per_frame(c);
+#pragma omp parallel
+  {
+    int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * tf);
+    double* logits = (double*)malloc(sizeof(double) * tf);
+    double* qrow = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t ih = 0; ih < n * H; ++ih) {
+      int64_t i = ih / H;
+      int h = (int)(ih % H);
+      int64_t t = rows[i], first = (t / tf) * tf;
+      for (int64_t j = 0; j < tf; ++j) toks[j] = first + j;
+      for (int e = 0; e < d; ++e) qrow[e] = elem(q, c->dtype, row_off(c, t, h) + e);
+      attend_tokens(c, qrow, k, v, toks, tf, h, logits, out + (i * H + h) * d);
+    }
+    free(toks);
+    free(logits);
+    free(qrow);
+  }
 }
 
 /* Token row of the qq-th pixel of window j (exported for the test harness,

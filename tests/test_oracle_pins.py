@@ -382,3 +382,44 @@ def test_guide_scores_are_the_raw_dot_products():
                     assert np.isnan(got[a, h, t])
                 else:
                     assert got[a, h, t] == float(qc[i, h].astype(np.int64) @ kc[j, h].astype(np.int64))
+
+
+# ---------------------------------------------------------------------------
+# P10 -- frame attention, the local step that alternates with GSA (section
+# "整体框架"): dense attention restricted to each frame, i.e. all-token
+# attention under a block-diagonal mask whose blocks are the frames.
+
+@pytest.mark.parametrize("dtype,n_special", [(F32, 0), (F32, 2), (BF16, 3)])
+def test_frame_attention_equals_block_diagonal_masked_attention(dtype, n_special):
+    sh = shape(n_frames=3, n_special=n_special, grid_h=6, grid_w=4, dtype=dtype)
+    q, k, v, _ = gen.make_inputs(sh)
+    rows = np.arange(sh.m_tokens)
+    got = oracle.frame(sh, q, k, v, rows)
+    frame_of = np.repeat(np.arange(sh.n_frames), sh.tokens_per_frame)  # from the token grid's rows
+    mask = np.where(frame_of[:, None] == frame_of[None, :], 0.0, -np.inf)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[:, h], K[:, h], V[:, h], sh.head_dim ** -0.5, mask)
+        np.testing.assert_allclose(got[:, h], ref, rtol=0, atol=1e-12)
+
+
+def test_frame_attention_of_one_frame_is_the_special_rows_dense_attention():
+    """With a single frame every token's frame is the whole sequence, so the special
+    rows' frame attention is the special-token attention over all M tokens."""
+    sh = shape(n_frames=1, n_special=3)
+    q, k, v, _ = gen.make_inputs(sh)
+    got = oracle.frame(sh, q, k, v, special_token_ids(sh))
+    ref = oracle.special(sh, q, k, v, np.arange(sh.m_spec))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
+
+
+def test_frame_attention_equal_keys_average_the_frame_values():
+    """Equal keys inside each frame give uniform weights: every output row is the mean
+    of its own frame's value rows (catches a key range off by one token or frame)."""
+    sh = shape(n_frames=3, n_special=1, grid_h=4, grid_w=6)
+    q, _, v, _ = gen.make_inputs(sh)
+    k = np.broadcast_to(np.float32(0.25), sh.qkv_shape).copy()
+    got = oracle.frame(sh, q, k, v, np.arange(sh.m_tokens))
+    V = flat(v, sh).reshape(sh.n_frames, sh.tokens_per_frame, sh.n_heads, sh.head_dim)
+    ref = np.repeat(V.mean(1), sh.tokens_per_frame, axis=0)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
