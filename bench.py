@@ -222,6 +222,15 @@ def main():
         "wall_s_timed_region": round(t_wall, 3),
         "input_gen_s": round(t_gen, 1),
     }
+    # Frame attention, the dense per-frame step that alternates with GSA in the
+    # aggregation transformer: its time and one alternating pair (frame + GSA).
+    t_frame = timed(lambda: gsa.gsa_frame_attn(cfg, dq, dk, dv, o2, stream=stream), reps)
+    detail["frame_attention"] = {
+        "kernel": "flash_kernel<bf16,4,final>" if sh.dtype == gen.BF16 else "flash_kernel<f32,4,final>",
+        "ms": round(t_frame, 4), "flop": fl["frame"],
+        "tflops": round(fl["frame"] / (t_frame * 1e-3) / 1e12, 2),
+        "frac_mfma_peak": round(fl["frame"] / (t_frame * 1e-3) / 1e12 / peak, 4),
+        "alternating_pair_ms": round(t_frame + ms_step, 4)}
     del ws_spec, ws_sel, ws_cmp, o2, osel
 
     # ---- dense comparator at the same shape --------------------------------------

@@ -79,6 +79,7 @@ class GSAShape:
             "compressed": 4.0 * self.n_windows ** 2 * d * h,
             "selection": 4.0 * self.m_img * keys_sel * d * h,
             "dense": 4.0 * self.m_tokens ** 2 * d * h,
+            "frame": 4.0 * self.n_frames * self.tokens_per_frame ** 2 * d * h,
         }
 
 

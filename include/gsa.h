@@ -164,6 +164,18 @@ gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, cons
 gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, const void* v,
                           void* o, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Frame attention, the dense per-frame step that the aggregation transformer
+ * alternates with GSA (section "整体框架": blocks alternate intra-frame
+ * attention and global sparse attention).  Every token (special and image)
+ * attends, in one softmax with the config scale, to the T_f tokens of its own
+ * frame.  Uses n_frames, n_special, grid_h, grid_w, n_heads, head_dim, scale
+ * and dtype of cfg (the other fields are validated as for every entry point).
+ * Writes every row of o.  No workspace.
+ */
+gsa_status gsa_frame_attn(const gsa_config* cfg, const void* q, const void* k, const void* v, void* o,
+                          void* stream);
+
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status status);
 

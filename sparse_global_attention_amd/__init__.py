@@ -30,7 +30,8 @@ GSA_OP_FORWARD, GSA_OP_SPECIAL, GSA_OP_SELECT, GSA_OP_DENSE, GSA_OP_COMPRESSED =
 GSA_MAX_CTX_FRAMES = 16
 
 EXPORTS = ("gsa_workspace_size", "gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn",
-           "gsa_special_attn", "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_status_string")
+           "gsa_special_attn", "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn",
+           "gsa_status_string")
 
 
 class GSAConfig(ctypes.Structure):
@@ -83,6 +84,7 @@ _sig = {
     "gsa_gate_combine": [_CFG, _P, _P, _P, _P, _P, _P, _P],
     "gsa_forward": [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_dense_attn": [_CFG, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "gsa_frame_attn": [_CFG, _P, _P, _P, _P, _P],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).argtypes = _args
@@ -166,6 +168,11 @@ def gsa_dense_attn(cfg, q, k, v, o, ws=None, ws_bytes=None, stream=None):
     wsb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(_lib.gsa_dense_attn(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(ws), wsb,
                                _stream(stream)), "gsa_dense_attn")
+
+
+def gsa_frame_attn(cfg, q, k, v, o, stream=None):
+    _check(_lib.gsa_frame_attn(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(stream)),
+           "gsa_frame_attn")
 
 
 def call_status(fn: str, *args) -> int:

@@ -349,12 +349,14 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   const int64_t qt = w % n_qt;
   const int64_t hs = w / n_qt;
   const int h = (int)(hs % p.n_heads);
-  const int split = (int)(hs / p.n_heads);
+  const int64_t sb = hs / p.n_heads;
+  const int split = (int)(sb % p.n_splits);
+  const int64_t batch = sb / p.n_splits;
 
   const int64_t qrow = qt * QW + wv * 32 + r;
   const bool qvalid = qrow < p.n_q;
   const int64_t hoff = (int64_t)h * kHeadDim;
-  const int64_t qtok = (qrow / p.qa) * p.qb + p.qc + qrow % p.qa;
+  const int64_t qtok = batch * p.q_bstride + (qrow / p.qa) * p.qb + p.qc + qrow % p.qa;
   const T* K = static_cast<const T*>(p.k);
   const T* V = static_cast<const T*>(p.v);
   typename F::Q qf = F::load_q(qvalid ? static_cast<const T*>(p.q) + qtok * p.row_stride + hoff : nullptr, hf);
@@ -388,8 +390,8 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   // loads in flight across the barriers.
   // Positions inside the range are int32 (the host keeps token counts below
   // 2^31 - 64), so the per-tile bookkeeping is scalar 32-bit arithmetic.
-  const int64_t kb = p.kbeg[split];
-  const int nk = (int)(p.kend[split] - kb);
+  const int64_t kb = p.kbeg[split] + batch * p.k_bstride;
+  const int nk = (int)(p.kend[split] - p.kbeg[split]);
   const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
   if (gend > n_tiles - 1) gend = n_tiles - 1;
   auto tile_rel = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
@@ -1042,8 +1044,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 template <typename T, int WAVES, int MODE>
 static hipError_t launch_flash_t(const FlashParams& p, hipStream_t stream) {
   const int64_t n_qt = (p.n_q + WAVES * 32 - 1) / (WAVES * 32);
-  const int64_t blocks = n_qt * p.n_heads * p.n_splits;
+  const int64_t blocks = n_qt * p.n_heads * p.n_splits * p.n_batch;
   if (blocks == 0) return hipSuccess;
+  if (p.n_batch < 1 || (p.n_batch > 1 && MODE != kFlashFinal) || blocks > 0xffffffffLL) return hipErrorInvalidValue;
   size_t lds = sizeof(T) == 2 ? 0 : 2 * (size_t)Tile<T>::BYTES;  // bf16 tiles live in static LDS
   const void* fn = reinterpret_cast<const void*>(&flash_kernel<T, WAVES, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -190,6 +190,7 @@ FlashParams flash_base(const Call& c, const void* q, const void* k, const void* 
   f.row_stride = c.g.n_heads * kHeadDim;
   f.n_heads = (int)c.g.n_heads;
   f.scale_log2 = c.scale * kLog2e;
+  f.n_batch = 1;
   return f;
 }
 
@@ -487,6 +488,26 @@ gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, c
   f.n_splits = 1;
   f.kbeg[0] = 0;
   f.kend[0] = c.g.m_tokens;
+  f.o = o;
+  return hip_status(launch_flash(c.dtype, kFlashFinal, f, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_frame_attn(const gsa_config* cfg, const void* q, const void* k, const void* v, void* o,
+                          void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v) return GSA_ERR_INVALID_ARG;
+  // one batch per frame: its T_f query rows over its own T_f keys
+  FlashParams f = flash_base(c, q, k, v);
+  set_rows_identity(f, c.g.tf);
+  f.n_splits = 1;
+  f.kbeg[0] = 0;
+  f.kend[0] = c.g.tf;
+  f.n_batch = c.g.n_frames;
+  f.q_bstride = c.g.tf;
+  f.k_bstride = c.g.tf;
   f.o = o;
   return hip_status(launch_flash(c.dtype, kFlashFinal, f, static_cast<hipStream_t>(stream)));
 }

@@ -79,6 +79,9 @@ struct FlashParams {
   // key splits: split s covers the non-empty contiguous key range [kbeg[s], kend[s])
   int n_splits;
   int64_t kbeg[kMaxRanges], kend[kMaxRanges];
+  // independent batches (kFlashFinal only; 1 otherwise): batch b shifts every
+  // query token row by b * q_bstride and every key range by b * k_bstride
+  int64_t n_batch, q_bstride, k_bstride;
   float scale_log2;  // softmax scale * log2(e)
   // kFlashFinal: normalised output in the input dtype at rows token(r) of o
   void* o;

@@ -97,6 +97,12 @@ class Case:
         gsa.gsa_forward(self.cfg, self.dq, self.dk, self.dv, self.dwg, o, ws)
         return o
 
+    def frame(self):
+        sh = self.sh
+        o = torch.zeros(sh.qkv_shape, dtype=self.dq.dtype, device=DEV)
+        gsa.gsa_frame_attn(self.cfg, self.dq, self.dk, self.dv, o)
+        return o
+
     def dense(self):
         sh = self.sh
         o = torch.zeros(sh.qkv_shape, dtype=self.dq.dtype, device=DEV)

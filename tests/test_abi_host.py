@@ -28,7 +28,8 @@ def header_functions():
 def test_header_declares_the_boundary():
     fns = header_functions()
     for want in ("gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn", "gsa_special_attn",
-                 "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_workspace_size", "gsa_status_string"):
+                 "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn", "gsa_workspace_size",
+                 "gsa_status_string"):
         assert want in fns
 
 
@@ -106,6 +107,9 @@ def test_pointer_validation(lib):
     assert lib.call_status("gsa_forward", c, A, A, A, A, A, A, 1 << 30, None) == 1  # o aliases q
     assert lib.call_status("gsa_special_attn", c, A, A, A, A, A, 1 << 30, None) == 1  # o aliases q
     assert lib.call_status("gsa_dense_attn", c, A, A + 16, A + 32, A, None, 0, None) == 1  # o aliases q
+    assert lib.call_status("gsa_frame_attn", c, A, A + 16, A + 32, A + 32, None) == 1  # o aliases v
+    assert lib.call_status("gsa_frame_attn", c, A, None, A + 32, A + 48, None) == 1
+    assert lib.call_status("gsa_frame_attn", c, A, A + 16, MISALIGNED, A + 48, None) == 1
 
 
 def test_workspace_validation(lib):

@@ -7,7 +7,8 @@ times (gsa_forward), checked on sampled outputs the oracle computes one by one:
 * the forward's image rows of those windows (oracle selection driven by the
   GPU's index sets, then upsample + gate);
 * the forward's special rows: sampled special tokens x all heads;
-* determinism: a second forward is bitwise identical.
+* determinism: a second forward is bitwise identical;
+* frame attention (the per-frame step beside GSA): sampled tokens x all heads.
 
 Workloads: VGGT-style 128 frames with fixed context {0, 100}; the pi^3-style
 1000-frame sequence; the peaky clustered 1024-frame sequence.
@@ -43,6 +44,13 @@ def test_full_size_sampled_parity(name):
     c = Case(sh)
     log(f"[{name}] inputs on device ({time.time() - t0:.0f} s); forward + pool + top-k on the GPU")
     out = c.forward()
+    fr_rows = np.unique(np.concatenate([np.arange(sh.tokens_per_frame),
+                                        np.arange(sh.m_tokens - sh.tokens_per_frame, sh.m_tokens),
+                                        np.random.default_rng(sh.seed + 5).choice(sh.m_tokens, 256, replace=False)]))
+    fr = c.frame()
+    o_frame = to_host(fr.view(sh.m_tokens, sh.n_heads, sh.head_dim).index_select(
+        0, torch.from_numpy(fr_rows).cuda()))
+    del fr
     qc, kc, vc = c.pool()
     oc, idx, _ = c.compressed(qc, kc, vc, with_scores=False)
     again = c.forward()
@@ -84,4 +92,9 @@ def test_full_size_sampled_parity(name):
     log(f"[{name}] oracle: special attention for {len(rows)} rows ({time.time() - t0:.0f} s)")
     ospec = oracle.special(sh, c.q, c.k, c.v, rows)
     mx, mean, rel = assert_close(o_spec, ospec, sh.dtype, f"{name} O_spec (sampled)")
-    log(f"[{name}] O_spec: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}; done in {time.time() - t0:.0f} s")
+    log(f"[{name}] O_spec: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}")
+
+    log(f"[{name}] oracle: frame attention for {len(fr_rows)} rows ({time.time() - t0:.0f} s)")
+    ofr = oracle.frame(sh, c.q, c.k, c.v, fr_rows)
+    mx, mean, rel = assert_close(o_frame, ofr, sh.dtype, f"{name} frame attention (sampled)")
+    log(f"[{name}] frame: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}; done in {time.time() - t0:.0f} s")

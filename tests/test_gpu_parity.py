@@ -1,7 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, element by
 element, on seeded inputs small enough for the whole oracle: the tiny fp32
 workload, the 32-frame bf16 workload, and edge shapes (ragged tails, s in
-{1, 2, 4, 5, 6, 8}, P = 0, fixed context, k beyond the candidate count, k = 40/64/128).
+{1, 2, 4, 5, 6, 8}, P = 0, fixed context, k beyond the candidate count, k = 40/64/128),
+and frame attention (every token over its own frame) on the same workloads
+plus one frame of the pi^3-style size (T_f = 1301).
 """
 import numpy as np
 import pytest
@@ -279,3 +281,26 @@ def test_scores_growing_along_the_keys():
         w = np.exp(s - s.max(1, keepdims=True))
         ref = (w / w.sum(1, keepdims=True)) @ V[:, h]
         assert_close(gdense[:, h], ref, sh.dtype, f"grow dense head {h}")
+
+
+# ---- frame attention (section "整体框架": the per-frame step beside GSA) ----
+
+FRAME_SHAPES = dict(SHAPES)
+FRAME_SHAPES["tf1301"] = GSAShape("frames 3f-36x36-h2-P5", 3, 5, 36, 36, 2, 64, 4, 3, BF16, seed=35)
+FRAME_SHAPES["tf1301_f32"] = GSAShape("frames 2f-36x36-h1-P5 fp32", 2, 5, 36, 36, 1, 64, 4, 3, F32, seed=36)
+
+
+@pytest.mark.parametrize("name", list(FRAME_SHAPES))
+def test_frame_attention(name):
+    sh = FRAME_SHAPES[name]
+    c = Case(sh)
+    got = to_host(c.frame()).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    tf = sh.tokens_per_frame
+    if sh.m_tokens * tf <= 6_000_000:
+        rows = np.arange(sh.m_tokens)
+    else:  # first and last frame whole, plus sampled rows of the others
+        rng = np.random.default_rng(sh.seed)
+        rows = np.unique(np.concatenate([np.arange(tf), np.arange(sh.m_tokens - tf, sh.m_tokens),
+                                         rng.choice(sh.m_tokens, 512, replace=False)]))
+    ref = oracle.frame(sh, c.q, c.k, c.v, rows)
+    assert_close(got[rows], ref, sh.dtype, f"{name} frame attention")
