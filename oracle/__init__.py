@@ -4,8 +4,10 @@ Thin ctypes wrapper over ``gsa_oracle.c``: a plain, double-precision,
 step-by-step CPU implementation of the Global Sparse Attention forward pass
 (Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models",
 sections "全局稀疏注意力（GSA）核心设计", "压缩分支", "选择分支", "门控聚合",
-"Speed3R-VGGT 适配"), and the frame attention it alternates with (section
-"整体框架").  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+"Speed3R-VGGT 适配"), the frame attention it alternates with (section
+"整体框架"), and the descriptor attention of the Paper-Notes page "FlashVGGT:
+Efficient and Scalable Visual Geometry Transformers with Compressed Descriptor
+Attention" (section "关键设计").  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 bench's CPU-baseline leg use it.  It shares no code with the HIP library and
 imports nothing from it.
 
@@ -55,13 +57,17 @@ def _load():
         lib.orc_pool.argtypes = [cfgp, P, P]
         lib.orc_special.argtypes = [cfgp, P, P, P, P, I64, P]
         lib.orc_frame.argtypes = [cfgp, P, P, P, P, I64, P]
+        lib.orc_descriptor_count.argtypes = [cfgp]
+        lib.orc_descriptor_count.restype = I64
+        lib.orc_descriptor_set.argtypes = [cfgp, P, P]
+        lib.orc_descriptor_attn.argtypes = [cfgp, P, P, P, I64, P, I64, P]
         lib.orc_compressed.argtypes = [cfgp, P, P, P, P, I64, P, P, P, P]
         lib.orc_guide_scores.argtypes = [cfgp, P, P, P, I64, P, ctypes.c_int, P]
         lib.orc_select.argtypes = [cfgp, P, P, P, P, I64, P, ctypes.c_int, P]
         lib.orc_gate_combine.argtypes = [cfgp, P, P, P, P, I64, P, P, P]
         lib.orc_window_token.argtypes = [cfgp, I64, ctypes.c_int]
         lib.orc_window_token.restype = I64
-        for f in ("orc_pool", "orc_special", "orc_frame", "orc_compressed", "orc_guide_scores", "orc_select",
+        for f in ("orc_pool", "orc_special", "orc_frame", "orc_descriptor_set", "orc_descriptor_attn", "orc_compressed", "orc_guide_scores", "orc_select",
                   "orc_gate_combine"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -108,6 +114,28 @@ def frame(sh, q, k, v, rows: np.ndarray) -> np.ndarray:
     rows = np.ascontiguousarray(rows, np.int64)
     out = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
     _load().orc_frame(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(rows), rows.size, _p(out))
+    return out
+
+
+def descriptor_set(sh, x: np.ndarray) -> np.ndarray:
+    """FlashVGGT key/value set of x: bilinear r x r descriptors (r = pool) of every frame, then
+    the auxiliary tokens (frame 0 and the keyframes ctx_frames whole, the other frames'
+    special tokens) -> float32 [n_set][H][d] (values in the input precision)."""
+    cfg = cfg_of(sh)
+    n = _load().orc_descriptor_count(ctypes.byref(cfg))
+    out = np.empty((n, sh.n_heads, sh.head_dim), np.float32)
+    _load().orc_descriptor_set(ctypes.byref(cfg), _p(x), _p(out))
+    return out
+
+
+def descriptor_attn(sh, q, kd: np.ndarray, vd: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Descriptor attention of the listed token rows over the set kd/vd -> [n][H][d] float64."""
+    rows = np.ascontiguousarray(rows, np.int64)
+    kd = np.ascontiguousarray(kd, np.float32)
+    vd = np.ascontiguousarray(vd, np.float32)
+    out = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
+    _load().orc_descriptor_attn(ctypes.byref(cfg_of(sh)), _p(q), _p(kd), _p(vd), kd.shape[0], _p(rows),
+                                rows.size, _p(out))
     return out
 
 

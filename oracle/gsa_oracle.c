@@ -6,8 +6,10 @@
  * Reconstruction Models" (CVPR 2026, arXiv 2603.08055), as described on the
  * Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models"
  * (sections "全局稀疏注意力（GSA）核心设计", "压缩分支", "选择分支",
- * "门控聚合", "Speed3R-VGGT 适配"), and of the frame attention that
- * alternates with it (section "整体框架").  Only the tests, the package smoke check
+ * "门控聚合", "Speed3R-VGGT 适配"), of the frame attention that alternates
+ * with it (section "整体框架"), and of the descriptor attention of the
+ * Paper-Notes page "FlashVGGT: Efficient and Scalable Visual Geometry
+ * Transformers with Compressed Descriptor Attention".  Only the tests, the package smoke check
  * and the benchmark's CPU-baseline leg may call it; the HIP library never
  * does, and the two share no code.
  *
@@ -401,6 +403,121 @@ void orc_frame(const orc_cfg* c, const void* q, const void* k, const void* v,
       for (int64_t j = 0; j < tf; ++j) toks[j] = first + j;
       for (int e = 0; e < d; ++e) qrow[e] = elem(q, c->dtype, row_off(c, t, h) + e);
       attend_tokens(c, qrow, k, v, toks, tf, h, logits, out + (i * H + h) * d);
+    }
+    free(toks);
+    free(logits);
+    free(qrow);
+  }
+}
+
+/* ======================================================================== */
+/* FlashVGGT descriptor attention (Paper-Notes page "FlashVGGT: Efficient and
+ * Scalable Visual Geometry Transformers with Compressed Descriptor
+ * Attention", section "关键设计": spatially compressed descriptor tokens,
+ * descriptor attention, and the auxiliary descriptor tokens of "关键发现").
+ * The downsampling factor r is the config's pool field and the keyframes are
+ * its ctx_frames list.
+ *
+ * The key/value set, in this order:
+ *   1. descriptors: each frame's h x w image grid bilinearly resampled to
+ *      (h/r) x (w/r), half-pixel centres: output (y, x) samples the input at
+ *      ((y + 0.5) r - 0.5, (x + 0.5) r - 0.5); frame-major, then row-major;
+ *   2. every token (special and image) of frame 0 and of each listed
+ *      keyframe (list order, frame 0 not repeated);
+ *   3. the special (camera) tokens of every other frame, frame-major. */
+
+static int is_full_aux(const orc_cfg* c, int64_t f) { return f == 0 || is_ctx_frame(c, f); }
+
+int64_t orc_descriptor_count(const orc_cfg* c) {
+  const int r = c->pool;
+  int64_t n = (int64_t)c->n_frames * (c->grid_h / r) * (c->grid_w / r);
+  for (int64_t f = 0; f < c->n_frames; ++f)
+    n += is_full_aux(c, f) ? tokens_per_frame(c) : c->n_special;
+  return n;
+}
+
+/* One bilinear sample (a float, before rounding to the input precision):
+ * the corner weights are the products of the row and column weights, the
+ * four weighted values are added in the order (y0,x0), (y0,x1), (y1,x0),
+ * (y1,x1) in float; a coordinate past the last row or column is clamped. */
+static float bilinear_sample(const orc_cfg* c, const void* x, int64_t f, int y, int xx, int h, int e) {
+  const int r = c->pool;
+  const double sy = (y + 0.5) * r - 0.5, sx = (xx + 0.5) * r - 0.5;
+  int y0 = (int)floor(sy), x0 = (int)floor(sx);
+  const float fy = (float)(sy - y0), fx = (float)(sx - x0);
+  int y1 = y0 + 1 < c->grid_h ? y0 + 1 : c->grid_h - 1;
+  int x1 = x0 + 1 < c->grid_w ? x0 + 1 : c->grid_w - 1;
+  const int64_t base = f * tokens_per_frame(c) + c->n_special;
+  const int ys[2] = {y0, y1}, xs[2] = {x0, x1};
+  const float wy[2] = {1.0f - fy, fy}, wx[2] = {1.0f - fx, fx};
+  float acc = 0.0f;
+  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b) {
+      const float w = wy[a] * wx[b];
+      const float v = (float)elem(x, c->dtype, row_off(c, base + (int64_t)ys[a] * c->grid_w + xs[b], h) + e);
+      acc = acc + w * v;
+    }
+  return acc;
+}
+
+/* The key (or value) set of x as float [n][H][d] (values exactly
+ * representable in the input precision: descriptors are rounded to it). */
+void orc_descriptor_set(const orc_cfg* c, const void* x, float* out) {
+  const int r = c->pool, H = c->n_heads, d = c->head_dim;
+  const int dh = c->grid_h / r, dw = c->grid_w / r;
+  const int64_t tf = tokens_per_frame(c);
+  const int64_t nd = (int64_t)c->n_frames * dh * dw;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nd; ++i) {
+    const int64_t f = i / ((int64_t)dh * dw);
+    const int y = (int)((i / dw) % dh), xx = (int)(i % dw);
+    for (int h = 0; h < H; ++h)
+      for (int e = 0; e < d; ++e) {
+        const float m = bilinear_sample(c, x, f, y, xx, h, e);
+        out[(i * H + h) * d + e] = c->dtype == 1 ? m : round_bf16(m);
+      }
+  }
+  int64_t row = nd;
+  int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (c->n_frames + 1));
+  int n_full = 0;
+  order[n_full++] = 0;
+  for (int i = 0; i < c->n_ctx; ++i)
+    if (c->ctx_frames[i] != 0) order[n_full++] = c->ctx_frames[i];
+  for (int i = 0; i < n_full; ++i)
+    for (int64_t t = 0; t < tf; ++t, ++row)
+      for (int h = 0; h < H; ++h)
+        for (int e = 0; e < d; ++e)
+          out[(row * H + h) * d + e] = (float)elem(x, c->dtype, row_off(c, order[i] * tf + t, h) + e);
+  for (int64_t f = 0; f < c->n_frames; ++f) {
+    if (is_full_aux(c, f)) continue;
+    for (int64_t t = 0; t < c->n_special; ++t, ++row)
+      for (int h = 0; h < H; ++h)
+        for (int e = 0; e < d; ++e)
+          out[(row * H + h) * d + e] = (float)elem(x, c->dtype, row_off(c, f * tf + t, h) + e);
+  }
+  free(order);
+}
+
+/* Descriptor attention of the listed token rows: each query (any token, full
+ * resolution) attends, in one softmax with the config scale, to all n_set
+ * rows of the key/value set kd/vd (float [n_set][H][d]).  out: [n][H][d]. */
+void orc_descriptor_attn(const orc_cfg* c, const void* q, const float* kd, const float* vd, int64_t n_set,
+                         const int64_t* rows, int64_t n, double* out) {
+  const int H = c->n_heads, d = c->head_dim;
+  orc_cfg cf = *c;
+  cf.dtype = 1; /* the set is float */
+#pragma omp parallel
+  {
+    int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * n_set);
+    double* logits = (double*)malloc(sizeof(double) * n_set);
+    double* qrow = (double*)malloc(sizeof(double) * d);
+    for (int64_t t = 0; t < n_set; ++t) toks[t] = t;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t ih = 0; ih < n * H; ++ih) {
+      int64_t i = ih / H;
+      int h = (int)(ih % H);
+      for (int e = 0; e < d; ++e) qrow[e] = elem(q, c->dtype, row_off(c, rows[i], h) + e);
+      attend_tokens(&cf, qrow, kd, vd, toks, n_set, h, logits, out + (i * H + h) * d);
     }
     free(toks);
     free(logits);

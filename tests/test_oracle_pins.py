@@ -423,3 +423,88 @@ def test_frame_attention_equal_keys_average_the_frame_values():
     V = flat(v, sh).reshape(sh.n_frames, sh.tokens_per_frame, sh.n_heads, sh.head_dim)
     ref = np.repeat(V.mean(1), sh.tokens_per_frame, axis=0)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# P11 -- FlashVGGT descriptor attention (Paper-Notes page "FlashVGGT: Efficient
+# and Scalable Visual Geometry Transformers with Compressed Descriptor
+# Attention", section "关键设计"; auxiliary tokens from "关键发现").  The
+# downsampling factor r is the config's pool field, the keyframes its
+# ctx_frames.
+
+def _image_planes(x64, sh):
+    """[N][T_f][H][d] -> torch [N, H*d, h, w] of the image tokens (float64)."""
+    img = x64.reshape(sh.n_frames, sh.tokens_per_frame, sh.n_heads * sh.head_dim)[:, sh.n_special:]
+    img = img.reshape(sh.n_frames, sh.grid_h, sh.grid_w, -1).transpose(0, 3, 1, 2)
+    return torch.from_numpy(np.ascontiguousarray(img))
+
+
+def _torch_descriptors(x64, sh):
+    r = sh.pool
+    out = torch.nn.functional.interpolate(_image_planes(x64, sh), size=(sh.grid_h // r, sh.grid_w // r),
+                                          mode="bilinear", align_corners=False)
+    return out.permute(0, 2, 3, 1).reshape(-1, sh.n_heads, sh.head_dim).numpy()
+
+
+def _aux_token_ids(sh, keyframes):
+    grid = token_grid(sh)
+    full = [0] + [f for f in keyframes if f != 0]
+    rest = [f for f in range(sh.n_frames) if f not in full]
+    return np.concatenate([grid[full].reshape(-1), grid[rest, :sh.n_special].reshape(-1)])
+
+
+@pytest.mark.parametrize("r", [1, 2, 3, 4])
+def test_descriptors_equal_torch_bilinear_resampling(r):
+    sh = shape(n_frames=2, n_special=2, grid_h=12, grid_w=12, pool=r)
+    _, k, _, _ = gen.make_inputs(sh)
+    got = oracle.descriptor_set(sh, k).astype(np.float64)
+    nd = sh.n_frames * (sh.grid_h // r) * (sh.grid_w // r)
+    ref = _torch_descriptors(f64(k, sh), sh)
+    # four weighted corners summed in float: at most 3 roundings of partial
+    # sums bounded by the sum of the terms' magnitudes
+    bound = 3 * 2.0 ** -24 * _torch_descriptors(np.abs(f64(k, sh)), sh)
+    assert np.all(np.abs(got[:nd] - ref) <= bound + 1e-30)
+    if r % 2 == 1:  # odd r samples one pixel exactly
+        np.testing.assert_array_equal(got[:nd], ref)
+
+
+def test_descriptors_r4_are_the_mean_of_the_central_2x2():
+    """Half-pixel centres at r = 4 sample between rows 4y+1 and 4y+2 (weights 1/2 each)."""
+    sh = shape(n_frames=2, n_special=1, grid_h=8, grid_w=12, pool=4)
+    rng = np.random.default_rng(4)
+    x = rng.integers(-8, 9, size=sh.qkv_shape).astype(np.float32)
+    got = oracle.descriptor_set(sh, x)
+    img = x.astype(np.float64).reshape(sh.n_frames, sh.tokens_per_frame, -1)[:, 1:]
+    img = img.reshape(sh.n_frames, 2, 4, 3, 4, sh.n_heads, sh.head_dim)
+    ref = img[:, :, 1:3, :, 1:3].mean(axis=(2, 4)).reshape(-1, sh.n_heads, sh.head_dim)
+    np.testing.assert_array_equal(got[:ref.shape[0]].astype(np.float64), ref)  # small integers: exact
+
+
+def test_descriptor_set_bf16_rounds_and_carries_the_auxiliary_tokens():
+    sh = shape(n_frames=5, n_special=3, grid_h=8, grid_w=8, pool=4, dtype=BF16, ctx_frames=(3, 0))
+    _, _, v, _ = gen.make_inputs(sh)
+    got = oracle.descriptor_set(sh, v)
+    nd = sh.n_frames * 4
+    aux = _aux_token_ids(sh, (3, 0))
+    assert got.shape[0] == nd + aux.size == nd + 2 * sh.tokens_per_frame + 3 * sh.n_special
+    np.testing.assert_array_equal(got[nd:].astype(np.float64), flat(v, sh)[aux])
+    ref = _torch_descriptors(f64(v, sh), sh)
+    assert np.all(np.abs(got[:nd] - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30)
+    assert np.all(got[:nd].view(np.uint32) & 0xFFFF == 0)
+
+
+@pytest.mark.parametrize("keyframes", [(), (2,)])
+def test_descriptor_attention_equals_attention_over_the_set(keyframes):
+    sh = shape(n_frames=4, n_special=2, grid_h=8, grid_w=8, pool=4, ctx_frames=keyframes)
+    q, k, v, _ = gen.make_inputs(sh)
+    rows = np.arange(sh.m_tokens)
+    kd, vd = oracle.descriptor_set(sh, k), oracle.descriptor_set(sh, v)
+    got = oracle.descriptor_attn(sh, q, kd, vd, rows)
+    # the set rebuilt from torch's resampling and numpy indexing
+    aux = _aux_token_ids(sh, keyframes)
+    K = np.concatenate([_torch_descriptors(f64(k, sh), sh), flat(k, sh)[aux]])
+    V = np.concatenate([_torch_descriptors(f64(v, sh), sh), flat(v, sh)[aux]])
+    Q = flat(q, sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[:, h], K[:, h], V[:, h], sh.head_dim ** -0.5)
+        np.testing.assert_allclose(got[:, h], ref, rtol=0, atol=2e-6)
