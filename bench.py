@@ -231,6 +231,24 @@ def main():
         "tflops": round(fl["frame"] / (t_frame * 1e-3) / 1e12, 2),
         "frac_mfma_peak": round(fl["frame"] / (t_frame * 1e-3) / 1e12 / peak, 4),
         "alternating_pair_ms": round(t_frame + ms_step, 4)}
+    # FlashVGGT descriptor attention at the same shape (r = s, keyframes = the
+    # context frames): building the key/value set, then every token over it.
+    n_set = gsa.gsa_descriptor_count(cfg)
+    kd, vd = (torch.empty((n_set, H, d), dtype=dq.dtype, device=dev) for _ in range(2))
+    t_dset = timed(lambda: gsa.gsa_descriptor_set(cfg, dk, dv, kd, vd, stream=stream), reps)
+    t_datt = timed(lambda: gsa.gsa_descriptor_attn(cfg, dq, kd, vd, o2, stream=stream), max(2, reps // 4))
+    datt_flop = 4.0 * sh.m_tokens * n_set * d * H
+    dset_bytes = (2 * sh.n_frames * (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool) * 4
+                  + 2 * (n_set - sh.n_frames * (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool))
+                  + 2 * n_set) * H * d * esz
+    detail["descriptor_attention"] = {
+        "kernels": ["descriptor_kernel", "flash_kernel<bf16,4,final>" if sh.dtype == gen.BF16 else
+                    "flash_kernel<f32,4,final>"],
+        "n_set": n_set, "set_ms": round(t_dset, 4), "set_hbm_gbs": round(dset_bytes / (t_dset * 1e-3) / 1e9, 1),
+        "attn_ms": round(t_datt, 4), "attn_flop": datt_flop,
+        "attn_tflops": round(datt_flop / (t_datt * 1e-3) / 1e12, 2),
+        "attn_frac_mfma_peak": round(datt_flop / (t_datt * 1e-3) / 1e12 / peak, 4)}
+    del kd, vd
     del ws_spec, ws_sel, ws_cmp, o2, osel
 
     # ---- dense comparator at the same shape --------------------------------------

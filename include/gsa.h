@@ -176,6 +176,39 @@ gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, c
 gsa_status gsa_frame_attn(const gsa_config* cfg, const void* q, const void* k, const void* v, void* o,
                           void* stream);
 
+/*
+ * FlashVGGT descriptor attention (Paper-Notes page "FlashVGGT: Efficient and
+ * Scalable Visual Geometry Transformers with Compressed Descriptor
+ * Attention", section "关键设计": compressed descriptor tokens and descriptor
+ * cross-attention; section "关键发现": auxiliary descriptor tokens).  These
+ * three calls use the config's pool field as the downsampling factor r and
+ * its ctx_frames as the keyframes (chosen by the caller); ctx_exclude_from_topk
+ * and topk are validated but unused.
+ *
+ * The key/value set has n_set rows [n_set][H][d] (dtype), in this order:
+ *   - descriptors: each frame's h x w image grid bilinearly resampled to
+ *     (h/r) x (w/r) with half-pixel centres (output (y, x) samples the input
+ *     at ((y + 0.5) r - 0.5, (x + 0.5) r - 0.5)), frame-major, row-major; the
+ *     four weighted corners are summed in float in the order (y0,x0), (y0,x1),
+ *     (y1,x0), (y1,x1) and rounded to the dtype (nearest even);
+ *   - every token of frame 0 and of each keyframe (list order, frame 0 once);
+ *   - the P special (camera) tokens of every other frame, frame-major.
+ * n_set = N (h/r)(w/r) + n_full T_f + (N - n_full) P with n_full = the number
+ * of distinct frames among {0} and the keyframes.
+ */
+gsa_status gsa_descriptor_count(const gsa_config* cfg, int64_t* n_set);
+
+/* Builds the key set kd and the value set vd from k and v.  GSA_ERR_SHAPE if
+ * n_set >= 2^31 - 64.  No workspace. */
+gsa_status gsa_descriptor_set(const gsa_config* cfg, const void* k, const void* v, void* kd, void* vd,
+                              void* stream);
+
+/* Every token of q (full resolution, special and image) attends, in one
+ * softmax with the config scale, to the n_set rows of kd/vd.  Writes every
+ * row of o ([N][T_f][H][d]).  No workspace. */
+gsa_status gsa_descriptor_attn(const gsa_config* cfg, const void* q, const void* kd, const void* vd, void* o,
+                               void* stream);
+
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status status);
 

@@ -31,7 +31,7 @@ GSA_MAX_CTX_FRAMES = 16
 
 EXPORTS = ("gsa_workspace_size", "gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn",
            "gsa_special_attn", "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn",
-           "gsa_status_string")
+           "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_status_string")
 
 
 class GSAConfig(ctypes.Structure):
@@ -85,6 +85,9 @@ _sig = {
     "gsa_forward": [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_dense_attn": [_CFG, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_frame_attn": [_CFG, _P, _P, _P, _P, _P],
+    "gsa_descriptor_count": [_CFG, ctypes.POINTER(ctypes.c_int64)],
+    "gsa_descriptor_set": [_CFG, _P, _P, _P, _P, _P],
+    "gsa_descriptor_attn": [_CFG, _P, _P, _P, _P, _P],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).argtypes = _args
@@ -173,6 +176,22 @@ def gsa_dense_attn(cfg, q, k, v, o, ws=None, ws_bytes=None, stream=None):
 def gsa_frame_attn(cfg, q, k, v, o, stream=None):
     _check(_lib.gsa_frame_attn(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _stream(stream)),
            "gsa_frame_attn")
+
+
+def gsa_descriptor_count(cfg) -> int:
+    out = ctypes.c_int64(0)
+    _check(_lib.gsa_descriptor_count(ctypes.byref(cfg), ctypes.byref(out)), "gsa_descriptor_count")
+    return out.value
+
+
+def gsa_descriptor_set(cfg, k, v, kd, vd, stream=None):
+    _check(_lib.gsa_descriptor_set(ctypes.byref(cfg), _ptr(k), _ptr(v), _ptr(kd), _ptr(vd), _stream(stream)),
+           "gsa_descriptor_set")
+
+
+def gsa_descriptor_attn(cfg, q, kd, vd, o, stream=None):
+    _check(_lib.gsa_descriptor_attn(ctypes.byref(cfg), _ptr(q), _ptr(kd), _ptr(vd), _ptr(o), _stream(stream)),
+           "gsa_descriptor_attn")
 
 
 def call_status(fn: str, *args) -> int:

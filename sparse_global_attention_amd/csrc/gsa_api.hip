@@ -84,6 +84,28 @@ gsa_status check_cfg(const gsa_config* c, Call* out) {
 
 bool ptr_ok(const void* p) { return p != nullptr && ((uintptr_t)p & 15) == 0; }
 
+// FlashVGGT key/value set: r = the pool field, keyframes = the context frames.
+DescParams descriptor_plan(const Call& c) {
+  DescParams d;
+  memset(&d, 0, sizeof(d));
+  const Geometry& g = c.g;
+  d.g = g;
+  d.r = (int)g.pool;
+  d.n_desc = g.n_frames * (g.grid_h / g.pool) * (g.grid_w / g.pool);
+  d.full[d.n_full++] = 0;
+  for (int i = 0; i < c.n_ctx; ++i)
+    if (c.ctx[i] != 0) d.full[d.n_full++] = c.ctx[i];
+  for (int i = 0; i < d.n_full; ++i) d.full_sorted[i] = d.full[i];
+  for (int i = 1; i < d.n_full; ++i)
+    for (int j = i; j > 0 && d.full_sorted[j - 1] > d.full_sorted[j]; --j) {
+      const int t = d.full_sorted[j];
+      d.full_sorted[j] = d.full_sorted[j - 1];
+      d.full_sorted[j - 1] = t;
+    }
+  d.n_set = d.n_desc + d.n_full * g.tf + (g.n_frames - d.n_full) * g.n_special;
+  return d;
+}
+
 // ---- workspace layout ----------------------------------------------------------
 struct Plan {
   int n_split;  // special-attention key splits
@@ -508,6 +530,50 @@ gsa_status gsa_frame_attn(const gsa_config* cfg, const void* q, const void* k, c
   f.n_batch = c.g.n_frames;
   f.q_bstride = c.g.tf;
   f.k_bstride = c.g.tf;
+  f.o = o;
+  return hip_status(launch_flash(c.dtype, kFlashFinal, f, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_descriptor_count(const gsa_config* cfg, int64_t* n_set) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!n_set) return GSA_ERR_INVALID_ARG;
+  *n_set = descriptor_plan(c).n_set;
+  return GSA_OK;
+}
+
+gsa_status gsa_descriptor_set(const gsa_config* cfg, const void* k, const void* v, void* kd, void* vd,
+                              void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(k) || !ptr_ok(v) || !ptr_ok(kd) || !ptr_ok(vd)) return GSA_ERR_INVALID_ARG;
+  if (kd == k || kd == v || vd == k || vd == v || kd == vd) return GSA_ERR_INVALID_ARG;
+  DescParams d = descriptor_plan(c);
+  if (d.n_set > INT32_MAX - 64) return GSA_ERR_SHAPE;
+  d.src[0] = k;
+  d.src[1] = v;
+  d.dst[0] = kd;
+  d.dst[1] = vd;
+  return hip_status(launch_descriptor(c.dtype, d, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_descriptor_attn(const gsa_config* cfg, const void* q, const void* kd, const void* vd, void* o,
+                               void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(kd) || !ptr_ok(vd) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
+  if (o == q || o == kd || o == vd) return GSA_ERR_INVALID_ARG;
+  const int64_t n_set = descriptor_plan(c).n_set;
+  if (n_set > INT32_MAX - 64) return GSA_ERR_SHAPE;
+  // every token over the n_set rows of the set (same row stride as q)
+  FlashParams f = flash_base(c, q, kd, vd);
+  set_rows_identity(f, c.g.m_tokens);
+  f.n_splits = 1;
+  f.kbeg[0] = 0;
+  f.kend[0] = n_set;
   f.o = o;
   return hip_status(launch_flash(c.dtype, kFlashFinal, f, static_cast<hipStream_t>(stream)));
 }

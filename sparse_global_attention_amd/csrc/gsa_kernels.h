@@ -151,6 +151,20 @@ struct SelectParams {
 };
 hipError_t launch_select(int dtype, const SelectParams& p, hipStream_t stream);
 
+// ---- FlashVGGT descriptor set (bilinear descriptors + auxiliary tokens) -------
+struct DescParams {
+  const void* src[2];  // k, v in the token layout
+  void* dst[2];        // [n_set][H][d]
+  Geometry g;
+  int r;               // downsampling factor (divides h and w)
+  int64_t n_desc;      // N * (h/r) * (w/r) descriptor rows
+  int64_t n_set;       // n_desc + auxiliary rows
+  int n_full;          // frames whose every token is in the set: frame 0, then the keyframes
+  int full[kMaxExcl + 1];         // in set order
+  int full_sorted[kMaxExcl + 1];  // ascending
+};
+hipError_t launch_descriptor(int dtype, const DescParams& p, hipStream_t stream);
+
 // ---- standalone upsample + gate + blend ----------------------------------------
 struct CombineParams {
   const void* q;

@@ -103,6 +103,19 @@ class Case:
         gsa.gsa_frame_attn(self.cfg, self.dq, self.dk, self.dv, o)
         return o
 
+    def descriptor_set(self):
+        sh = self.sh
+        n = gsa.gsa_descriptor_count(self.cfg)
+        kd, vd = empty((n, sh.n_heads, sh.head_dim), sh.dtype), empty((n, sh.n_heads, sh.head_dim), sh.dtype)
+        gsa.gsa_descriptor_set(self.cfg, self.dk, self.dv, kd, vd)
+        return kd, vd
+
+    def descriptor_attn(self, kd, vd):
+        sh = self.sh
+        o = torch.zeros(sh.qkv_shape, dtype=self.dq.dtype, device=DEV)
+        gsa.gsa_descriptor_attn(self.cfg, self.dq, kd, vd, o)
+        return o
+
     def dense(self):
         sh = self.sh
         o = torch.zeros(sh.qkv_shape, dtype=self.dq.dtype, device=DEV)

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     for want in ("gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn", "gsa_special_attn",
                  "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn", "gsa_workspace_size",
-                 "gsa_status_string"):
+                 "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_status_string"):
         assert want in fns
 
 
@@ -110,6 +110,12 @@ def test_pointer_validation(lib):
     assert lib.call_status("gsa_frame_attn", c, A, A + 16, A + 32, A + 32, None) == 1  # o aliases v
     assert lib.call_status("gsa_frame_attn", c, A, None, A + 32, A + 48, None) == 1
     assert lib.call_status("gsa_frame_attn", c, A, A + 16, MISALIGNED, A + 48, None) == 1
+    assert lib.call_status("gsa_descriptor_set", c, A, A + 16, A + 16, A + 48, None) == 1  # kd aliases v
+    assert lib.call_status("gsa_descriptor_set", c, A, A + 16, A + 32, A + 32, None) == 1  # kd aliases vd
+    assert lib.call_status("gsa_descriptor_set", c, A, A + 16, None, A + 48, None) == 1
+    assert lib.call_status("gsa_descriptor_attn", c, A, A + 16, A + 32, A + 16, None) == 1  # o aliases kd
+    assert lib.call_status("gsa_descriptor_attn", c, MISALIGNED, A + 16, A + 32, A + 48, None) == 1
+    assert lib.call_status("gsa_descriptor_count", c, None) == 1
 
 
 def test_workspace_validation(lib):
@@ -134,3 +140,17 @@ def test_binding_raises_gsa_error(lib):
     with pytest.raises(lib.GSAError) as e:
         lib.gsa_workspace_size(cfg(lib, grid_h=7), lib.GSA_OP_FORWARD)
     assert e.value.status == lib.GSA_ERR_SHAPE
+
+
+def test_descriptor_count_matches_the_set_layout(lib):
+    """N (h/r)(w/r) descriptors + frame 0 and the keyframes whole + the other frames' specials."""
+    n = ctypes.c_int64(0)
+    c = lib.GSAConfig.make(10, 5, 36, 36, 16, 64, 4, 32)
+    assert lib.call_status("gsa_descriptor_count", ctypes.byref(c), ctypes.byref(n)) == 0
+    assert n.value == 10 * 81 + 1301 + 9 * 5
+    c = lib.GSAConfig.make(10, 5, 36, 36, 16, 64, 4, 32, ctx_frames=(0, 7, 3))
+    assert lib.call_status("gsa_descriptor_count", ctypes.byref(c), ctypes.byref(n)) == 0
+    assert n.value == 10 * 81 + 3 * 1301 + 7 * 5
+    c = lib.GSAConfig.make(4, 0, 8, 12, 2, 64, 2, 3)
+    assert lib.call_status("gsa_descriptor_count", ctypes.byref(c), ctypes.byref(n)) == 0
+    assert n.value == 4 * 4 * 6 + 96

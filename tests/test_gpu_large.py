@@ -8,7 +8,9 @@ times (gsa_forward), checked on sampled outputs the oracle computes one by one:
   GPU's index sets, then upsample + gate);
 * the forward's special rows: sampled special tokens x all heads;
 * determinism: a second forward is bitwise identical;
-* frame attention (the per-frame step beside GSA): sampled tokens x all heads.
+* frame attention (the per-frame step beside GSA): sampled tokens x all heads;
+* FlashVGGT descriptor attention (r = s, keyframes = the context frames): the
+  key/value set bit for bit, sampled tokens x all heads.
 
 Workloads: VGGT-style 128 frames with fixed context {0, 100}; the pi^3-style
 1000-frame sequence; the peaky clustered 1024-frame sequence.
@@ -51,6 +53,13 @@ def test_full_size_sampled_parity(name):
     o_frame = to_host(fr.view(sh.m_tokens, sh.n_heads, sh.head_dim).index_select(
         0, torch.from_numpy(fr_rows).cuda()))
     del fr
+    kd, vd = c.descriptor_set()
+    de = c.descriptor_attn(kd, vd)
+    de_rows = np.unique(np.concatenate([[0, sh.m_tokens - 1],
+                                        np.random.default_rng(sh.seed + 6).choice(sh.m_tokens, 30, replace=False)]))
+    o_desc = to_host(de.view(sh.m_tokens, sh.n_heads, sh.head_dim).index_select(0, torch.from_numpy(de_rows).cuda()))
+    g_set = [x.float().cpu().numpy() for x in (kd, vd)]
+    del de, kd, vd
     qc, kc, vc = c.pool()
     oc, idx, _ = c.compressed(qc, kc, vc, with_scores=False)
     again = c.forward()
@@ -97,4 +106,12 @@ def test_full_size_sampled_parity(name):
     log(f"[{name}] oracle: frame attention for {len(fr_rows)} rows ({time.time() - t0:.0f} s)")
     ofr = oracle.frame(sh, c.q, c.k, c.v, fr_rows)
     mx, mean, rel = assert_close(o_frame, ofr, sh.dtype, f"{name} frame attention (sampled)")
-    log(f"[{name}] frame: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}; done in {time.time() - t0:.0f} s")
+    log(f"[{name}] frame: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}")
+
+    log(f"[{name}] oracle: descriptor set and attention for {len(de_rows)} rows ({time.time() - t0:.0f} s)")
+    o_set = [oracle.descriptor_set(sh, x) for x in (c.k, c.v)]
+    for g, o, what in zip(g_set, o_set, "KV"):
+        assert np.array_equal(g.view(np.uint32), o.view(np.uint32)), f"{name}: descriptor {what} set differs"
+    ode = oracle.descriptor_attn(sh, c.q, o_set[0], o_set[1], de_rows)
+    mx, mean, rel = assert_close(o_desc, ode, sh.dtype, f"{name} descriptor attention (sampled)")
+    log(f"[{name}] descriptor: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}; done in {time.time() - t0:.0f} s")

@@ -2,8 +2,9 @@
 element, on seeded inputs small enough for the whole oracle: the tiny fp32
 workload, the 32-frame bf16 workload, and edge shapes (ragged tails, s in
 {1, 2, 4, 5, 6, 8}, P = 0, fixed context, k beyond the candidate count, k = 40/64/128),
-and frame attention (every token over its own frame) on the same workloads
-plus one frame of the pi^3-style size (T_f = 1301).
+frame attention (every token over its own frame) on the same workloads
+plus frames of the pi^3-style size (T_f = 1301), and FlashVGGT descriptor
+attention (r = the workload's s, keyframes = its context frames).
 """
 import numpy as np
 import pytest
@@ -304,3 +305,40 @@ def test_frame_attention(name):
                                          rng.choice(sh.m_tokens, 512, replace=False)]))
     ref = oracle.frame(sh, c.q, c.k, c.v, rows)
     assert_close(got[rows], ref, sh.dtype, f"{name} frame attention")
+
+
+# ---- FlashVGGT descriptor attention (Paper-Notes page "FlashVGGT: Efficient and
+# Scalable Visual Geometry Transformers with Compressed Descriptor Attention") ----
+
+DESC_SHAPES = dict(SHAPES)
+DESC_SHAPES["r4_keyframes"] = GSAShape("desc 12f-36x36-h2-r4+key{5,0,9}", 12, 5, 36, 36, 2, 64, 4, 3, BF16,
+                                       ctx_frames=(5, 0, 9), seed=37)
+
+
+@pytest.mark.parametrize("name", list(DESC_SHAPES))
+def test_descriptor_set_bit_exact(name):
+    sh = DESC_SHAPES[name]
+    c = Case(sh)
+    kd, vd = c.descriptor_set()
+    for got, x, what in ((kd, c.k, "K"), (vd, c.v, "V")):
+        ref = oracle.descriptor_set(sh, x)
+        g = got.float().cpu().numpy()
+        assert g.shape == ref.shape, (g.shape, ref.shape)
+        bad = np.flatnonzero(g.reshape(len(g), -1).view(np.uint32) != ref.reshape(len(ref), -1).view(np.uint32))
+        assert bad.size == 0, f"{name}: {bad.size} {what} set elements differ, first at {bad[:4]}"
+
+
+@pytest.mark.parametrize("name", list(DESC_SHAPES))
+def test_descriptor_attention(name):
+    sh = DESC_SHAPES[name]
+    c = Case(sh)
+    kd, vd = c.descriptor_set()
+    got = to_host(c.descriptor_attn(kd, vd)).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    n_set = kd.shape[0]
+    if sh.m_tokens * n_set <= 6_000_000:
+        rows = np.arange(sh.m_tokens)
+    else:
+        rows = np.unique(np.concatenate([[0, sh.m_tokens - 1],
+                                         np.random.default_rng(sh.seed).choice(sh.m_tokens, 1024, replace=False)]))
+    ref = oracle.descriptor_attn(sh, c.q, oracle.descriptor_set(sh, c.k), oracle.descriptor_set(sh, c.v), rows)
+    assert_close(got[rows], ref, sh.dtype, f"{name} descriptor attention")
