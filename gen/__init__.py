@@ -24,6 +24,7 @@ BF16, F32 = 0, 1
 STREAM_Q, STREAM_K, STREAM_V, STREAM_WG = 1, 2, 3, 4
 STREAM_KCEN, STREAM_VCEN, STREAM_KVMAP, STREAM_QMAP = 5, 6, 7, 8
 STREAM_SAMPLE_WIN, STREAM_SAMPLE_SPEC = 9, 10
+STREAM_DO = 11
 
 
 def build() -> None:
@@ -111,6 +112,12 @@ def make_inputs(sh: GSAShape, seed: int | None = None):
         k = normal(sh.qkv_shape, sh.dtype, seed, STREAM_K)
         v = normal(sh.qkv_shape, sh.dtype, seed, STREAM_V)
     return q, k, v, wg
+
+
+def make_output_grad(sh: GSAShape, seed: int | None = None) -> np.ndarray:
+    """Output gradient dO [N][T_f][H][d] ~ N(0, 1) in the workload's dtype."""
+    seed = sh.seed if seed is None else seed
+    return normal(sh.qkv_shape, sh.dtype, seed, STREAM_DO)
 
 
 def sample_windows(sh: GSAShape, n: int, seed: int | None = None) -> np.ndarray:

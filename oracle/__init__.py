@@ -5,7 +5,8 @@ step-by-step CPU implementation of the Global Sparse Attention forward pass
 (Paper-Notes page "Speed3R: Sparse Feed-forward 3D Reconstruction Models",
 sections "全局稀疏注意力（GSA）核心设计", "压缩分支", "选择分支", "门控聚合",
 "Speed3R-VGGT 适配"), the frame attention it alternates with (section
-"整体框架"), and the descriptor attention of the Paper-Notes page "FlashVGGT:
+"整体框架"), the gradients of the GSA layer (for end-to-end training), and the
+descriptor attention of the Paper-Notes page "FlashVGGT:
 Efficient and Scalable Visual Geometry Transformers with Compressed Descriptor
 Attention" (section "关键设计").  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 bench's CPU-baseline leg use it.  It shares no code with the HIP library and
@@ -57,6 +58,7 @@ def _load():
         lib.orc_pool.argtypes = [cfgp, P, P]
         lib.orc_special.argtypes = [cfgp, P, P, P, P, I64, P]
         lib.orc_frame.argtypes = [cfgp, P, P, P, P, I64, P]
+        lib.orc_backward.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, P, P, P, P, P]
         lib.orc_descriptor_count.argtypes = [cfgp]
         lib.orc_descriptor_count.restype = I64
         lib.orc_descriptor_set.argtypes = [cfgp, P, P]
@@ -67,7 +69,7 @@ def _load():
         lib.orc_gate_combine.argtypes = [cfgp, P, P, P, P, I64, P, P, P]
         lib.orc_window_token.argtypes = [cfgp, I64, ctypes.c_int]
         lib.orc_window_token.restype = I64
-        for f in ("orc_pool", "orc_special", "orc_frame", "orc_descriptor_set", "orc_descriptor_attn", "orc_compressed", "orc_guide_scores", "orc_select",
+        for f in ("orc_pool", "orc_special", "orc_frame", "orc_backward", "orc_descriptor_set", "orc_descriptor_attn", "orc_compressed", "orc_guide_scores", "orc_select",
                   "orc_gate_combine"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -106,6 +108,19 @@ def special(sh, q, k, v, rows: np.ndarray) -> np.ndarray:
     out = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
     _load().orc_special(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(rows), rows.size, _p(out))
     return out
+
+
+def backward(sh, q, k, v, wg, idx: np.ndarray, d_o):
+    """Gradients of sum(d_o * forward(q, k, v, wg)) with the top-k window sets fixed at
+    idx [M'][H][k] -> (dq, dk, dv [N][T_f][H][d] float64, dwg [H][d] float64).
+    Whole workload; small shapes only."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    shp = (sh.n_frames, sh.tokens_per_frame, sh.n_heads, sh.head_dim)
+    dq, dk, dv = (np.empty(shp, np.float64) for _ in range(3))
+    dwg = np.empty((sh.n_heads, sh.head_dim), np.float64)
+    _load().orc_backward(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(wg), _p(idx), idx.shape[-1],
+                         _p(np.ascontiguousarray(d_o)), _p(dq), _p(dk), _p(dv), _p(dwg))
+    return dq, dk, dv, dwg
 
 
 def frame(sh, q, k, v, rows: np.ndarray) -> np.ndarray:

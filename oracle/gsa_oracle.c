@@ -380,6 +380,217 @@ void orc_gate_combine(const orc_cfg* c, const void* q, const void* wg, const dou
 }
 
 /* ======================================================================== */
+/* Backward of the GSA layer.  Given the gradient dO [M][H][d] of a loss with
+ * respect to the layer output o, the gradients dq, dk, dv [M][H][d] and dwg
+ * [H][d] of that loss (equivalently of sum(dO * o)) with respect to the
+ * inputs, with the top-k window sets held fixed at idx [M'][H][kcols] (the
+ * selection is an index choice and is not differentiated; entries < 0 are
+ * ignored).  The pages train GSA end to end by distillation from the dense
+ * model (Paper-Notes page, sections "研究背景与动机", "训练策略" and
+ * "亮点与创新"), which needs exactly these gradients of the forward above.
+ *
+ * Softmax attention of one query q over keys k_j, values v_j, weights
+ * P_j = softmax_j(scale q.k_j), output O = sum_j P_j v_j:
+ *   dP_j = dO . v_j,   D = sum_j P_j dP_j (= dO . O),   dS_j = P_j (dP_j - D),
+ *   dq += scale sum_j dS_j k_j,   dk_j += scale dS_j q,   dv_j += P_j dO.
+ * Gate g = sigmoid(z), z = W_g[h] . q, O_img = g O_comp + (1 - g) O_sel:
+ *   dO_comp += g dO,  dO_sel = (1 - g) dO,  dz = (dO . (O_comp - O_sel)) g (1 - g),
+ *   dq += dz W_g[h],  dW_g[h] += dz q.
+ * Nearest upsampling sums dO_comp over the s^2 tokens of each window; the
+ * compressed attention is the softmax attention of pooled rows over all M'
+ * pooled rows; the pooled tensors are rounded as in the forward and the
+ * rounding is passed through as the identity, so a pooled row's gradient
+ * reaches each of its s^2 token rows times 1/s^2.
+ * Every quantity is a double; this is the plain definition, for workloads
+ * small enough to run whole. */
+
+static double dot_d(const double* a, const double* b, int d) {
+  double s = 0.0;
+  for (int e = 0; e < d; ++e) s += a[e] * b[e];
+  return s;
+}
+
+/* Softmax weights of query row qrow over the listed rows of K (a double
+ * [rows][H][d] array, head h) into P[0..n). */
+static void softmax_weights(int d, int H, int h, double sc, const double* qrow, const double* K,
+                            const int64_t* rows, int64_t n, double* P) {
+  double mx = -INFINITY, den = 0.0;
+  for (int64_t t = 0; t < n; ++t) {
+    P[t] = sc * dot_d(qrow, K + (rows[t] * H + h) * d, d);
+    if (P[t] > mx) mx = P[t];
+  }
+  for (int64_t t = 0; t < n; ++t) {
+    P[t] = exp(P[t] - mx);
+    den += P[t];
+  }
+  for (int64_t t = 0; t < n; ++t) P[t] /= den;
+}
+
+/* out[0..d) = sum_t P_t V[rows[t]] */
+static void weighted_values(int d, int H, int h, const double* V, const int64_t* rows, int64_t n,
+                            const double* P, double* out) {
+  for (int e = 0; e < d; ++e) out[e] = 0.0;
+  for (int64_t t = 0; t < n; ++t)
+    for (int e = 0; e < d; ++e) out[e] += P[t] * V[(rows[t] * H + h) * d + e];
+}
+
+/* Attention backward of one query (weights recomputed): adds to dq_row[d]
+ * and to the rows of dK, dV (double [rows][H][d]). */
+static void attention_backward(int d, int H, int h, double sc, const double* qrow, const double* K,
+                               const double* V, const int64_t* rows, int64_t n, const double* dorow,
+                               double* P, double* dP, double* dq_row, double* dK, double* dV) {
+  softmax_weights(d, H, h, sc, qrow, K, rows, n, P);
+  double D = 0.0;
+  for (int64_t t = 0; t < n; ++t) {
+    dP[t] = dot_d(dorow, V + (rows[t] * H + h) * d, d);
+    D += P[t] * dP[t];
+  }
+  for (int64_t t = 0; t < n; ++t) {
+    const double ds = P[t] * (dP[t] - D);
+    const double* kr = K + (rows[t] * H + h) * d;
+    double* dkr = dK + (rows[t] * H + h) * d;
+    double* dvr = dV + (rows[t] * H + h) * d;
+    for (int e = 0; e < d; ++e) {
+      dq_row[e] += sc * ds * kr[e];
+      dkr[e] += sc * ds * qrow[e];
+      dvr[e] += P[t] * dorow[e];
+    }
+  }
+}
+
+void orc_backward(const orc_cfg* c, const void* q, const void* k, const void* v, const void* wg,
+                  const int32_t* idx, int kcols, const void* d_o, double* dq, double* dk, double* dv,
+                  double* dwg) {
+  const int H = c->n_heads, d = c->head_dim, s2 = c->pool * c->pool;
+  const int64_t M = n_tokens(c), tf = tokens_per_frame(c), nw = n_windows(c);
+  const double sc = scale_of(c);
+  const size_t nel = (size_t)M * H * d, nwel = (size_t)nw * H * d;
+  double* Q = (double*)malloc(sizeof(double) * nel);
+  double* K = (double*)malloc(sizeof(double) * nel);
+  double* V = (double*)malloc(sizeof(double) * nel);
+  double* G = (double*)malloc(sizeof(double) * nel);
+  for (size_t i = 0; i < nel; ++i) {
+    Q[i] = elem(q, c->dtype, (int64_t)i);
+    K[i] = elem(k, c->dtype, (int64_t)i);
+    V[i] = elem(v, c->dtype, (int64_t)i);
+    G[i] = elem(d_o, c->dtype, (int64_t)i);
+    dq[i] = dk[i] = dv[i] = 0.0;
+  }
+  /* pooled rows, rounded as in the forward */
+  float* pooled = (float*)malloc(sizeof(float) * nwel);
+  double* Qc = (double*)malloc(sizeof(double) * nwel);
+  double* Kc = (double*)malloc(sizeof(double) * nwel);
+  double* Vc = (double*)malloc(sizeof(double) * nwel);
+  double* dQc = (double*)calloc(nwel, sizeof(double));
+  double* dKc = (double*)calloc(nwel, sizeof(double));
+  double* dVc = (double*)calloc(nwel, sizeof(double));
+  double* dOc = (double*)calloc(nwel, sizeof(double));
+  double* Oc = (double*)malloc(sizeof(double) * nwel);
+  const void* src[3] = {q, k, v};
+  double* dstp[3] = {Qc, Kc, Vc};
+  for (int x = 0; x < 3; ++x) {
+    orc_pool(c, src[x], pooled);
+    for (size_t i = 0; i < nwel; ++i) dstp[x][i] = pooled[i];
+  }
+  free(pooled);
+
+  const int64_t cap = (M > nw ? M : nw) + (int64_t)kcols * s2;
+#pragma omp parallel for schedule(static, 1)
+  for (int h = 0; h < H; ++h) {
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * cap);
+    double* P = (double*)malloc(sizeof(double) * cap);
+    double* dP = (double*)malloc(sizeof(double) * cap);
+    double osel[512], dosel[512], dorow[512];
+    for (int e = 0; e < d; ++e) dwg[h * d + e] = 0.0;
+
+    /* special rows: attention over all M tokens */
+    for (int64_t t = 0; t < M; ++t) rows[t] = t;
+    for (int64_t f = 0; f < c->n_frames; ++f)
+      for (int p = 0; p < c->n_special; ++p) {
+        const int64_t t = f * tf + p;
+        attention_backward(d, H, h, sc, Q + (t * H + h) * d, K, V, rows, M, G + (t * H + h) * d, P, dP,
+                           dq + (t * H + h) * d, dk, dv);
+      }
+
+    /* compressed attention output of every window */
+    for (int64_t j = 0; j < nw; ++j) rows[j] = j;
+    for (int64_t i = 0; i < nw; ++i) {
+      softmax_weights(d, H, h, sc, Qc + (i * H + h) * d, Kc, rows, nw, P);
+      weighted_values(d, H, h, Vc, rows, nw, P, Oc + (i * H + h) * d);
+    }
+
+    /* image rows: gate, selection attention (+ context), compressed-branch gradient */
+    for (int64_t i = 0; i < nw; ++i) {
+      int64_t nt = 0;
+      for (int t = 0; t < kcols; ++t) {
+        const int32_t j = idx[(i * H + h) * kcols + t];
+        if (j < 0) continue;
+        for (int kk = 0; kk < s2; ++kk) rows[nt++] = window_token(c, j, kk);
+      }
+      for (int cf = 0; cf < c->n_ctx; ++cf)
+        for (int64_t p = 0; p < tf; ++p) rows[nt++] = (int64_t)c->ctx_frames[cf] * tf + p;
+      const double* oc = Oc + (i * H + h) * d;
+      for (int qq = 0; qq < s2; ++qq) {
+        const int64_t t = window_token(c, i, qq);
+        const double* qrow = Q + (t * H + h) * d;
+        const double* g_o = G + (t * H + h) * d;
+        softmax_weights(d, H, h, sc, qrow, K, rows, nt, P);
+        weighted_values(d, H, h, V, rows, nt, P, osel);
+        double z = 0.0;
+        for (int e = 0; e < d; ++e) z += elem(wg, c->dtype, (int64_t)h * d + e) * qrow[e];
+        const double g = 1.0 / (1.0 + exp(-z));
+        double dg = 0.0;
+        for (int e = 0; e < d; ++e) {
+          dg += g_o[e] * (oc[e] - osel[e]);
+          dOc[(i * H + h) * d + e] += g * g_o[e];
+          dosel[e] = (1.0 - g) * g_o[e];
+        }
+        const double dz = dg * g * (1.0 - g);
+        for (int e = 0; e < d; ++e) {
+          dq[(t * H + h) * d + e] += dz * elem(wg, c->dtype, (int64_t)h * d + e);
+          dwg[h * d + e] += dz * qrow[e];
+        }
+        attention_backward(d, H, h, sc, qrow, K, V, rows, nt, dosel, P, dP, dq + (t * H + h) * d, dk, dv);
+      }
+    }
+
+    /* compressed attention backward over the pooled rows */
+    for (int64_t j = 0; j < nw; ++j) rows[j] = j;
+    for (int64_t i = 0; i < nw; ++i) {
+      for (int e = 0; e < d; ++e) dorow[e] = dOc[(i * H + h) * d + e];
+      attention_backward(d, H, h, sc, Qc + (i * H + h) * d, Kc, Vc, rows, nw, dorow, P, dP,
+                         dQc + (i * H + h) * d, dKc, dVc);
+    }
+
+    /* pooling backward: each token of window j gets its pooled row's gradient / s^2 */
+    for (int64_t j = 0; j < nw; ++j)
+      for (int kk = 0; kk < s2; ++kk) {
+        const int64_t t = window_token(c, j, kk);
+        for (int e = 0; e < d; ++e) {
+          dq[(t * H + h) * d + e] += dQc[(j * H + h) * d + e] / s2;
+          dk[(t * H + h) * d + e] += dKc[(j * H + h) * d + e] / s2;
+          dv[(t * H + h) * d + e] += dVc[(j * H + h) * d + e] / s2;
+        }
+      }
+    free(rows);
+    free(P);
+    free(dP);
+  }
+  free(Q);
+  free(K);
+  free(V);
+  free(G);
+  free(Qc);
+  free(Kc);
+  free(Vc);
+  free(dQc);
+  free(dKc);
+  free(dVc);
+  free(dOc);
+  free(Oc);
+}
+
+/* ======================================================================== */
 /* Frame attention: the local step that alternates with GSA in the
  * aggregation transformer (Paper-Notes page, section "整体框架": blocks
  * alternate intra-frame attention and global sparse attention).  Each token

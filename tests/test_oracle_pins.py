@@ -508,3 +508,138 @@ def test_descriptor_attention_equals_attention_over_the_set(keyframes):
     for h in range(sh.n_heads):
         ref = sdpa(Q[:, h], K[:, h], V[:, h], sh.head_dim ** -0.5)
         np.testing.assert_allclose(got[:, h], ref, rtol=0, atol=2e-6)
+
+
+# ---------------------------------------------------------------------------
+# P12 -- the backward: gradients of sum(dO * O) with the top-k sets fixed
+# (trained end to end: Paper-Notes page, sections "研究背景与动机", "训练策略").
+# Pins: torch autograd (float64) through a forward rebuilt from masks and
+# reshapes; central differences of the oracle's own forward steps on dyadic
+# inputs (every pooled mean exact); the identities sum_t dV = sum_t dO and
+# sum_t dK = 0 that every softmax attention obeys.
+
+def _fixed_topk(sh, seed):
+    """A valid top-k set per (window, head): distinct candidate windows, -1 padded."""
+    rng = np.random.default_rng(seed)
+    wpf = (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool)
+    cand = np.array([j for j in range(sh.n_windows) if j // wpf not in sh.ctx_frames])
+    kk = min(sh.topk, cand.size)
+    idx = np.full((sh.n_windows, sh.n_heads, sh.topk), -1, np.int32)
+    for i in range(sh.n_windows):
+        for h in range(sh.n_heads):
+            idx[i, h, :kk] = rng.choice(cand, kk, replace=False)
+    return idx
+
+
+def _torch_forward(sh, Q, K, V, W, idx):
+    """GSA forward in float64 torch ops: pooling by reshape-mean, attention by SDPA
+    under masks built from the window sets."""
+    H, d, sc = sh.n_heads, sh.head_dim, sh.head_dim ** -0.5
+    M, tf = sh.m_tokens, sh.tokens_per_frame
+    wt = torch.from_numpy(window_token_ids(sh))            # [M'][s^2] token rows
+    Qc, Kc, Vc = (X[wt].mean(1) for X in (Q, K, V))        # [M'][H][d]
+    out = torch.zeros(M, H, d, dtype=torch.float64)
+    spec = torch.from_numpy(special_token_ids(sh))
+    img = wt.reshape(-1)                                    # image tokens, window-major
+    win_of = torch.arange(sh.n_windows).repeat_interleave(sh.pool ** 2)
+    frame_of_tok = torch.arange(M) // tf
+    sdp = torch.nn.functional.scaled_dot_product_attention
+    rows = []
+    for h in range(H):
+        o_h = torch.zeros(M, d, dtype=torch.float64)
+        if spec.numel():
+            o_h = o_h.index_put((spec,), sdp(Q[spec, h][None], K[:, h][None], V[:, h][None], scale=sc)[0])
+        oc = sdp(Qc[:, h][None], Kc[:, h][None], Vc[:, h][None], scale=sc)[0]
+        allowed = np.zeros((sh.n_windows, M), bool)
+        for i in range(sh.n_windows):
+            for j in idx[i, h]:
+                if j >= 0:
+                    allowed[i, window_token_ids(sh)[j]] = True
+            for f in sh.ctx_frames:
+                allowed[i, f * tf:(f + 1) * tf] = True
+        mask = torch.from_numpy(np.where(allowed, 0.0, -np.inf))[win_of]
+        osel = sdp(Q[img, h][None], K[:, h][None], V[:, h][None], attn_mask=mask[None], scale=sc)[0]
+        g = torch.sigmoid(Q[img, h] @ W[h])[:, None]
+        o_h = o_h.index_put((img,), g * oc[win_of] + (1 - g) * osel)
+        rows.append(o_h)
+    return torch.stack(rows, 1)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(n_special=0, pool=4, topk=2), dict(ctx_frames=(1,), topk=2)])
+def test_backward_equals_torch_autograd(kw):
+    sh = shape(**kw)
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    idx = _fixed_topk(sh, 5)
+    dq, dk, dv, dwg = oracle.backward(sh, q, k, v, wg, idx, d_o)
+    Q, K, V = (torch.from_numpy(flat(x, sh)).requires_grad_() for x in (q, k, v))
+    W = torch.from_numpy(f64(wg, sh).reshape(sh.n_heads, sh.head_dim)).requires_grad_()
+    out = _torch_forward(sh, Q, K, V, W, idx)
+    (out * torch.from_numpy(flat(d_o, sh))).sum().backward()
+    # the oracle's pooled rows are rounded to float, the torch means are not
+    for got, ref in ((dq, Q.grad), (dk, K.grad), (dv, V.grad), (dwg, W.grad)):
+        ref = ref.numpy().reshape(got.shape)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6 * max(1.0, np.abs(ref).max()))
+
+
+def _dyadic_inputs(sh, seed):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.integers(-16, 17, size=sh.qkv_shape).astype(np.float32) / 16 for _ in range(3))
+    wg = rng.integers(-4, 5, size=(sh.n_heads, sh.head_dim)).astype(np.float32) / 16
+    d_o = rng.integers(-8, 9, size=sh.qkv_shape).astype(np.float32) / 8
+    return q, k, v, wg, d_o
+
+
+def _loss(sh, q, k, v, wg, idx, d_o):
+    """sum(dO * O) from the oracle's forward steps with the top-k sets fixed."""
+    wins = np.arange(sh.n_windows)
+    qc, kc, vc = oracle.pool(sh, q), oracle.pool(sh, k), oracle.pool(sh, v)
+    oc = oracle.compressed(sh, qc, kc, vc, wins)[0]
+    osel = oracle.select(sh, q, k, v, wins, idx)
+    oimg = oracle.gate_combine(sh, q, wg, wins, oc, osel)
+    G = d_o.astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    L = float((G[window_token_ids(sh).reshape(-1)] * oimg.reshape(-1, sh.n_heads, sh.head_dim)).sum())
+    if sh.m_spec:
+        L += float((G[special_token_ids(sh)] * oracle.special(sh, q, k, v, np.arange(sh.m_spec))).sum())
+    return L
+
+
+def test_backward_matches_central_differences():
+    sh = shape(n_frames=2, n_special=1, grid_h=4, grid_w=4, pool=2, topk=2, head_dim=8)
+    q, k, v, wg, d_o = _dyadic_inputs(sh, 3)
+    idx = _fixed_topk(sh, 6)
+    grads = oracle.backward(sh, q, k, v, wg, idx, d_o)
+    eps = 2.0 ** -10
+    rng = np.random.default_rng(7)
+    checked = 0
+    for which, arr in enumerate((q, k, v, wg)):
+        for _ in range(6):
+            pos = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            if which < 3 and _ == 0:
+                pos = (0, 0) + pos[2:]  # a special token
+            plus, minus = arr.copy(), arr.copy()
+            plus[pos] += eps
+            minus[pos] -= eps
+            args = [q, k, v, wg]
+            args[which] = plus
+            lp = _loss(sh, *args, idx, d_o)
+            args[which] = minus
+            lm = _loss(sh, *args, idx, d_o)
+            fd = (lp - lm) / (2 * eps)
+            g = grads[which][pos]
+            assert abs(fd - g) <= 1e-5 * max(1.0, abs(g)), (which, pos, fd, g)
+            checked += 1
+    assert checked == 24
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(ctx_frames=(0,), topk=2, dtype=BF16)])
+def test_backward_sum_identities(kw):
+    """sum_t dV_t = sum_t dO_t and sum_t dK_t = 0 per head and channel: softmax weights
+    sum to one and the score gradients of each query sum to zero."""
+    sh = shape(**kw)
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    dq, dk, dv, dwg = oracle.backward(sh, q, k, v, wg, _fixed_topk(sh, 8), d_o)
+    G = flat(d_o, sh)
+    np.testing.assert_allclose(dv.reshape(G.shape).sum(0), G.sum(0), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dk.reshape(G.shape).sum(0), 0.0, rtol=0, atol=1e-10)
