@@ -249,6 +249,21 @@ def main():
         "attn_tflops": round(datt_flop / (t_datt * 1e-3) / 1e12, 2),
         "attn_frac_mfma_peak": round(datt_flop / (t_datt * 1e-3) / 1e12 / peak, 4)}
     del kd, vd
+    # Backward of the layer (gradients of q, k, v and W_g for a seeded dO, the
+    # top-k sets of the compressed step above held fixed).  Algorithmic work:
+    # 2.5x the forward attention FLOPs (recomputed scores, dP, dV, dQ, dK).
+    d_o = to_dev(gen.make_output_grad(sh))
+    gq, gk, gv = (torch.empty(sh.qkv_shape, dtype=torch.float32, device=dev) for _ in range(3))
+    gw = torch.empty((H, d), dtype=torch.float32, device=dev)
+    ws_bwd = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_BACKWARD)), dtype=torch.uint8, device=dev)
+    t_bwd = timed(lambda: gsa.gsa_backward(cfg, dq, dk, dv, dwg, idx, d_o, gq, gk, gv, gw, ws_bwd, stream=stream),
+                  max(2, reps // 2))
+    bwd_flop = 2.5 * gsa_flops
+    detail["backward"] = {"ms": round(t_bwd, 4), "flop": bwd_flop,
+                          "tflops": round(bwd_flop / (t_bwd * 1e-3) / 1e12, 2),
+                          "frac_mfma_peak": round(bwd_flop / (t_bwd * 1e-3) / 1e12 / peak, 4),
+                          "workspace_gb": round(ws_bwd.numel() / 1e9, 2)}
+    del d_o, gq, gk, gv, gw, ws_bwd
     del ws_spec, ws_sel, ws_cmp, o2, osel
 
     # ---- dense comparator at the same shape --------------------------------------

@@ -67,7 +67,8 @@ typedef enum {
   GSA_OP_SPECIAL = 1, /* gsa_special_attn */
   GSA_OP_SELECT = 2,  /* gsa_select_attn */
   GSA_OP_DENSE = 3,   /* gsa_dense_attn */
-  GSA_OP_COMPRESSED = 4 /* gsa_compressed_attn_topk */
+  GSA_OP_COMPRESSED = 4, /* gsa_compressed_attn_topk */
+  GSA_OP_BACKWARD = 5    /* gsa_backward */
 } gsa_op;
 
 #define GSA_MAX_CTX_FRAMES 16
@@ -156,6 +157,27 @@ gsa_status gsa_gate_combine(const gsa_config* cfg, const void* q, const void* wg
  */
 gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, const void* v,
                        const void* wg, void* o, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the GSA layer (GSA is trained end to end by distillation from
+ * the dense model: sections "研究背景与动机", "训练策略", "亮点与创新").
+ * Given the gradient d_o ([N][T_f][H][d], dtype) of a loss with respect to
+ * the output of gsa_forward(q, k, v, wg), writes the gradients of that loss
+ * with respect to the inputs: dq, dk, dv float [N][T_f][H][d] (every row) and
+ * dwg float [H][d].  The top-k window sets are held fixed at topk_idx
+ * ([M'][H][k], as written by gsa_compressed_attn_topk for these inputs; the
+ * selection is an index choice and is not differentiated; entries < 0 or
+ * >= M' are skipped).  The pooled Q/K/V are used rounded to the dtype, as in
+ * the forward, and the rounding is passed through as the identity (each
+ * token of a window receives 1/s^2 of its pooled row's gradient).  The
+ * forward quantities (pooled rows, the three attention outputs and their
+ * softmax denominators, the gate) are recomputed inside the call.
+ * Outputs must not alias inputs or each other.  GSA_ERR_SHAPE if M' H k >=
+ * 2^31.  Workspace: GSA_OP_BACKWARD bytes.
+ */
+gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                        const int32_t* topk_idx, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense global attention of all M tokens over all M tokens at the same shape

@@ -26,12 +26,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 GSA_OK, GSA_ERR_INVALID_ARG, GSA_ERR_SHAPE, GSA_ERR_UNSUPPORTED, GSA_ERR_WORKSPACE, GSA_ERR_HIP = range(6)
 GSA_BF16, GSA_F32 = 0, 1
-GSA_OP_FORWARD, GSA_OP_SPECIAL, GSA_OP_SELECT, GSA_OP_DENSE, GSA_OP_COMPRESSED = range(5)
+GSA_OP_FORWARD, GSA_OP_SPECIAL, GSA_OP_SELECT, GSA_OP_DENSE, GSA_OP_COMPRESSED, GSA_OP_BACKWARD = range(6)
 GSA_MAX_CTX_FRAMES = 16
 
 EXPORTS = ("gsa_workspace_size", "gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn",
            "gsa_special_attn", "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn",
-           "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_status_string")
+           "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_backward",
+           "gsa_status_string")
 
 
 class GSAConfig(ctypes.Structure):
@@ -88,6 +89,7 @@ _sig = {
     "gsa_descriptor_count": [_CFG, ctypes.POINTER(ctypes.c_int64)],
     "gsa_descriptor_set": [_CFG, _P, _P, _P, _P, _P],
     "gsa_descriptor_attn": [_CFG, _P, _P, _P, _P, _P],
+    "gsa_backward": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).argtypes = _args
@@ -192,6 +194,13 @@ def gsa_descriptor_set(cfg, k, v, kd, vd, stream=None):
 def gsa_descriptor_attn(cfg, q, kd, vd, o, stream=None):
     _check(_lib.gsa_descriptor_attn(ctypes.byref(cfg), _ptr(q), _ptr(kd), _ptr(vd), _ptr(o), _stream(stream)),
            "gsa_descriptor_attn")
+
+
+def gsa_backward(cfg, q, k, v, wg, topk_idx, d_o, dq, dk, dv, dwg, ws, ws_bytes=None, stream=None):
+    wsb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(_lib.gsa_backward(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(topk_idx), _ptr(d_o),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwg), _ptr(ws), wsb, _stream(stream)),
+           "gsa_backward")
 
 
 def call_status(fn: str, *args) -> int:

@@ -112,7 +112,24 @@ struct Plan {
   int64_t qc, kc, vc, oc, topk, kblk, vblk, spec_o, spec_lse, ctx_o, ctx_lse, total;
   int n_groups, group_tiles;  // compressed step: key-tile groups of the score bounds
   int64_t gbound;
+  // backward
+  int ctx_qsplits;  // query splits of the context frames' key-side pass
+  int64_t qblk, qT, kT, vrow, lse_c, spec_o32, spec_l2, spec_dd, osel, l2sel, doblk, doT, l2blk, dblk,
+      dosel_img, dsel_img, doc, dc, dwg_part, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list,
+      ctx_dq, ctx_dkdv;
 };
+
+// Query splits of the key-side backward pass over one context frame: enough
+// workgroups to fill the resident slots, at most one per query tile.
+int ctx_query_splits(const Call& c) {
+  const Geometry& g = c.g;
+  const int64_t per = ((g.tf + 127) / 128) * g.n_heads;
+  int64_t z = (kWorkgroupSlots * 2 + per - 1) / per;
+  const int64_t n_qt = (g.m_img + 31) / 32;
+  if (z > n_qt) z = n_qt;
+  if (z < 1) z = 1;
+  return (int)z;
+}
 
 // Groups of key tiles for the score bounds: at most refine_groups_for_k(k)
 // groups (128 for k <= 48, 512 beyond; a lane of the refine kernel holds half
@@ -187,6 +204,56 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.spec_o = take(spec_o);
     p.spec_lse = take(spec_lse);
   }
+  if (op == GSA_OP_BACKWARD) {
+    const int64_t wf = g.n_windows * g.n_heads * kHeadDim * 4;  // float [M'][H][d]
+    const int64_t wl = g.n_windows * g.n_heads * 4;             // float [M'][H]
+    const int64_t bl = g.n_windows * g.n_heads * g.sb * 4;      // float [M'][H][sb]
+    const int64_t imgf = g.m_img * g.n_heads * kHeadDim * 4;
+    const int64_t segs = g.n_windows * g.n_heads;
+    const int64_t entries = segs * c.topk;
+    p.ctx_qsplits = ctx_query_splits(c);
+    p.qc = take(pooled);
+    p.kc = take(pooled);
+    p.vc = take(pooled);
+    p.qblk = take(blk);
+    p.qT = take(blk);
+    p.kblk = take(blk);
+    p.kT = take(blk);
+    p.vrow = take(blk);
+    p.vblk = take(blk);
+    p.oc = take(wf);
+    p.lse_c = take(wl);
+    p.spec_o = take(spec_o);
+    p.spec_lse = take(spec_lse);
+    p.spec_o32 = take(g.m_spec * g.n_heads * kHeadDim * 4);
+    p.spec_l2 = take(g.m_spec * g.n_heads * 4);
+    p.spec_dd = take(g.m_spec * g.n_heads * 4);
+    p.ctx_o = take(ctx_o);
+    p.ctx_lse = take(ctx_lse);
+    p.osel = take(imgf);
+    p.l2sel = take(g.m_img * g.n_heads * 4);
+    p.doblk = take(blk);
+    p.doT = take(blk);
+    p.l2blk = take(bl);
+    p.dblk = take(bl);
+    if (c.n_ctx) {
+      p.dosel_img = take(g.m_img * g.n_heads * kHeadDim * c.esz);
+      p.dsel_img = take(g.m_img * g.n_heads * 4);
+      p.ctx_dq = take(c.n_ctx > 1 ? c.n_ctx * imgf : 0);
+      p.ctx_dkdv = take(p.ctx_qsplits > 1 ? 2 * (int64_t)p.ctx_qsplits * g.tf * g.n_heads * kHeadDim * 4 : 0);
+    }
+    p.doc = take(g.n_windows * g.n_heads * kHeadDim * c.esz);
+    p.dc = take(wl);
+    p.dwg_part = take(wf);
+    p.dqc = take(wf);
+    p.dkc = take(wf);
+    p.dvc = take(wf);
+    p.inv_off = take((segs + 1) * 4);
+    p.inv_cursor = take(segs * 4);
+    p.inv_bsum = take(((segs + 1 + 1023) / 1024) * 4);
+    p.inv_raw = take(entries * 4);
+    p.inv_list = take(entries * 4);
+  }
   p.total = off;
   return p;
 }
@@ -245,6 +312,7 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
   hipError_t e = launch_flash(c.dtype, kFlashPartial, f, st);
   if (e != hipSuccess) return e;
   MergeParams m;
+  memset(&m, 0, sizeof(m));
   m.part_o = f.part_o;
   m.part_lse = f.part_lse;
   m.n_splits = ns;
@@ -365,7 +433,7 @@ gsa_status gsa_workspace_size(const gsa_config* cfg, gsa_op op, size_t* bytes) {
   gsa_status s = check_cfg(cfg, &c);
   if (s != GSA_OK) return s;
   if (!bytes) return GSA_ERR_INVALID_ARG;
-  if (op < GSA_OP_FORWARD || op > GSA_OP_COMPRESSED) return GSA_ERR_INVALID_ARG;
+  if (op < GSA_OP_FORWARD || op > GSA_OP_BACKWARD) return GSA_ERR_INVALID_ARG;
   *bytes = (size_t)make_plan(c, op).total;
   return GSA_OK;
 }
@@ -411,8 +479,8 @@ gsa_status gsa_select_attn(const gsa_config* cfg, const void* q, const void* k, 
   PoolParams pp = pool_base(c);
   pp.src[1] = k;
   pp.src[2] = v;
-  pp.kblk = at(ws, pl.kblk);
-  pp.vblk = at(ws, pl.vblk);
+  pp.rows[1] = at(ws, pl.kblk);
+  pp.trans[2] = at(ws, pl.vblk);
   pp.first_tensor = 1;
   hipError_t e = launch_pool(c.dtype, pp, 2, st);
   if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
@@ -473,8 +541,8 @@ gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, cons
   pp.dst[0] = at(ws, pl.qc);
   pp.dst[1] = at(ws, pl.kc);
   pp.dst[2] = at(ws, pl.vc);
-  pp.kblk = at(ws, pl.kblk);
-  pp.vblk = at(ws, pl.vblk);
+  pp.rows[1] = at(ws, pl.kblk);
+  pp.trans[2] = at(ws, pl.vblk);
   pp.first_tensor = 0;
   hipError_t e = launch_pool(c.dtype, pp, 3, st);
   // 2. special tokens over all tokens
@@ -576,6 +644,341 @@ gsa_status gsa_descriptor_attn(const gsa_config* cfg, const void* q, const void*
   f.kend[0] = n_set;
   f.o = o;
   return hip_status(launch_flash(c.dtype, kFlashFinal, f, static_cast<hipStream_t>(stream)));
+}
+
+gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                        const int32_t* topk_idx, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
+                        void* ws, size_t ws_bytes, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  const void* in[6] = {q, k, v, wg, topk_idx, d_o};
+  const void* out[4] = {dq, dk, dv, dwg};
+  for (const void* x : in)
+    if (!ptr_ok(x)) return GSA_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i) {
+    if (!ptr_ok(out[i])) return GSA_ERR_INVALID_ARG;
+    for (const void* x : in)
+      if (x == out[i]) return GSA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (out[j] == out[i]) return GSA_ERR_INVALID_ARG;
+  }
+  const Geometry& g = c.g;
+  if (g.n_windows * g.n_heads * (int64_t)c.topk > INT32_MAX) return GSA_ERR_SHAPE;
+  Plan pl = make_plan(c, GSA_OP_BACKWARD);
+  if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t H = g.n_heads;
+  const float kFloatL2 = kLog2e;  // natural log-sum-exp -> log2 denominator
+  hipError_t e = hipSuccess;
+  auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; return e == hipSuccess; };
+
+  // 1. pooled Q/K/V and the window-blocked copies the selection passes gather
+  PoolParams pp = pool_base(c);
+  pp.src[0] = q;
+  pp.src[1] = k;
+  pp.src[2] = v;
+  pp.dst[0] = at(ws, pl.qc);
+  pp.dst[1] = at(ws, pl.kc);
+  pp.dst[2] = at(ws, pl.vc);
+  pp.rows[0] = at(ws, pl.qblk);
+  pp.trans[0] = at(ws, pl.qT);
+  pp.rows[1] = at(ws, pl.kblk);
+  pp.trans[1] = at(ws, pl.kT);
+  pp.rows[2] = at(ws, pl.vrow);
+  pp.trans[2] = at(ws, pl.vblk);
+  ok(launch_pool(c.dtype, pp, 3, st));
+
+  // 2. forward quantities: compressed output + log-sum-exp (one split)
+  float* oc = reinterpret_cast<float*>(at(ws, pl.oc));
+  float* lse_c = reinterpret_cast<float*>(at(ws, pl.lse_c));
+  if (g.n_windows) {
+    FlashParams f = flash_base(c, at(ws, pl.qc), at(ws, pl.kc), at(ws, pl.vc));
+    set_rows_identity(f, g.n_windows);
+    f.n_splits = 1;
+    f.kbeg[0] = 0;
+    f.kend[0] = g.n_windows;
+    f.part_o = oc;
+    f.part_lse = lse_c;
+    ok(launch_flash(c.dtype, kFlashPartial, f, st));
+  }
+  //    special rows: merged output in float, L2 and D = dO . O
+  float* spec_o32 = reinterpret_cast<float*>(at(ws, pl.spec_o32));
+  float* spec_l2 = reinterpret_cast<float*>(at(ws, pl.spec_l2));
+  float* spec_dd = reinterpret_cast<float*>(at(ws, pl.spec_dd));
+  FlashParams fs = flash_base(c, q, k, v);
+  if (g.m_spec) {
+    fs.n_q = g.m_spec;
+    fs.qa = g.n_special;
+    fs.qb = g.tf;
+    fs.qc = 0;
+    const int ns = pl.n_split;
+    const int64_t tiles = (g.m_tokens + 31) / 32;
+    fs.n_splits = ns;
+    for (int i = 0; i < ns; ++i) {
+      fs.kbeg[i] = tiles * i / ns * 32;
+      fs.kend[i] = i + 1 == ns ? g.m_tokens : tiles * (i + 1) / ns * 32;
+    }
+    fs.part_o = reinterpret_cast<float*>(at(ws, pl.spec_o));
+    fs.part_lse = reinterpret_cast<float*>(at(ws, pl.spec_lse));
+    ok(launch_flash(c.dtype, kFlashPartial, fs, st));
+    MergeParams m;
+    memset(&m, 0, sizeof(m));
+    m.part_o = fs.part_o;
+    m.part_lse = fs.part_lse;
+    m.n_splits = ns;
+    m.n_q = g.m_spec;
+    m.qa = g.n_special;
+    m.qb = g.tf;
+    m.qc = 0;
+    m.n_heads = (int)H;
+    m.row_stride = H * kHeadDim;
+    m.o32 = spec_o32;
+    m.l2 = spec_l2;
+    m.d_o = d_o;
+    m.dd = spec_dd;
+    ok(launch_merge(c.dtype, m, st));
+  }
+  //    selection output and joint L2 (context partials first)
+  float* osel = reinterpret_cast<float*>(at(ws, pl.osel));
+  float* l2sel = reinterpret_cast<float*>(at(ws, pl.l2sel));
+  if (c.n_ctx && e == hipSuccess) ok(run_context(c, pl, q, k, v, ws, st));
+  SelectParams sp = select_base(c, pl, q, topk_idx, ws);
+  sp.osel = osel;
+  sp.l2 = l2sel;
+  ok(launch_select(c.dtype, sp, st));
+
+  // 3. gate: dq (image rows) = dz W_g, dO_sel blocks, dO_comp, dW_g partials
+  GateBwdParams gp;
+  memset(&gp, 0, sizeof(gp));
+  gp.q = q;
+  gp.wg = wg;
+  gp.d_o = d_o;
+  gp.oc = oc;
+  gp.osel = osel;
+  gp.l2sel = l2sel;
+  gp.g = g;
+  gp.dq = dq;
+  gp.doblk = at(ws, pl.doblk);
+  gp.doT = at(ws, pl.doT);
+  gp.l2blk = reinterpret_cast<float*>(at(ws, pl.l2blk));
+  gp.dblk = reinterpret_cast<float*>(at(ws, pl.dblk));
+  if (c.n_ctx) {
+    gp.dosel_img = at(ws, pl.dosel_img);
+    gp.dsel_img = reinterpret_cast<float*>(at(ws, pl.dsel_img));
+  }
+  gp.doc = at(ws, pl.doc);
+  gp.dc = reinterpret_cast<float*>(at(ws, pl.dc));
+  gp.dwg_part = reinterpret_cast<float*>(at(ws, pl.dwg_part));
+  ok(launch_gate_bwd(c.dtype, gp, st));
+  DwgParams dp;
+  dp.part = gp.dwg_part;
+  dp.n_windows = g.n_windows;
+  dp.n_heads = (int)H;
+  dp.dwg = dwg;
+  ok(launch_dwg_reduce(dp, st));
+
+  FlashBwdParams b0;
+  memset(&b0, 0, sizeof(b0));
+  b0.row_stride = H * kHeadDim;
+  b0.n_heads = (int)H;
+  b0.scale = c.scale;
+  b0.scale_log2 = c.scale * kLog2e;
+  b0.n_splits = 1;
+  b0.n_qsplits = 1;
+
+  // 4. special tokens over all tokens: dq of the special rows, dk / dv of every row
+  if (g.m_spec) {
+    FlashBwdParams b = b0;
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.d_o = d_o;
+    b.n_q = g.m_spec;
+    b.qa = g.n_special;
+    b.qb = g.tf;
+    b.qc = 0;
+    b.do_mapped = 1;
+    b.lse = spec_l2;
+    b.lse_mul = 1.0f;
+    b.dd = spec_dd;
+    b.n_splits = fs.n_splits;
+    for (int i = 0; i < fs.n_splits; ++i) {
+      b.kbeg[i] = fs.kbeg[i];
+      b.kend[i] = fs.kend[i];
+    }
+    b.dq = dq;
+    b.part = reinterpret_cast<float*>(at(ws, pl.spec_o));  // the merged partials are no longer needed
+    ok(launch_flash_bwd(c.dtype, kBwdDQ, b, st));
+    if (b.n_splits > 1) {
+      ReduceParams r;
+      r.part = b.part;
+      r.n_parts = b.n_splits;
+      r.part_stride = g.m_spec * H * kHeadDim;
+      r.n_rows = g.m_spec;
+      r.n_heads = (int)H;
+      r.qa = g.n_special;
+      r.qb = g.tf;
+      r.qc = 0;
+      r.out = dq;
+      r.accumulate = 0;
+      ok(launch_reduce(r, st));
+    }
+    FlashBwdParams kv = b;
+    kv.n_splits = 1;
+    kv.kbeg[0] = 0;
+    kv.kend[0] = g.m_tokens;
+    kv.dk = dk;
+    kv.dv = dv;
+    kv.accumulate = 0;
+    ok(launch_flash_bwd(c.dtype, kBwdDKDV, kv, st));
+  } else {
+    ok(launch_fill(dk, g.m_tokens * H * kHeadDim, st));
+    ok(launch_fill(dv, g.m_tokens * H * kHeadDim, st));
+  }
+
+  // 5. compressed attention over the pooled windows
+  float* dqc = reinterpret_cast<float*>(at(ws, pl.dqc));
+  float* dkc = reinterpret_cast<float*>(at(ws, pl.dkc));
+  float* dvc = reinterpret_cast<float*>(at(ws, pl.dvc));
+  {
+    FlashBwdParams b = b0;
+    b.q = at(ws, pl.qc);
+    b.k = at(ws, pl.kc);
+    b.v = at(ws, pl.vc);
+    b.d_o = gp.doc;
+    b.n_q = g.n_windows;
+    b.qa = g.n_windows > 0 ? g.n_windows : 1;
+    b.qb = 0;
+    b.qc = 0;
+    b.do_mapped = 0;
+    b.lse = lse_c;
+    b.lse_mul = kFloatL2;
+    b.dd = gp.dc;
+    b.kbeg[0] = 0;
+    b.kend[0] = g.n_windows;
+    b.dq = dqc;
+    b.dk = dkc;
+    b.dv = dvc;
+    ok(launch_flash_bwd(c.dtype, kBwdDQ, b, st));
+    ok(launch_flash_bwd(c.dtype, kBwdDKDV, b, st));
+  }
+
+  // 6. selection: inverse top-k lists, then the query and key sides
+  InvParams ip;
+  ip.topk_idx = topk_idx;
+  ip.topk = c.topk;
+  ip.n_windows = g.n_windows;
+  ip.n_heads = (int)H;
+  ip.off = reinterpret_cast<int32_t*>(at(ws, pl.inv_off));
+  ip.cursor = reinterpret_cast<int32_t*>(at(ws, pl.inv_cursor));
+  ip.bsum = reinterpret_cast<int32_t*>(at(ws, pl.inv_bsum));
+  ip.raw = reinterpret_cast<int32_t*>(at(ws, pl.inv_raw));
+  ip.list = reinterpret_cast<int32_t*>(at(ws, pl.inv_list));
+  ok(launch_inverse_index(ip, st));
+  SelBwdParams sb;
+  sb.qblk = at(ws, pl.qblk);
+  sb.qT = at(ws, pl.qT);
+  sb.kblk = at(ws, pl.kblk);
+  sb.kT = at(ws, pl.kT);
+  sb.vrow = at(ws, pl.vrow);
+  sb.doblk = gp.doblk;
+  sb.doT = gp.doT;
+  sb.l2blk = gp.l2blk;
+  sb.dblk = gp.dblk;
+  sb.topk_idx = topk_idx;
+  sb.topk = c.topk;
+  sb.inv_off = ip.off;
+  sb.inv_list = ip.list;
+  sb.g = g;
+  sb.scale = c.scale;
+  sb.scale_log2 = c.scale * kLog2e;
+  sb.dq = dq;
+  sb.dk = dk;
+  sb.dv = dv;
+  ok(launch_sel_bwd(c.dtype, sb, st));
+
+  // 7. context frames (one joint softmax with the selection): image queries over each frame
+  if (c.n_ctx) {
+    FlashBwdParams b = b0;
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.d_o = gp.dosel_img;
+    b.n_q = g.m_img;
+    b.qa = g.grid_h * g.grid_w;
+    b.qb = g.tf;
+    b.qc = g.n_special;
+    b.do_mapped = 0;
+    b.lse = l2sel;
+    b.lse_mul = 1.0f;
+    b.dd = gp.dsel_img;
+    b.n_splits = c.n_ctx;
+    for (int i = 0; i < c.n_ctx; ++i) {
+      b.kbeg[i] = (int64_t)c.ctx[i] * g.tf;
+      b.kend[i] = b.kbeg[i] + g.tf;
+    }
+    b.dq = dq;
+    b.accumulate = 1;
+    b.part = reinterpret_cast<float*>(at(ws, pl.ctx_dq));
+    ok(launch_flash_bwd(c.dtype, kBwdDQ, b, st));
+    if (c.n_ctx > 1) {
+      ReduceParams r;
+      r.part = b.part;
+      r.n_parts = c.n_ctx;
+      r.part_stride = g.m_img * H * kHeadDim;
+      r.n_rows = g.m_img;
+      r.n_heads = (int)H;
+      r.qa = g.grid_h * g.grid_w;
+      r.qb = g.tf;
+      r.qc = g.n_special;
+      r.out = dq;
+      r.accumulate = 1;
+      ok(launch_reduce(r, st));
+    }
+    for (int i = 0; i < c.n_ctx; ++i) {
+      FlashBwdParams kv = b;
+      kv.n_splits = 1;
+      kv.kbeg[0] = (int64_t)c.ctx[i] * g.tf;
+      kv.kend[0] = kv.kbeg[0] + g.tf;
+      kv.n_qsplits = pl.ctx_qsplits;
+      kv.dk = dk;
+      kv.dv = dv;
+      kv.accumulate = 1;
+      kv.part = reinterpret_cast<float*>(at(ws, pl.ctx_dkdv));
+      ok(launch_flash_bwd(c.dtype, kBwdDKDV, kv, st));
+      if (kv.n_qsplits > 1) {
+        ReduceParams r;
+        r.n_parts = kv.n_qsplits;
+        r.part_stride = g.tf * H * kHeadDim;
+        r.n_rows = g.tf;
+        r.n_heads = (int)H;
+        r.qa = g.tf;
+        r.qb = 0;
+        r.qc = kv.kbeg[0];
+        r.accumulate = 1;
+        r.part = kv.part;
+        r.out = dk;
+        ok(launch_reduce(r, st));
+        r.part = kv.part + (int64_t)kv.n_qsplits * g.tf * H * kHeadDim;
+        r.out = dv;
+        ok(launch_reduce(r, st));
+      }
+    }
+  }
+
+  // 8. pooling: each window token gets its pooled row's gradient / s^2
+  PoolBwdParams pb;
+  pb.dqc = dqc;
+  pb.dkc = dkc;
+  pb.dvc = dvc;
+  pb.g = g;
+  pb.inv_area = 1.0f / (float)(g.pool * g.pool);
+  pb.dq = dq;
+  pb.dk = dk;
+  pb.dv = dv;
+  ok(launch_pool_bwd(pb, st));
+  return hip_status(e);
 }
 
 }  // extern "C"

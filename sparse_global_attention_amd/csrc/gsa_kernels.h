@@ -40,8 +40,10 @@ __host__ __device__ __forceinline__ int64_t window_image_index(const Geometry& g
 struct PoolParams {
   const void* src[3];  // q, k, v in the token layout
   void* dst[3];        // pooled [M'][H][d] (an entry may be null: no mean written)
-  void* kblk;          // optional [M'][H][sb][d] copy of K, window-local key order
-  void* vblk;          // optional [M'][H][d][sb] transposed copy of V
+  // optional blocked copies of each tensor's windows, window-local token order
+  // (zero padded to sb tokens): rows [M'][H][sb][d] and transposed [M'][H][d][sb]
+  void* rows[3];
+  void* trans[3];
   Geometry g;
   float inv_area;      // 1.0f / (s*s)
   int first_tensor;    // grid.y enumerates tensors first_tensor .. first_tensor+grid.y-1
@@ -128,7 +130,14 @@ struct MergeParams {
   int64_t n_q, qa, qb, qc;
   int n_heads;
   int64_t row_stride;
-  void* o;
+  void* o;              // merged rows in the input dtype at token rows (or null)
+  // optional backward inputs: o32 [n_q][H][d] merged rows in float, l2
+  // [n_q][H] log2 of the softmax denominator; with d_o (token rows, dtype)
+  // also dd [n_q][H] = d_o . o
+  float* o32;
+  float* l2;
+  const void* d_o;
+  float* dd;
 };
 hipError_t launch_merge(int dtype, const MergeParams& p, hipStream_t stream);
 
@@ -145,6 +154,7 @@ struct SelectParams {
   const float* ctx_o;   // [n_ctx][M_img][H][d] (normalised)
   const float* ctx_lse; // [n_ctx][M_img][H] log-sum-exp
   float* osel;          // standalone output [M_img][H][d]
+  float* l2;            // standalone, optional: [M_img][H] log2 of the joint softmax denominator
   const void* wg;       // fused epilogue: gate projection [H][d]
   const float* oc;      // fused epilogue: compressed output [M'][H][d]
   void* o;              // fused epilogue: output rows in the token layout
@@ -176,5 +186,133 @@ struct CombineParams {
   Geometry g;
 };
 hipError_t launch_combine(int dtype, const CombineParams& p, hipStream_t stream);
+
+// ---- backward ------------------------------------------------------------------
+// Softmax attention backward with the log2 denominators L2 (P = exp2(c s - L2),
+// c = scale log2 e) and D = dO . O given per query:
+//   kBwdDQ    a workgroup owns 32*WAVES query rows and sweeps one key range:
+//             dQ = scale sum_j dS_j k_j, dS_j = P_j (dO . v_j - D);
+//   kBwdDKDV  a workgroup owns 32*WAVES keys of range 0 and sweeps the queries
+//             (a contiguous part of them per query split):
+//             dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i.
+enum BwdKind { kBwdDQ = 0, kBwdDKDV = 1 };
+struct FlashBwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  int64_t row_stride;  // elements between rows of q/k/v/d_o and of the float outputs (H*d)
+  int n_heads;
+  int64_t n_q, qa, qb, qc;  // query r -> token row (r / qa) * qb + qc + r % qa of q
+  int do_mapped;            // 1: d_o rows follow that map; 0: d_o row = r
+  const float* lse;         // [n_q][H]; L2 = lse * lse_mul
+  float lse_mul;
+  const float* dd;          // [n_q][H]
+  int n_splits;             // kBwdDQ: one split per key range (partials when > 1)
+  int64_t kbeg[kMaxRanges], kend[kMaxRanges];
+  int n_qsplits;            // kBwdDKDV: query splits (partials when > 1)
+  float scale, scale_log2;
+  float* dq;                // kBwdDQ, one split: rows by the query map
+  float* dk;                // kBwdDKDV, one query split: rows kbeg[0] + key
+  float* dv;
+  float* part;              // partials: kBwdDQ [split][n_q][H][d]; kBwdDKDV dk [z][nk][H][d] then dv
+  int accumulate;           // add into dq / dk / dv instead of storing
+};
+hipError_t launch_flash_bwd(int dtype, int kind, const FlashBwdParams& p, hipStream_t stream);
+
+// out[row(r)] (+)= sum over n_parts of part[i * part_stride + r*H*d ...]
+struct ReduceParams {
+  const float* part;
+  int n_parts;
+  int64_t part_stride;  // elements between consecutive partials
+  int64_t n_rows;
+  int n_heads;
+  int64_t qa, qb, qc;   // row r -> output row (r / qa) * qb + qc + r % qa
+  float* out;
+  int accumulate;
+};
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
+
+// Gate backward, one wave per (window, head): g, dz, the selection and
+// compressed output gradients and the blocked copies the selection backward
+// gathers.
+struct GateBwdParams {
+  const void* q;
+  const void* wg;
+  const void* d_o;
+  const float* oc;     // [M'][H][d]
+  const float* osel;   // [M_img][H][d]
+  const float* l2sel;  // [M_img][H]
+  Geometry g;
+  float* dq;           // token rows (float): image rows stored = dz W_g
+  void* doblk;         // [M'][H][sb][d] dO_sel rows (dtype)
+  void* doT;           // [M'][H][d][sb] dO_sel transposed (dtype)
+  float* l2blk;        // [M'][H][sb] (+inf on padding)
+  float* dblk;         // [M'][H][sb] D_sel = dO_sel . O_sel (0 on padding)
+  void* dosel_img;     // optional [M_img][H][d] (dtype)
+  float* dsel_img;     // optional [M_img][H]
+  void* doc;           // [M'][H][d] dO_comp (dtype)
+  float* dc;           // [M'][H] dO_comp . O'_comp
+  float* dwg_part;     // [M'][H][d]
+};
+hipError_t launch_gate_bwd(int dtype, const GateBwdParams& p, hipStream_t stream);
+
+// Inverse top-k lists: for head h and window j, the query windows whose
+// top-k holds j, ascending.  off [H*M' + 1] (exclusive scan of the counts).
+struct InvParams {
+  const int32_t* topk_idx;
+  int topk;
+  int64_t n_windows;
+  int n_heads;
+  int32_t* off;     // [H*M' + 1]: counts, then offsets
+  int32_t* cursor;  // [H*M']
+  int32_t* bsum;    // scan block sums
+  int32_t* raw;     // [H*M'*k] lists in fill order
+  int32_t* list;    // [H*M'*k] lists, ascending
+};
+hipError_t launch_inverse_index(const InvParams& p, hipStream_t stream);
+
+struct SelBwdParams {
+  const void* qblk;  // [M'][H][sb][d]
+  const void* qT;    // [M'][H][d][sb]
+  const void* kblk;
+  const void* kT;
+  const void* vrow;  // [M'][H][sb][d]
+  const void* doblk;
+  const void* doT;
+  const float* l2blk;
+  const float* dblk;
+  const int32_t* topk_idx;
+  int topk;
+  const int32_t* inv_off;
+  const int32_t* inv_list;
+  Geometry g;
+  float scale, scale_log2;
+  float* dq;  // token rows (float), added
+  float* dk;
+  float* dv;
+};
+hipError_t launch_sel_bwd(int dtype, const SelBwdParams& p, hipStream_t stream);
+
+struct PoolBwdParams {
+  const float* dqc;  // [M'][H][d]
+  const float* dkc;
+  const float* dvc;
+  Geometry g;
+  float inv_area;
+  float* dq;  // token rows (float), added
+  float* dk;
+  float* dv;
+};
+hipError_t launch_pool_bwd(const PoolBwdParams& p, hipStream_t stream);
+
+struct DwgParams {
+  const float* part;  // [M'][H][d]
+  int64_t n_windows;
+  int n_heads;
+  float* dwg;         // [H][d]
+};
+hipError_t launch_dwg_reduce(const DwgParams& p, hipStream_t stream);
+hipError_t launch_fill(float* x, int64_t n, hipStream_t stream);
 
 }  // namespace gsa

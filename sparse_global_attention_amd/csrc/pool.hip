@@ -8,12 +8,14 @@
 // in row-major order from +0, multiplied by 1/s^2 and rounded to the dtype,
 // so the pooled tensors are reproducible bit for bit.
 //
-// While the K and V windows are in registers the kernel can also write the
-// two copies the selection kernel gathers from, one contiguous block per
+// While a tensor's windows are in registers the kernel can also write the
+// copies the selection kernels gather from, one contiguous block per
 // (window, head):
-//   kblk [M'][H][sb][d]  K rows in window-local order (zero padded to sb keys)
-//   vblk [M'][H][d][sb]  V transposed (keys contiguous per channel), the
-//                        layout the PV matrix-core operand wants.
+//   rows  [M'][H][sb][d]  rows in window-local order (zero padded to sb tokens),
+//                         the layout of a score-product operand;
+//   trans [M'][H][d][sb]  transposed (tokens contiguous per channel), the
+//                         layout of an operand that contracts over tokens.
+// The forward uses K rows and V transposed; the backward also Q, K^T, V rows.
 #include "gsa_device.h"
 #include "gsa_kernels.h"
 
@@ -37,8 +39,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   const T* src = static_cast<const T*>(p.src[tensor]);
   const int s2 = (int)(g.pool * g.pool);
 
-  T* kb = (tensor == 1 && p.kblk) ? static_cast<T*>(p.kblk) + (j * g.n_heads + h) * g.sb * kHeadDim : nullptr;
-  T* vb = (tensor == 2 && p.vblk) ? static_cast<T*>(p.vblk) + (j * g.n_heads + h) * kHeadDim * g.sb : nullptr;
+  T* kb = p.rows[tensor] ? static_cast<T*>(p.rows[tensor]) + (j * g.n_heads + h) * g.sb * kHeadDim : nullptr;
+  T* vb = p.trans[tensor] ? static_cast<T*>(p.trans[tensor]) + (j * g.n_heads + h) * kHeadDim * g.sb : nullptr;
 
   float acc[VE];
 #pragma unroll

@@ -24,6 +24,7 @@
 
 #include "gsa_device.h"
 #include "gsa_kernels.h"
+#include "select_frag.h"
 
 namespace gsa {
 
@@ -37,105 +38,6 @@ struct SelChunk {
   int jv;    // window of this lane's 8 S^T slots (-1: none)
   int kkv0;  // window-local key of the first of them
 };
-
-template <typename T>
-struct Frag16;
-
-template <>
-struct Frag16<__bf16> {
-  struct Q {
-    bf16x8 v[2];
-  };
-  // lane (q, g) holds d = 16 g + 8 ks + [0, 8)
-  __device__ static Q load_q(const __bf16* row, int g) {
-    Q f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (row) {
-        f.v[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * g + 8 * ks);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f.v[ks][e] = (__bf16)0.0f;
-      }
-    }
-    return f;
-  }
-  __device__ static float q_dot(const Q& f, const __bf16* w, int g) {
-    float z = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) z += (float)f.v[ks][e] * (float)w[16 * g + 8 * ks + e];
-    return z;
-  }
-  __device__ static f32x4 qk(const uint4 (&k)[2], const Q& q) {
-    f32x4 s = {0, 0, 0, 0};
-    s = mfma16(__builtin_bit_cast(bf16x8, k[0]), q.v[0], s);
-    s = mfma16(__builtin_bit_cast(bf16x8, k[1]), q.v[1], s);
-    return s;
-  }
-  __device__ static void pv(const uint4 (&v)[4][1], const f32x4& p0, const f32x4& p1, f32x4 o[4]) {
-    bf16x8 b = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],
-                (__bf16)p1[0], (__bf16)p1[1], (__bf16)p1[2], (__bf16)p1[3]};
-#pragma unroll
-    for (int m = 0; m < 4; ++m) o[m] = mfma16(__builtin_bit_cast(bf16x8, v[m][0]), b, o[m]);
-  }
-};
-
-template <>
-struct Frag16<float> {
-  struct Q {
-    float v[16];
-  };
-  // lane (q, g) holds d = 16 g + i; MFMA i contracts that d.
-  __device__ static Q load_q(const float* row, int g) {
-    Q f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 x = row ? *reinterpret_cast<const f32x4*>(row + 16 * g + 4 * i) : f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f.v[4 * i + e] = x[e];
-    }
-    return f;
-  }
-  __device__ static float q_dot(const Q& f, const float* w, int g) {
-    float z = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) z += f.v[i] * w[16 * g + i];
-    return z;
-  }
-  __device__ static f32x4 qk(const uint4 (&k)[4], const Q& q) {
-    f32x4 s = {0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 a = __builtin_bit_cast(f32x4, k[i]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = mfma16(a[e], q.v[4 * i + e], s);
-    }
-    return s;
-  }
-  // slot 8g + 4 tau + e <-> S_tau[e] (B) and v element 4 tau + e (A)
-  __device__ static void pv(const uint4 (&v)[4][2], const f32x4& p0, const f32x4& p1, f32x4 o[4]) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      f32x4 lo = __builtin_bit_cast(f32x4, v[m][0]);
-      f32x4 hi = __builtin_bit_cast(f32x4, v[m][1]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[m] = mfma16(lo[e], p0[e], o[m]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[m] = mfma16(hi[e], p1[e], o[m]);
-    }
-  }
-};
-
-// Window id of top-k entry t, from the two registers holding entries lane and
-// lane+64.  Entries past k, negative or not below M' read as -1 (skipped).
-__device__ __forceinline__ int topk_entry(int tr0, int tr1, int t, int K, int64_t n_windows) {
-  int a = __builtin_amdgcn_ds_bpermute((t & 63) << 2, tr0);
-  int b = __builtin_amdgcn_ds_bpermute((t & 63) << 2, tr1);
-  int j = t < 64 ? a : b;
-  return (t >= K || j < 0 || j >= n_windows) ? -1 : j;
-}
 
 template <typename T>
 __device__ __forceinline__ void load_chunk(SelChunk<T>& ch, const SelectParams& p, int64_t h, int c, int ql,
@@ -327,6 +229,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         *reinterpret_cast<f32x4*>(p.osel + (u * H + h) * kHeadDim + 16 * m + 4 * g) = res[m];
+      // log2 of the joint denominator: sum of exp2(c s) over all keys = den 2^mm
+      if (p.l2 && g == 0) p.l2[u * H + h] = den > 0.0f ? mm + log2f(den) : INFINITY;
     }
     }
   }

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     fns = header_functions()
     for want in ("gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn", "gsa_special_attn",
                  "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn", "gsa_workspace_size",
-                 "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_status_string"):
+                 "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_backward",
+                 "gsa_status_string"):
         assert want in fns
 
 
@@ -116,6 +117,14 @@ def test_pointer_validation(lib):
     assert lib.call_status("gsa_descriptor_attn", c, A, A + 16, A + 32, A + 16, None) == 1  # o aliases kd
     assert lib.call_status("gsa_descriptor_attn", c, MISALIGNED, A + 16, A + 32, A + 48, None) == 1
     assert lib.call_status("gsa_descriptor_count", c, None) == 1
+    # gsa_backward(cfg, q, k, v, wg, idx, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream)
+    bw = [A, A + 16, A + 32, A + 48, A + 64, A + 80, A + 96, A + 112, A + 128, A + 144]
+    # rejected on the host before any launch: an output aliasing an input or
+    # another output, a null or misaligned pointer
+    for i, bad in ((6, A), (7, A + 96), (9, A + 128), (3, None), (8, MISALIGNED)):
+        args = list(bw)
+        args[i] = bad
+        assert lib.call_status("gsa_backward", c, *args, A + 256, 1 << 40, None) == 1, (i, bad)
 
 
 def test_workspace_validation(lib):
@@ -133,6 +142,10 @@ def test_workspace_validation(lib):
     need = lib.gsa_workspace_size(cc, lib.GSA_OP_COMPRESSED)
     assert need > 0
     assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, o, o + 4096, None, A, need - 1, None) == 4
+    need = lib.gsa_workspace_size(cc, lib.GSA_OP_BACKWARD)
+    bw = [A + 16 * i for i in range(6)] + [o, o + 4096, o + 8192, o + 12288]
+    assert lib.call_status("gsa_backward", c, *bw, A, need - 1, None) == 4
+    assert lib.call_status("gsa_backward", c, *bw, None, need, None) == 1
     assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, o, o + 4096, None, None, need, None) == 1
 
 

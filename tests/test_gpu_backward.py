@@ -1,0 +1,148 @@
+"""Parity of the HIP backward (gsa_backward, through the C ABI) with the CPU
+oracle's gradients, element by element, on seeded inputs and output
+gradients.  The top-k window sets both sides hold fixed come from the
+oracle's own top-k of the same inputs, so no oracle input comes from the GPU.
+At the full workload sizes (too large for the whole-layer oracle) the checks
+are properties that hold at any size: sum_t dV_t = sum_t dO_t and
+sum_t dK_t = 0 per head and channel, finite values, and determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import sparse_global_attention_amd as gsa
+from gen.configs import BF16, F32, PI3_LONG, TINY_F32, VGGT_CTX, GSAShape
+from gsa_testlib import DEV, to_dev, workspace
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny_f32": TINY_F32,
+    "odd_bf16": GSAShape("odd 3f-12x8-h3-s4-k5", 3, 2, 12, 8, 3, 64, 4, 5, BF16, seed=21),
+    "odd_f32": GSAShape("odd 3f-12x8-h3-s4-k5 fp32", 3, 2, 12, 8, 3, 64, 4, 5, F32, seed=22),
+    "mid_bf16": GSAShape("mid 8f-16x16-h4-s4-k8", 8, 5, 16, 16, 4, 64, 4, 8, BF16, seed=40),
+    "s8": GSAShape("s8 3f-16x16-h2-s8-k3", 3, 1, 16, 16, 2, 64, 8, 3, BF16, seed=23),
+    "s1": GSAShape("s1 2f-6x5-h2-s1-k7", 2, 1, 6, 5, 2, 64, 1, 7, BF16, seed=24),
+    "s2": GSAShape("s2 4f-8x8-h2-s2-k4", 4, 3, 8, 8, 2, 64, 2, 4, BF16, seed=25),
+    "s5": GSAShape("s5 2f-10x10-h2-s5-k3", 2, 2, 10, 10, 2, 64, 5, 3, BF16, seed=33),
+    "s6_f32": GSAShape("s6 3f-12x12-h2-s6-k3 fp32", 3, 1, 12, 12, 2, 64, 6, 3, F32, seed=34),
+    "p0": GSAShape("p0 4f-8x12-h2-s4-k3", 4, 0, 8, 12, 2, 64, 4, 3, BF16, seed=26),
+    "ctx": GSAShape("ctx 6f-8x8-h2-s4-k3+ctx{0,3}", 6, 2, 8, 8, 2, 64, 4, 3, BF16, ctx_frames=(0, 3), seed=27),
+    "ctx_f32": GSAShape("ctx 5f-8x8-h1-s2-k6+ctx{4}", 5, 1, 8, 8, 1, 64, 2, 6, F32, ctx_frames=(4,), seed=28),
+    "k_clamp": GSAShape("kclamp 2f-8x8-h2-s4-k64", 2, 1, 8, 8, 2, 64, 4, 64, BF16, seed=29),
+    "k40": GSAShape("k40 10f-16x16-h2-s4-k40", 10, 1, 16, 16, 2, 64, 4, 40, BF16, seed=32),
+}
+
+# Gradients are sums of many products; errors are stated relative to the
+# largest reference magnitude of each tensor.  bf16: operands of every
+# matrix-core product (q, k, v, dO, P, dS) are bf16 (relative rounding 2^-9),
+# the accumulation is fp32.  fp32: the exp2 and the fp32 accumulation.
+BF16_MAX_REL, BF16_MEAN_REL = 2e-2, 2e-3
+F32_MAX_REL = 1e-5
+
+
+def assert_grad_close(got, ref, dtype, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = np.abs(got - ref) / scale
+    mx, mean = float(err.max()), float(err.mean())
+    if dtype == BF16:
+        assert mx <= BF16_MAX_REL and mean <= BF16_MEAN_REL, f"{what}: max {mx:.3g} mean {mean:.3g} (of {scale:.3g})"
+    else:
+        assert mx <= F32_MAX_REL, f"{what}: max {mx:.3g} mean {mean:.3g} (of {scale:.3g})"
+    return mx, mean
+
+
+def oracle_topk(sh, q, k):
+    """The oracle's top-k of the workload (its own pooling and guide scores)."""
+    qc, kc = oracle.pool(sh, q), oracle.pool(sh, k)
+    vc = np.zeros_like(qc)
+    return oracle.compressed(sh, qc, kc, vc, np.arange(sh.n_windows))[1]
+
+
+def gpu_backward(sh, q, k, v, wg, idx, d_o):
+    cfg = gsa.GSAConfig.from_shape(sh)
+    dq_, dk_, dv_ = (torch.empty(sh.qkv_shape, dtype=torch.float32, device=DEV) for _ in range(3))
+    dwg_ = torch.empty((sh.n_heads, sh.head_dim), dtype=torch.float32, device=DEV)
+    ws = workspace(cfg, gsa.GSA_OP_BACKWARD)
+    gsa.gsa_backward(cfg, to_dev(q, sh.dtype), to_dev(k, sh.dtype), to_dev(v, sh.dtype), to_dev(wg, sh.dtype),
+                     torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV), to_dev(d_o, sh.dtype),
+                     dq_, dk_, dv_, dwg_, ws)
+    torch.cuda.synchronize()
+    return dq_, dk_, dv_, dwg_
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_backward_matches_oracle(name):
+    sh = SHAPES[name]
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    idx = oracle_topk(sh, q, k)
+    got = [x.cpu().numpy() for x in gpu_backward(sh, q, k, v, wg, idx, d_o)]
+    ref = oracle.backward(sh, q, k, v, wg, idx, d_o)
+    for g_, r_, what in zip(got, ref, ("dq", "dk", "dv", "dwg")):
+        mx, mean = assert_grad_close(g_.reshape(r_.shape), r_, sh.dtype, f"{name} {what}")
+        print(f"{name} {what}: max {mx:.3g} mean {mean:.3g} of the largest |ref|")
+
+
+def test_backward_is_deterministic():
+    sh = SHAPES["mid_bf16"]
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    idx = oracle_topk(sh, q, k)
+    a = gpu_backward(sh, q, k, v, wg, idx, d_o)
+    b = gpu_backward(sh, q, k, v, wg, idx, d_o)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("sh", [VGGT_CTX, PI3_LONG], ids=["vggt_ctx", "pi3_long"])
+def test_backward_full_size_sum_identities(sh):
+    """At the full sizes: column sums of dV equal those of dO, column sums of dK
+    vanish (per head and channel; softmax weights sum to one and each query's
+    score gradients sum to zero), the gradients are finite and a second call is
+    bitwise identical.  The top-k sets are those of the GPU forward step (any
+    fixed sets satisfy the identities)."""
+    from gsa_testlib import Case
+    c = Case(sh)
+    qc, kc, vc = c.pool()
+    _, idx, _ = c.compressed(qc, kc, vc, with_scores=False)
+    del qc, kc, vc
+    d_o = to_dev(gen.make_output_grad(sh), sh.dtype)
+    cfg = c.cfg
+    dq_, dk_, dv_ = (torch.empty(sh.qkv_shape, dtype=torch.float32, device=DEV) for _ in range(3))
+    dwg_ = torch.empty((sh.n_heads, sh.head_dim), dtype=torch.float32, device=DEV)
+    ws = workspace(cfg, gsa.GSA_OP_BACKWARD)
+    gsa.gsa_backward(cfg, c.dq, c.dk, c.dv, c.dwg, idx, d_o, dq_, dk_, dv_, dwg_, ws)
+    torch.cuda.synchronize()
+    shp = (sh.m_tokens, sh.n_heads, sh.head_dim)
+    G = d_o.float().view(shp).double()
+    for x in (dq_, dk_, dv_, dwg_):
+        assert torch.isfinite(x).all()
+    sum_dv = dv_.view(shp).double().sum(0)
+    sum_do = G.sum(0)
+    sum_dk = dk_.view(shp).double().sum(0)
+    # Each column sum adds ~1e6 terms whose matrix-core operands (P, dS, dO_sel)
+    # were rounded to bf16 (relative 2^-9, independent signs): the deviation is
+    # a random sum of size ~2^-9 sqrt(sum of squared terms).  Allow 8x that with
+    # 2^-8 per term; a dropped or mis-scaled branch moves a sum by orders more.
+    sig_v = (dv_.view(shp).double().pow(2).sum(0) + G.pow(2).sum(0)).sqrt()
+    sig_k = dk_.view(shp).double().pow(2).sum(0).sqrt()
+    err_v = (sum_dv - sum_do).abs() / sig_v
+    err_k = sum_dk.abs() / sig_k
+    print(f"{sh.name}: |sum dV - sum dO| / sqrt(sum sq) max {err_v.max().item():.3g}, "
+          f"|sum dK| / sqrt(sum sq) max {err_k.max().item():.3g}")
+    assert err_v.max().item() <= 8 * 2.0 ** -8
+    assert err_k.max().item() <= 8 * 2.0 ** -8
+    first = [x.clone() for x in (dq_, dk_, dv_, dwg_)]
+    gsa.gsa_backward(cfg, c.dq, c.dk, c.dv, c.dwg, idx, d_o, dq_, dk_, dv_, dwg_, ws)
+    torch.cuda.synchronize()
+    for x, y in zip(first, (dq_, dk_, dv_, dwg_)):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
