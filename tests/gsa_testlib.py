@@ -191,3 +191,18 @@ def check_topk(sh, gpu_idx: np.ndarray, orc_idx: np.ndarray, orc_sc: np.ndarray,
             s = gpu_s[i, h, :kp]
             assert np.all(np.diff(s) <= TIE_REL * np.abs(s[:-1]) + TIE_ABS * absmax[i, h] + 1e-12), (i, h, s)
     return banded
+
+
+def same_sets(gpu_idx: np.ndarray, orc_idx: np.ndarray) -> np.ndarray:
+    """[n][H] mask of the (window, head) rows whose GPU top-k set equals the oracle's.
+
+    Only those rows have a unique expected selection output; the others hold a
+    different, valid choice inside the tie band (checked by check_topk)."""
+    return np.all(np.sort(gpu_idx, axis=-1) == np.sort(orc_idx, axis=-1), axis=-1)
+
+
+def assert_close_rows(got: np.ndarray, ref: np.ndarray, rows: np.ndarray, dtype: int, what: str):
+    """assert_close on the (window, head) rows selected by rows [n][H], for
+    per-window outputs [n][s*s][H][d]."""
+    mask = np.broadcast_to(rows[:, None, :, None], got.shape)
+    return assert_close(got[mask], ref[mask], dtype, what)

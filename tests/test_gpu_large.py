@@ -4,8 +4,9 @@ times (gsa_forward), checked on sampled outputs the oracle computes one by one:
 * pooled Q/K/V: every element, bit for bit;
 * compressed attention and top-k: sampled query windows x all heads
   (tie-band rule for the index sets);
-* the forward's image rows of those windows (oracle selection driven by the
-  GPU's index sets, then upsample + gate);
+* the forward's image rows of those windows (oracle selection over the
+  oracle's own index sets, then upsample + gate), on every (window, head)
+  whose GPU set equals the oracle's (the others: valid tie-band choices);
 * the forward's special rows: sampled special tokens x all heads;
 * determinism: a second forward is bitwise identical;
 * frame attention (the per-frame step beside GSA): sampled tokens x all heads;
@@ -25,7 +26,8 @@ import torch
 import gen
 import oracle
 from gen.configs import PEAKY, PI3_LONG, VGGT_CTX
-from gsa_testlib import Case, assert_close, check_topk, special_token_ids, to_host, window_token_ids
+from gsa_testlib import (Case, assert_close, assert_close_rows, check_topk, same_sets, special_token_ids, to_host,
+                         window_token_ids)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -93,10 +95,15 @@ def test_full_size_sampled_parity(name):
     log(f"[{name}] top-k: {banded} of {gidx.shape[0] * gidx.shape[1]} (window, head) rows in the tie band")
 
     log(f"[{name}] oracle: selection + gate ({time.time() - t0:.0f} s)")
-    osel = oracle.select(sh, c.q, c.k, c.v, wins, gidx)
+    # the oracle's own sets; rows where the GPU chose another valid tie-band
+    # set have no unique expected output and are left out
+    same = same_sets(gidx, oidx)
+    assert (~same).sum() <= banded, f"{name}: {(~same).sum()} rows with other sets, {banded} in the band"
+    osel = oracle.select(sh, c.q, c.k, c.v, wins, oidx)
     oimg = oracle.gate_combine(sh, c.q, c.wg, wins, ooc, osel)
-    mx, mean, rel = assert_close(o_img.reshape(oimg.shape), oimg, sh.dtype, f"{name} O_img (sampled)")
-    log(f"[{name}] O_img: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e}")
+    mx, mean, rel = assert_close_rows(o_img.reshape(oimg.shape), oimg, same, sh.dtype, f"{name} O_img (sampled)")
+    log(f"[{name}] O_img: max-abs {mx:.2e} mean-abs {mean:.2e} rel-L2 {rel:.2e} "
+        f"({same.sum()} of {same.size} (window, head) rows with the oracle's sets)")
 
     log(f"[{name}] oracle: special attention for {len(rows)} rows ({time.time() - t0:.0f} s)")
     ospec = oracle.special(sh, c.q, c.k, c.v, rows)

@@ -13,8 +13,8 @@ import torch
 import gen
 import oracle
 from gen.configs import BF16, F32, SMALL_BF16, TINY_F32, GSAShape
-from gsa_testlib import (Case, assert_close, check_topk, special_token_ids, to_host, window_image_ids,
-                         window_token_ids)
+from gsa_testlib import (DEV, Case, assert_close, assert_close_rows, check_topk, same_sets, special_token_ids,
+                         to_dev, to_host, window_image_ids, window_token_ids)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ class Result:
         # HIP path
         self.gqc, self.gkc, self.gvc = c.pool()
         self.goc, self.gidx, self.gsc = c.compressed(self.gqc, self.gkc, self.gvc)
-        self.gosel = c.select(self.gidx)
+        self.gosel_own = c.select(self.gidx)  # the GPU's own sets (GPU-only consistency checks)
         self.gspec = c.special()
         self.gout = c.forward()
         torch.cuda.synchronize()
@@ -56,7 +56,11 @@ class Result:
         self.qc, self.kc, self.vc = (oracle.pool(sh, x) for x in (c.q, c.k, c.v))
         self.oc, self.idx, self.sc, self.amax = oracle.compressed(sh, self.qc, self.kc, self.vc, wins)
         self.gidx_h = self.gidx.cpu().numpy()
-        self.osel_gpu_idx = oracle.select(sh, c.q, c.k, c.v, wins, self.gidx_h)
+        self.same = same_sets(self.gidx_h, self.idx)
+        self.osel = oracle.select(sh, c.q, c.k, c.v, wins, self.idx)
+        # the selection kernel driven by the oracle's sets: every row has a unique expected value
+        self.gosel = c.select(torch.from_numpy(self.idx).to(DEV))
+        torch.cuda.synchronize()
         rows = np.arange(sh.m_spec)
         self.spec = oracle.special(sh, c.q, c.k, c.v, rows) if sh.m_spec else None
 
@@ -100,7 +104,7 @@ def test_selection_attention(name):
     sh = r.sh
     osel = to_host(r.gosel)  # [M_img][H][d] by image token
     got = osel[window_image_ids(sh)]  # -> [M'][s*s][H][d]
-    assert_close(got, r.osel_gpu_idx, sh.dtype, f"{name} O_sel")
+    assert_close(got, r.osel, sh.dtype, f"{name} O_sel")
 
 
 @pytest.mark.parametrize("name", [n for n in ALL if SHAPES[n].n_special > 0])
@@ -120,9 +124,13 @@ def test_forward_matches_oracle(name):
     sh = r.sh
     c = r.case
     wins = np.arange(sh.n_windows)
-    oimg = oracle.gate_combine(sh, c.q, c.wg, wins, r.oc, r.osel_gpu_idx)
+    oimg = oracle.gate_combine(sh, c.q, c.wg, wins, r.oc, r.osel)
     got = to_host(r.gout).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
-    assert_close(got[window_token_ids(sh)], oimg, sh.dtype, f"{name} O_img")
+    # the forward picks its own top-k: rows whose set differs from the oracle's
+    # (a valid tie-band choice, see test_compressed_attention_and_topk) have no
+    # unique expected output and are left out; they must be rare
+    assert (~r.same).sum() <= max(2, r.same.size // 100), f"{name}: {(~r.same).sum()} rows with other sets"
+    assert_close_rows(got[window_token_ids(sh)], oimg, r.same, sh.dtype, f"{name} O_img")
     if sh.m_spec:
         assert_close(got[special_token_ids(sh)], r.spec, sh.dtype, f"{name} O_spec (forward)")
 
@@ -133,7 +141,7 @@ def test_forward_equals_composed_calls(name):
     r = result(name)
     sh, c = r.sh, r.case
     o = r.gspec.clone()
-    gsa.gsa_gate_combine(c.cfg, c.dq, c.dwg, None, r.goc, r.gosel, o)
+    gsa.gsa_gate_combine(c.cfg, c.dq, c.dwg, None, r.goc, r.gosel_own, o)
     torch.cuda.synchronize()
     fused = to_host(r.gout)
     composed = to_host(o)
@@ -202,14 +210,17 @@ def test_topk_ties_beyond_the_candidate_slots(k):
     match the oracle.  k = 8 runs with the 64 slots per query, k = 100 with 144."""
     sh = GSAShape(f"ties-many 16f-16x16-h2-s4-k{k}", 16, 1, 16, 16, 2, 64, 4, k, BF16, seed=41)
     c = Case(sh)
-    qc, kc, vc = c.pool()
-    kc[:, 0] = kc[5, 0].clone()
+    # seeded pooled tensors (host), with head 0's key windows all equal
+    shp = (sh.n_windows, sh.n_heads, sh.head_dim)
+    pq, pk, pv = (gen.normal(shp, sh.dtype, sh.seed, 20 + i) for i in range(3))
+    pk[:, 0] = pk[5, 0]
+    qc, kc, vc = (to_dev(x, sh.dtype) for x in (pq, pk, pv))
     oc, idx, sc = c.compressed(qc, kc, vc)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
     assert np.all(gi[:, 0] == np.arange(sh.topk, dtype=np.int32))
     wins = np.arange(sh.n_windows)
-    q64, k64, v64 = (to_host(x).astype(np.float32) for x in (qc, kc, vc))  # the oracle takes float32 pooled values
+    q64, k64, v64 = (gen.to_f32(x, sh.dtype) for x in (pq, pk, pv))  # the oracle takes float32 pooled values
     roc, ridx, rsc, amax = oracle.compressed(sh, q64, k64, v64, wins)
     assert_close(to_host(oc), roc, sh.dtype, "ties-many O'_comp")
     check_topk(sh, gi, ridx, rsc, amax, oracle.guide_scores(sh, q64, k64, wins, gi))
@@ -270,10 +281,12 @@ def test_scores_growing_along_the_keys():
     spec = oracle.special(sh, c.q, c.k, c.v, np.arange(sh.m_spec))
     got = to_host(gspec).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
     assert_close(got[special_token_ids(sh)], spec, sh.dtype, "grow O_spec")
-    osel = oracle.select(sh, c.q, c.k, c.v, wins, gi)
+    osel = oracle.select(sh, c.q, c.k, c.v, wins, idx)
     oimg = oracle.gate_combine(sh, c.q, c.wg, wins, oc, osel)
     got = to_host(gout).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
-    assert_close(got[window_token_ids(sh)], oimg, sh.dtype, "grow O_img")
+    same = same_sets(gi, idx)
+    assert (~same).sum() <= 2
+    assert_close_rows(got[window_token_ids(sh)], oimg, same, sh.dtype, "grow O_img")
     # dense comparator (the attention kernel's plain mode) on every row
     Q, K, V = (gen.to_f32(x, sh.dtype).astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
                for x in (c.q, c.k, c.v))
