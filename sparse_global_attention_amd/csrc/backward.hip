@@ -19,7 +19,8 @@
 //  * sel_dq_kernel / sel_dkdv_kernel   the selection branch, gathering whole
 //                       windows from blocked copies: the query side walks a
 //                       window's top-k list, the key side walks the inverse
-//                       list (the query windows that selected it);
+//                       list (the query windows that selected it); bf16 chunks
+//                       are transposed in LDS, fp32 ones gathered twice;
 //  * inverse-index, reduction, pooling-backward and dW_g kernels.
 // All sums run in a fixed order, so the gradients are deterministic.
 #include <math.h>
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdParams p) {
   const T* Q = static_cast<const T*>(p.q);
   const T* G = static_cast<const T*>(p.d_o);
   T* doblk = static_cast<T*>(p.doblk) + (win * H + h) * sb * kHeadDim;
-  T* doT = static_cast<T*>(p.doT) + (win * H + h) * kHeadDim * sb;
+  T* doT = p.doT ? static_cast<T*>(p.doT) + (win * H + h) * kHeadDim * sb : nullptr;
   f32x4 acc_doc = {0, 0, 0, 0}, acc_dwg = {0, 0, 0, 0};
   for (int it = 0; 4 * it < sb; ++it) {
     const int kk = 4 * it + tg;
@@ -437,8 +438,10 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdParams p) {
     }
     // blocked copies (padding slots get zeros, L2 = +inf)
     store4(doblk + kk * kHeadDim + ch, ds4);
+    if (p.doT) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) doT[(ch + e) * sb + kk] = from_f32<T>(ds4[e]);
+      for (int e = 0; e < 4; ++e) doT[(ch + e) * sb + kk] = from_f32<T>(ds4[e]);
+    }
     if (cl == 0) {
       p.l2blk[(win * H + h) * sb + kk] = valid ? p.l2sel[u * H + h] : INFINITY;
       p.dblk[(win * H + h) * sb + kk] = valid ? dsel : 0.0f;
@@ -640,6 +643,35 @@ __device__ __forceinline__ void load_trans(uint4 (&dst)[4][BwdChunk<T>::VV], con
     for (int x = 0; x < C::VV; ++x) dst[m][x] = ld16(b + (16 * m + ql) * sb + x * C::VE);
 }
 
+// bf16: the transposed operand of a chunk is built from its rows, already in
+// registers, through a wave-private LDS slab instead of a second gather.  Lane
+// (ql, g) holds rows 8 (ql/4) + 4 tau + ql%4 (tau = 0, 1), channels 16 g .. 16 g
+// + 15; the transposing read (ds_read_b64_tr_b16: within a 16-lane group, lane
+// i gets element i%4 of the 8-byte chunks addressed by lanes 4e + i/4) hands
+// lane i of group g channel 16 m + i of rows 8 g .. 8 g + 7 when lane j of the
+// group addresses row 8 g + j/4 (then + 4), channels 16 m + 4 (j%4).
+constexpr int kSlabStride = kHeadDim + 8;  // bf16 per slab row: 16-byte aligned rows, shifted banks
+constexpr int kSlabElems = 32 * kSlabStride;
+__device__ __forceinline__ void transpose_chunk(const uint4 (&rows)[2][2], uint4 (&tr)[4][1], __bf16* slab, int ql,
+                                                int g) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      st16(slab + (8 * (ql >> 2) + 4 * tau + (ql & 3)) * kSlabStride + 16 * g + 8 * x, rows[tau][x]);
+  // a wave's LDS operations complete in order; the wait keeps the compiler from
+  // moving the transposing reads above the stores
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  const __bf16* r0 = slab + (8 * g + (ql >> 2)) * kSlabStride + 4 * (ql & 3);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bf16x4 lo = lds_read_tr16(r0 + 16 * m);
+    const bf16x4 hi = lds_read_tr16(r0 + 4 * kSlabStride + 16 * m);
+    tr[m][0] = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+__shared__ __attribute__((aligned(16))) __bf16 sel_slab[4][2][kSlabElems];
+
 // Query side: one wave per (window, head, group of QB blocks of 16 queries);
 // per chunk of the window's top-k slots: S^T = K Q^T, P, dP^T = V dO^T,
 // dS, dq^T += K^T dS.  Adds scale * dq into the query rows.
@@ -689,7 +721,10 @@ __global__ __launch_bounds__(256) void sel_dq_kernel(SelBwdParams p) {
     const int64_t gv = (int64_t)ci * 32 + 8 * g;
     ch.jv = topk_entry(tr0, tr1, (int)(gv / sb), K, geo.n_windows);
     ch.kkv0 = (int)(gv % sb);
-    load_trans<T>(ch.t, static_cast<const T*>(p.kT), ch.jv, ch.kkv0, h, H, sb, ql);
+    if constexpr (sizeof(T) == 2)
+      transpose_chunk(ch.x, ch.t, sel_slab[wv][0], ql, g);
+    else
+      load_trans<T>(ch.t, static_cast<const T*>(p.kT), ch.jv, ch.kkv0, h, H, sb, ql);
   };
   auto process = [&](const C& ch) __attribute__((always_inline)) {
 #pragma unroll
@@ -783,8 +818,13 @@ __global__ __launch_bounds__(256) void sel_dkdv_kernel(SelBwdParams p) {
     const int64_t gv = (int64_t)ci * 32 + 8 * g;
     ch.jv = entry(gv / sb);
     ch.kkv0 = (int)(gv % sb);
-    load_trans<T>(ch.t, static_cast<const T*>(p.doT), ch.jv, ch.kkv0, h, H, sb, kl);
-    load_trans<T>(ch.u, static_cast<const T*>(p.qT), ch.jv, ch.kkv0, h, H, sb, kl);
+    if constexpr (sizeof(T) == 2) {
+      transpose_chunk(ch.y, ch.t, sel_slab[wv][0], kl, g);
+      transpose_chunk(ch.x, ch.u, sel_slab[wv][1], kl, g);
+    } else {
+      load_trans<T>(ch.t, static_cast<const T*>(p.doT), ch.jv, ch.kkv0, h, H, sb, kl);
+      load_trans<T>(ch.u, static_cast<const T*>(p.qT), ch.jv, ch.kkv0, h, H, sb, kl);
+    }
     const int64_t lrow = ((int64_t)(ch.jv < 0 ? 0 : ch.jv) * H + h) * sb + ch.kkv0;
 #pragma unroll
     for (int e = 0; e < 8; e += 4) {
@@ -814,21 +854,13 @@ __global__ __launch_bounds__(256) void sel_dkdv_kernel(SelBwdParams p) {
       F::pv(ch.u, ds0, ds1, dk[b]);
     }
   };
-  if (n_chunks > 0) {
-    C A, B;
-    load(A, 0);
-    if (n_chunks > 1) load(B, 1);
-    int ci = 0;
-    for (; ci + 3 < n_chunks; ci += 2) {
-      process(A);
-      load(A, ci + 2);
-      process(B);
-      load(B, ci + 3);
-    }
+  // One chunk in registers at a time (148 VGPRs, three waves per SIMD): the
+  // other waves' gathers hide each wave's load latency; two chunks in flight
+  // per wave would cost the occupancy (one wave per SIMD, 45 % slower).
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    C A;
+    load(A, ci);
     process(A);
-    if (ci + 2 < n_chunks) load(A, ci + 2);
-    if (ci + 1 < n_chunks) process(B);
-    if (ci + 2 < n_chunks) process(A);
   }
 
 #pragma unroll

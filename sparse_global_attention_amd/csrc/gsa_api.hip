@@ -215,10 +215,11 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.qc = take(pooled);
     p.kc = take(pooled);
     p.vc = take(pooled);
+    const int64_t tblk = c.dtype == GSA_BF16 ? 0 : blk;  // transposed copies: fp32 only
     p.qblk = take(blk);
-    p.qT = take(blk);
+    p.qT = take(tblk);
     p.kblk = take(blk);
-    p.kT = take(blk);
+    p.kT = take(tblk);
     p.vrow = take(blk);
     p.vblk = take(blk);
     p.oc = take(wf);
@@ -233,7 +234,7 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.osel = take(imgf);
     p.l2sel = take(g.m_img * g.n_heads * 4);
     p.doblk = take(blk);
-    p.doT = take(blk);
+    p.doT = take(tblk);
     p.l2blk = take(bl);
     p.dblk = take(bl);
     if (c.n_ctx) {
@@ -681,10 +682,11 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
   pp.dst[0] = at(ws, pl.qc);
   pp.dst[1] = at(ws, pl.kc);
   pp.dst[2] = at(ws, pl.vc);
+  // (bf16: the selection backward transposes Q and K chunks in LDS)
   pp.rows[0] = at(ws, pl.qblk);
-  pp.trans[0] = at(ws, pl.qT);
+  pp.trans[0] = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.qT);
   pp.rows[1] = at(ws, pl.kblk);
-  pp.trans[1] = at(ws, pl.kT);
+  pp.trans[1] = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.kT);
   pp.rows[2] = at(ws, pl.vrow);
   pp.trans[2] = at(ws, pl.vblk);
   ok(launch_pool(c.dtype, pp, 3, st));
@@ -760,7 +762,7 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
   gp.g = g;
   gp.dq = dq;
   gp.doblk = at(ws, pl.doblk);
-  gp.doT = at(ws, pl.doT);
+  gp.doT = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.doT);
   gp.l2blk = reinterpret_cast<float*>(at(ws, pl.l2blk));
   gp.dblk = reinterpret_cast<float*>(at(ws, pl.dblk));
   if (c.n_ctx) {

@@ -246,7 +246,7 @@ struct GateBwdParams {
   Geometry g;
   float* dq;           // token rows (float): image rows stored = dz W_g
   void* doblk;         // [M'][H][sb][d] dO_sel rows (dtype)
-  void* doT;           // [M'][H][d][sb] dO_sel transposed (dtype)
+  void* doT;           // [M'][H][d][sb] dO_sel transposed (dtype), or null (bf16: transposed in LDS)
   float* l2blk;        // [M'][H][sb] (+inf on padding)
   float* dblk;         // [M'][H][sb] D_sel = dO_sel . O_sel (0 on padding)
   void* dosel_img;     // optional [M_img][H][d] (dtype)
