@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--grid", type=int, nargs=2, default=None, metavar=("H", "W"), help="override the image grid")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the frame attention, descriptor attention and backward timings")
     ap.add_argument("--cpu-windows", type=int, default=64)
     ap.add_argument("--cpu-special", type=int, default=16)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -222,48 +224,58 @@ def main():
         "wall_s_timed_region": round(t_wall, 3),
         "input_gen_s": round(t_gen, 1),
     }
-    # Frame attention, the dense per-frame step that alternates with GSA in the
-    # aggregation transformer: its time and one alternating pair (frame + GSA).
-    t_frame = timed(lambda: gsa.gsa_frame_attn(cfg, dq, dk, dv, o2, stream=stream), reps)
-    detail["frame_attention"] = {
-        "kernel": "flash_kernel<bf16,4,final>" if sh.dtype == gen.BF16 else "flash_kernel<f32,4,final>",
-        "ms": round(t_frame, 4), "flop": fl["frame"],
-        "tflops": round(fl["frame"] / (t_frame * 1e-3) / 1e12, 2),
-        "frac_mfma_peak": round(fl["frame"] / (t_frame * 1e-3) / 1e12 / peak, 4),
-        "alternating_pair_ms": round(t_frame + ms_step, 4)}
-    # FlashVGGT descriptor attention at the same shape (r = s, keyframes = the
-    # context frames): building the key/value set, then every token over it.
-    n_set = gsa.gsa_descriptor_count(cfg)
-    kd, vd = (torch.empty((n_set, H, d), dtype=dq.dtype, device=dev) for _ in range(2))
-    t_dset = timed(lambda: gsa.gsa_descriptor_set(cfg, dk, dv, kd, vd, stream=stream), reps)
-    t_datt = timed(lambda: gsa.gsa_descriptor_attn(cfg, dq, kd, vd, o2, stream=stream), max(2, reps // 4))
-    datt_flop = 4.0 * sh.m_tokens * n_set * d * H
-    dset_bytes = (2 * sh.n_frames * (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool) * 4
-                  + 2 * (n_set - sh.n_frames * (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool))
-                  + 2 * n_set) * H * d * esz
-    detail["descriptor_attention"] = {
-        "kernels": ["descriptor_kernel", "flash_kernel<bf16,4,final>" if sh.dtype == gen.BF16 else
-                    "flash_kernel<f32,4,final>"],
-        "n_set": n_set, "set_ms": round(t_dset, 4), "set_hbm_gbs": round(dset_bytes / (t_dset * 1e-3) / 1e9, 1),
-        "attn_ms": round(t_datt, 4), "attn_flop": datt_flop,
-        "attn_tflops": round(datt_flop / (t_datt * 1e-3) / 1e12, 2),
-        "attn_frac_mfma_peak": round(datt_flop / (t_datt * 1e-3) / 1e12 / peak, 4)}
-    del kd, vd
-    # Backward of the layer (gradients of q, k, v and W_g for a seeded dO, the
-    # top-k sets of the compressed step above held fixed).  Algorithmic work:
-    # 2.5x the forward attention FLOPs (recomputed scores, dP, dV, dQ, dK).
-    d_o = to_dev(gen.make_output_grad(sh))
-    gq, gk, gv = (torch.empty(sh.qkv_shape, dtype=torch.float32, device=dev) for _ in range(3))
-    gw = torch.empty((H, d), dtype=torch.float32, device=dev)
-    ws_bwd = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_BACKWARD)), dtype=torch.uint8, device=dev)
-    t_bwd = timed(lambda: gsa.gsa_backward(cfg, dq, dk, dv, dwg, idx, d_o, gq, gk, gv, gw, ws_bwd, stream=stream),
-                  max(2, reps // 2))
-    bwd_flop = 2.5 * gsa_flops
-    detail["backward"] = {"ms": round(t_bwd, 4), "flop": bwd_flop,
-                          "tflops": round(bwd_flop / (t_bwd * 1e-3) / 1e12, 2),
-                          "frac_mfma_peak": round(bwd_flop / (t_bwd * 1e-3) / 1e12 / peak, 4),
-                          "workspace_gb": round(ws_bwd.numel() / 1e9, 2)}
-    del d_o, gq, gk, gv, gw, ws_bwd
+    if not args.no_extras:
+        # Frame attention, the dense per-frame step that alternates with GSA in the
+        # aggregation transformer: its time and one alternating pair (frame + GSA).
+        t_frame = timed(lambda: gsa.gsa_frame_attn(cfg, dq, dk, dv, o2, stream=stream), reps)
+        detail["frame_attention"] = {
+            "kernel": "flash_kernel<bf16,4,final>" if sh.dtype == gen.BF16 else "flash_kernel<f32,4,final>",
+            "ms": round(t_frame, 4), "flop": fl["frame"],
+            "tflops": round(fl["frame"] / (t_frame * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(fl["frame"] / (t_frame * 1e-3) / 1e12 / peak, 4),
+            "alternating_pair_ms": round(t_frame + ms_step, 4)}
+        # FlashVGGT descriptor attention at the same shape (r = s, keyframes = the
+        # context frames): building the key/value set, then every token over it.
+        n_set = gsa.gsa_descriptor_count(cfg)
+        kd, vd = (torch.empty((n_set, H, d), dtype=dq.dtype, device=dev) for _ in range(2))
+        t_dset = timed(lambda: gsa.gsa_descriptor_set(cfg, dk, dv, kd, vd, stream=stream), reps)
+        t_datt = timed(lambda: gsa.gsa_descriptor_attn(cfg, dq, kd, vd, o2, stream=stream), max(2, reps // 4))
+        datt_flop = 4.0 * sh.m_tokens * n_set * d * H
+        dset_bytes = (2 * sh.n_frames * (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool) * 4
+                      + 2 * (n_set - sh.n_frames * (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool))
+                      + 2 * n_set) * H * d * esz
+        detail["descriptor_attention"] = {
+            "kernels": ["descriptor_kernel", "flash_kernel<bf16,4,final>" if sh.dtype == gen.BF16 else
+                        "flash_kernel<f32,4,final>"],
+            "n_set": n_set, "set_ms": round(t_dset, 4), "set_hbm_gbs": round(dset_bytes / (t_dset * 1e-3) / 1e9, 1),
+            "attn_ms": round(t_datt, 4), "attn_flop": datt_flop,
+            "attn_tflops": round(datt_flop / (t_datt * 1e-3) / 1e12, 2),
+            "attn_frac_mfma_peak": round(datt_flop / (t_datt * 1e-3) / 1e12 / peak, 4)}
+        del kd, vd
+        # Backward of the layer (gradients of q, k, v and W_g for a seeded dO, the
+        # top-k sets of the compressed step above held fixed).  Algorithmic work:
+        # 2.5x the forward attention FLOPs (recomputed scores, dP, dV, dQ, dK).
+        d_o = to_dev(gen.make_output_grad(sh))
+        gq, gk, gv = (torch.empty(sh.qkv_shape, dtype=torch.float32, device=dev) for _ in range(3))
+        gw = torch.empty((H, d), dtype=torch.float32, device=dev)
+        ws_bwd = torch.empty(max(256, gsa.gsa_workspace_size(cfg, gsa.GSA_OP_BACKWARD)), dtype=torch.uint8, device=dev)
+        t_bwd = timed(lambda: gsa.gsa_backward(cfg, dq, dk, dv, dwg, idx, d_o, gq, gk, gv, gw, ws_bwd, stream=stream),
+                      max(2, reps // 2))
+        # the training pair: the forward saves its state, the backward reads it
+        state = torch.empty(gsa.gsa_train_state_size(cfg), dtype=torch.uint8, device=dev)
+        t_ftr = timed(lambda: gsa.gsa_forward_train(cfg, dq, dk, dv, dwg, o2, state, ws, stream=stream), reps)
+        t_btr = timed(lambda: gsa.gsa_backward_train(cfg, dq, dk, dv, dwg, state, d_o, gq, gk, gv, gw, ws_bwd,
+                                                     stream=stream), max(2, reps // 2))
+        bwd_flop = 2.5 * gsa_flops
+        detail["backward"] = {"ms": round(t_bwd, 4), "flop": bwd_flop,
+                              "tflops": round(bwd_flop / (t_bwd * 1e-3) / 1e12, 2),
+                              "frac_mfma_peak": round(bwd_flop / (t_bwd * 1e-3) / 1e12 / peak, 4),
+                              "workspace_gb": round(ws_bwd.numel() / 1e9, 2),
+                              "train_pair": {"forward_train_ms": round(t_ftr, 4), "backward_train_ms": round(t_btr, 4),
+                                             "step_ms": round(t_ftr + t_btr, 4),
+                                             "backward_tflops": round(bwd_flop / (t_btr * 1e-3) / 1e12, 2),
+                                             "state_gb": round(state.numel() / 1e9, 2)}}
+        del d_o, gq, gk, gv, gw, ws_bwd, state
     del ws_spec, ws_sel, ws_cmp, o2, osel
 
     # ---- dense comparator at the same shape --------------------------------------

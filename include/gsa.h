@@ -180,6 +180,27 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Training pair: the forward saves what the backward needs, so the backward
+ * recomputes only the pooled rows.  The state (gsa_train_state_size bytes,
+ * device memory owned by the caller, 256-byte aligned) holds, in this order
+ * at 256-byte aligned offsets: topk_idx int32 [M'][H][k], O'_comp float
+ * [M'][H][d] and its log-sum-exp float [M'][H] (natural log), the special rows'
+ * outputs float [M_spec][H][d] and log2 softmax denominators float [M_spec][H],
+ * O_sel float [M_img][H][d] and its log2 joint denominators float [M_img][H].
+ * gsa_forward_train writes o exactly as gsa_forward does, plus the state
+ * (workspace: GSA_OP_FORWARD bytes).  gsa_backward_train computes what
+ * gsa_backward computes for the state's top-k sets, from the saved
+ * quantities (workspace: GSA_OP_BACKWARD bytes; the state must come from
+ * gsa_forward_train on the same inputs and config).
+ */
+gsa_status gsa_train_state_size(const gsa_config* cfg, size_t* bytes);
+gsa_status gsa_forward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                             void* o, void* state, void* ws, size_t ws_bytes, void* stream);
+gsa_status gsa_backward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                              const void* state, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dense global attention of all M tokens over all M tokens at the same shape
  * (the attention GSA replaces; benchmark comparator).  Writes every row of o.
  */

@@ -32,7 +32,7 @@ GSA_MAX_CTX_FRAMES = 16
 EXPORTS = ("gsa_workspace_size", "gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn",
            "gsa_special_attn", "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn",
            "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_backward",
-           "gsa_status_string")
+           "gsa_train_state_size", "gsa_forward_train", "gsa_backward_train", "gsa_status_string")
 
 
 class GSAConfig(ctypes.Structure):
@@ -90,6 +90,9 @@ _sig = {
     "gsa_descriptor_set": [_CFG, _P, _P, _P, _P, _P],
     "gsa_descriptor_attn": [_CFG, _P, _P, _P, _P, _P],
     "gsa_backward": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "gsa_train_state_size": [_CFG, ctypes.POINTER(ctypes.c_size_t)],
+    "gsa_forward_train": [_CFG, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "gsa_backward_train": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).argtypes = _args
@@ -201,6 +204,25 @@ def gsa_backward(cfg, q, k, v, wg, topk_idx, d_o, dq, dk, dv, dwg, ws, ws_bytes=
     _check(_lib.gsa_backward(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(topk_idx), _ptr(d_o),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwg), _ptr(ws), wsb, _stream(stream)),
            "gsa_backward")
+
+
+def gsa_train_state_size(cfg) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.gsa_train_state_size(ctypes.byref(cfg), ctypes.byref(out)), "gsa_train_state_size")
+    return out.value
+
+
+def gsa_forward_train(cfg, q, k, v, wg, o, state, ws, ws_bytes=None, stream=None):
+    wsb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(_lib.gsa_forward_train(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(o), _ptr(state),
+                                  _ptr(ws), wsb, _stream(stream)), "gsa_forward_train")
+
+
+def gsa_backward_train(cfg, q, k, v, wg, state, d_o, dq, dk, dv, dwg, ws, ws_bytes=None, stream=None):
+    wsb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(_lib.gsa_backward_train(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(state), _ptr(d_o),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwg), _ptr(ws), wsb, _stream(stream)),
+           "gsa_backward_train")
 
 
 def call_status(fn: str, *args) -> int:

@@ -382,8 +382,10 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
         }
       }
     }
-    if constexpr (MODE == kFlashPartial) {
-      if (hf == 0)
+    // log-sum-exp of the row (natural log); the compressed sweep writes it
+    // only when asked (training state)
+    if constexpr (MODE == kFlashPartial || MODE == kFlashBound) {
+      if (hf == 0 && (MODE == kFlashPartial || p.part_lse))
         p.part_lse[(split * p.n_q + qrow) * p.n_heads + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
     }
   }

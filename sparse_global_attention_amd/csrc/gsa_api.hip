@@ -119,6 +119,30 @@ struct Plan {
       ctx_dq, ctx_dkdv;
 };
 
+// Training state saved by gsa_forward_train for gsa_backward_train.
+struct TrainState {
+  int64_t topk, oc, lse_c, spec_o32, spec_l2, osel, l2sel, total;
+};
+TrainState state_plan(const Call& c) {
+  const Geometry& g = c.g;
+  TrainState t;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  t.topk = take(g.n_windows * g.n_heads * (int64_t)c.topk * 4);
+  t.oc = take(g.n_windows * g.n_heads * kHeadDim * 4);
+  t.lse_c = take(g.n_windows * g.n_heads * 4);
+  t.spec_o32 = take(g.m_spec * g.n_heads * kHeadDim * 4);
+  t.spec_l2 = take(g.m_spec * g.n_heads * 4);
+  t.osel = take(g.m_img * g.n_heads * kHeadDim * 4);
+  t.l2sel = take(g.m_img * g.n_heads * 4);
+  t.total = off;
+  return t;
+}
+
 // Query splits of the key-side backward pass over one context frame: enough
 // workgroups to fill the resident slots, at most one per query tile.
 int ctx_query_splits(const Call& c) {
@@ -292,7 +316,7 @@ void set_rows_identity(FlashParams& f, int64_t n) {
 }
 
 hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void* k, const void* v, void* o,
-                       void* ws, hipStream_t st) {
+                       void* ws, hipStream_t st, float* o32 = nullptr, float* l2 = nullptr) {
   const Geometry& g = c.g;
   if (g.m_spec == 0) return hipSuccess;
   FlashParams f = flash_base(c, q, k, v);
@@ -324,6 +348,8 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
   m.n_heads = (int)g.n_heads;
   m.row_stride = g.n_heads * kHeadDim;
   m.o = o;
+  m.o32 = o32;
+  m.l2 = l2;
   return launch_merge(c.dtype, m, st);
 }
 
@@ -332,7 +358,7 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
 //  2. refine_kernel: theta from the bounds, score-only sweep collecting the
 //     keys >= theta, ranking -> topk.
 hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const void* kc, const void* vc, float* oc,
-                          int32_t* idx, float* score, void* ws, hipStream_t st) {
+                          int32_t* idx, float* score, void* ws, hipStream_t st, float* lse = nullptr) {
   const Geometry& g = c.g;
   if (g.n_windows == 0) return hipSuccess;
   FlashParams f = flash_base(c, qc, kc, vc);
@@ -341,6 +367,7 @@ hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const v
   f.kbeg[0] = 0;
   f.kend[0] = g.n_windows;
   f.oc = oc;
+  f.part_lse = lse;
   f.wins_per_frame = g.wpf;
   f.n_excl = c.exclude ? c.n_ctx : 0;
   for (int i = 0; i < f.n_excl; ++i) f.excl_frames[i] = c.ctx[i];
@@ -523,16 +550,25 @@ gsa_status gsa_gate_combine(const gsa_config* cfg, const void* q, const void* wg
   return hip_status(launch_combine(c.dtype, p, static_cast<hipStream_t>(stream)));
 }
 
-gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg, void* o,
-                       void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gsa_forward and gsa_forward_train (state: the training state, or null).
+gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg, void* o,
+                        void* state, void* ws, size_t ws_bytes, void* stream) {
   Call c;
   gsa_status s = check_cfg(cfg, &c);
   if (s != GSA_OK) return s;
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(wg) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
   if (o == q || o == k || o == v) return GSA_ERR_INVALID_ARG;
+  if (state && (((uintptr_t)state & (kAlign - 1)) != 0 || state == q || state == k || state == v || state == o))
+    return GSA_ERR_INVALID_ARG;
   Plan pl = make_plan(c, GSA_OP_FORWARD);
   if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const TrainState ts = state_plan(c);
+  auto saved = [&](int64_t off) { return state ? reinterpret_cast<float*>(at(state, off)) : nullptr; };
 
   // 1. pooling of Q/K/V plus the blocked K / transposed-V copies for the gather
   PoolParams pp = pool_base(c);
@@ -547,11 +583,12 @@ gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, cons
   pp.first_tensor = 0;
   hipError_t e = launch_pool(c.dtype, pp, 3, st);
   // 2. special tokens over all tokens
-  if (e == hipSuccess) e = run_special(c, pl, q, k, v, o, ws, st);
+  if (e == hipSuccess) e = run_special(c, pl, q, k, v, o, ws, st, saved(ts.spec_o32), saved(ts.spec_l2));
   // 3. compressed attention + top-k
-  float* oc = reinterpret_cast<float*>(at(ws, pl.oc));
-  int32_t* idx = reinterpret_cast<int32_t*>(at(ws, pl.topk));
-  if (e == hipSuccess) e = run_compressed(c, pl, pp.dst[0], pp.dst[1], pp.dst[2], oc, idx, nullptr, ws, st);
+  float* oc = state ? saved(ts.oc) : reinterpret_cast<float*>(at(ws, pl.oc));
+  int32_t* idx = reinterpret_cast<int32_t*>(state ? at(state, ts.topk) : at(ws, pl.topk));
+  if (e == hipSuccess)
+    e = run_compressed(c, pl, pp.dst[0], pp.dst[1], pp.dst[2], oc, idx, nullptr, ws, st, saved(ts.lse_c));
   // 4. fixed-context partial
   if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
   // 5. selection + upsample + gate
@@ -560,9 +597,35 @@ gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, cons
     sp.wg = wg;
     sp.oc = oc;
     sp.o = o;
+    sp.osel = saved(ts.osel);
+    sp.l2 = saved(ts.l2sel);
     e = launch_select(c.dtype, sp, st);
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg, void* o,
+                       void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(cfg, q, k, v, wg, o, nullptr, ws, ws_bytes, stream);
+}
+
+gsa_status gsa_train_state_size(const gsa_config* cfg, size_t* bytes) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!bytes) return GSA_ERR_INVALID_ARG;
+  *bytes = (size_t)state_plan(c).total;
+  return GSA_OK;
+}
+
+gsa_status gsa_forward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                             void* o, void* state, void* ws, size_t ws_bytes, void* stream) {
+  if (state == nullptr) return GSA_ERR_INVALID_ARG;
+  return forward_impl(cfg, q, k, v, wg, o, state, ws, ws_bytes, stream);
 }
 
 gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, const void* v, void* o, void* ws,
@@ -647,12 +710,24 @@ gsa_status gsa_descriptor_attn(const gsa_config* cfg, const void* q, const void*
   return hip_status(launch_flash(c.dtype, kFlashFinal, f, static_cast<hipStream_t>(stream)));
 }
 
-gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
-                        const int32_t* topk_idx, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
-                        void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gsa_backward (state null: the forward quantities are recomputed) and
+// gsa_backward_train (top-k sets and forward quantities read from the state).
+gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                         const int32_t* topk_idx, const void* state, const void* d_o, float* dq, float* dk,
+                         float* dv, float* dwg, void* ws, size_t ws_bytes, void* stream) {
   Call c;
   gsa_status s = check_cfg(cfg, &c);
   if (s != GSA_OK) return s;
+  const TrainState ts = state_plan(c);
+  if (state) {
+    if (((uintptr_t)state & (kAlign - 1)) != 0) return GSA_ERR_INVALID_ARG;
+    topk_idx = reinterpret_cast<const int32_t*>(at(const_cast<void*>(state), ts.topk));
+  }
+  auto saved = [&](int64_t off) { return reinterpret_cast<float*>(at(const_cast<void*>(state), off)); };
   const void* in[6] = {q, k, v, wg, topk_idx, d_o};
   const void* out[4] = {dq, dk, dv, dwg};
   for (const void* x : in)
@@ -663,6 +738,7 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
       if (x == out[i]) return GSA_ERR_INVALID_ARG;
     for (int j = 0; j < i; ++j)
       if (out[j] == out[i]) return GSA_ERR_INVALID_ARG;
+    if (state && out[i] == state) return GSA_ERR_INVALID_ARG;
   }
   const Geometry& g = c.g;
   if (g.n_windows * g.n_heads * (int64_t)c.topk > INT32_MAX) return GSA_ERR_SHAPE;
@@ -688,13 +764,13 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
   pp.rows[1] = at(ws, pl.kblk);
   pp.trans[1] = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.kT);
   pp.rows[2] = at(ws, pl.vrow);
-  pp.trans[2] = at(ws, pl.vblk);
+  pp.trans[2] = state ? nullptr : at(ws, pl.vblk);  // V^T only for the selection recompute
   ok(launch_pool(c.dtype, pp, 3, st));
 
   // 2. forward quantities: compressed output + log-sum-exp (one split)
-  float* oc = reinterpret_cast<float*>(at(ws, pl.oc));
-  float* lse_c = reinterpret_cast<float*>(at(ws, pl.lse_c));
-  if (g.n_windows) {
+  float* oc = state ? saved(ts.oc) : reinterpret_cast<float*>(at(ws, pl.oc));
+  float* lse_c = state ? saved(ts.lse_c) : reinterpret_cast<float*>(at(ws, pl.lse_c));
+  if (g.n_windows && !state) {
     FlashParams f = flash_base(c, at(ws, pl.qc), at(ws, pl.kc), at(ws, pl.vc));
     set_rows_identity(f, g.n_windows);
     f.n_splits = 1;
@@ -705,11 +781,35 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
     ok(launch_flash(c.dtype, kFlashPartial, f, st));
   }
   //    special rows: merged output in float, L2 and D = dO . O
-  float* spec_o32 = reinterpret_cast<float*>(at(ws, pl.spec_o32));
-  float* spec_l2 = reinterpret_cast<float*>(at(ws, pl.spec_l2));
+  float* spec_o32 = state ? saved(ts.spec_o32) : reinterpret_cast<float*>(at(ws, pl.spec_o32));
+  float* spec_l2 = state ? saved(ts.spec_l2) : reinterpret_cast<float*>(at(ws, pl.spec_l2));
   float* spec_dd = reinterpret_cast<float*>(at(ws, pl.spec_dd));
   FlashParams fs = flash_base(c, q, k, v);
-  if (g.m_spec) {
+  if (g.m_spec && state) {
+    // the split layout of the key-range sweep, and D = dO . O from the saved rows
+    // (a one-part merge: weight 1, the part itself)
+    const int ns = pl.n_split;
+    const int64_t tiles = (g.m_tokens + 31) / 32;
+    fs.n_splits = ns;
+    for (int i = 0; i < ns; ++i) {
+      fs.kbeg[i] = tiles * i / ns * 32;
+      fs.kend[i] = i + 1 == ns ? g.m_tokens : tiles * (i + 1) / ns * 32;
+    }
+    MergeParams m;
+    memset(&m, 0, sizeof(m));
+    m.part_o = spec_o32;
+    m.part_lse = spec_l2;
+    m.n_splits = 1;
+    m.n_q = g.m_spec;
+    m.qa = g.n_special;
+    m.qb = g.tf;
+    m.qc = 0;
+    m.n_heads = (int)H;
+    m.row_stride = H * kHeadDim;
+    m.d_o = d_o;
+    m.dd = spec_dd;
+    ok(launch_merge(c.dtype, m, st));
+  } else if (g.m_spec) {
     fs.n_q = g.m_spec;
     fs.qa = g.n_special;
     fs.qb = g.tf;
@@ -742,13 +842,15 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
     ok(launch_merge(c.dtype, m, st));
   }
   //    selection output and joint L2 (context partials first)
-  float* osel = reinterpret_cast<float*>(at(ws, pl.osel));
-  float* l2sel = reinterpret_cast<float*>(at(ws, pl.l2sel));
-  if (c.n_ctx && e == hipSuccess) ok(run_context(c, pl, q, k, v, ws, st));
-  SelectParams sp = select_base(c, pl, q, topk_idx, ws);
-  sp.osel = osel;
-  sp.l2 = l2sel;
-  ok(launch_select(c.dtype, sp, st));
+  float* osel = state ? saved(ts.osel) : reinterpret_cast<float*>(at(ws, pl.osel));
+  float* l2sel = state ? saved(ts.l2sel) : reinterpret_cast<float*>(at(ws, pl.l2sel));
+  if (!state) {
+    if (c.n_ctx && e == hipSuccess) ok(run_context(c, pl, q, k, v, ws, st));
+    SelectParams sp = select_base(c, pl, q, topk_idx, ws);
+    sp.osel = osel;
+    sp.l2 = l2sel;
+    ok(launch_select(c.dtype, sp, st));
+  }
 
   // 3. gate: dq (image rows) = dz W_g, dO_sel blocks, dO_comp, dW_g partials
   GateBwdParams gp;
@@ -981,6 +1083,23 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
   pb.dv = dv;
   ok(launch_pool_bwd(pb, st));
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                        const int32_t* topk_idx, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return backward_impl(cfg, q, k, v, wg, topk_idx, nullptr, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream);
+}
+
+gsa_status gsa_backward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                              const void* state, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
+                              void* ws, size_t ws_bytes, void* stream) {
+  if (state == nullptr) return GSA_ERR_INVALID_ARG;
+  return backward_impl(cfg, q, k, v, wg, nullptr, state, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -90,7 +90,7 @@ struct FlashParams {
   // kFlashPartial: part_o [split][n_q][H][d] (normalised), part_lse [split][n_q][H] (natural log)
   float* part_o;
   float* part_lse;
-  // kFlashBound: oc [n_q][H][d] fp32
+  // kFlashBound: oc [n_q][H][d] fp32 (and, if part_lse is set, the rows' log-sum-exp there)
   float* oc;
   int64_t wins_per_frame;
   int n_excl;                 // frames whose windows are not top-k candidates
@@ -153,8 +153,8 @@ struct SelectParams {
   int n_ctx;            // context partials (one per context frame), 0 if none
   const float* ctx_o;   // [n_ctx][M_img][H][d] (normalised)
   const float* ctx_lse; // [n_ctx][M_img][H] log-sum-exp
-  float* osel;          // standalone output [M_img][H][d]
-  float* l2;            // standalone, optional: [M_img][H] log2 of the joint softmax denominator
+  float* osel;          // standalone output [M_img][H][d]; fused path: optional copy of O_sel
+  float* l2;            // optional: [M_img][H] log2 of the joint softmax denominator
   const void* wg;       // fused epilogue: gate projection [H][d]
   const float* oc;      // fused epilogue: compressed output [M'][H][d]
   void* o;              // fused epilogue: output rows in the token layout

@@ -225,13 +225,14 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
           }
         }
       }
-    } else if (qvalid) {
+    }
+    if (p.osel && qvalid) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         *reinterpret_cast<f32x4*>(p.osel + (u * H + h) * kHeadDim + 16 * m + 4 * g) = res[m];
-      // log2 of the joint denominator: sum of exp2(c s) over all keys = den 2^mm
-      if (p.l2 && g == 0) p.l2[u * H + h] = den > 0.0f ? mm + log2f(den) : INFINITY;
     }
+    // log2 of the joint denominator: sum of exp2(c s) over all keys = den 2^mm
+    if (p.l2 && g == 0 && qvalid) p.l2[u * H + h] = den > 0.0f ? mm + log2f(den) : INFINITY;
     }
   }
 }

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     for want in ("gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn", "gsa_special_attn",
                  "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn", "gsa_workspace_size",
                  "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_backward",
-                 "gsa_status_string"):
+                 "gsa_train_state_size", "gsa_forward_train", "gsa_backward_train", "gsa_status_string"):
         assert want in fns
 
 
@@ -146,6 +146,21 @@ def test_workspace_validation(lib):
     bw = [A + 16 * i for i in range(6)] + [o, o + 4096, o + 8192, o + 12288]
     assert lib.call_status("gsa_backward", c, *bw, A, need - 1, None) == 4
     assert lib.call_status("gsa_backward", c, *bw, None, need, None) == 1
+    # the training pair: a null, misaligned or aliased state is rejected before any launch
+    need_f = lib.gsa_workspace_size(cc, lib.GSA_OP_FORWARD)
+    st = A + (1 << 24)
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, None, A, need_f, None) == 1
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st + 16, A, need_f, None) == 1
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, o, A, need_f, None) == 1
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st, A, need_f - 1, None) == 4
+    tr = [A, A + 16, A + 32, A + 48, st, A + 64, o, o + 4096, o + 8192, o + 12288]
+    assert lib.call_status("gsa_backward_train", c, *tr, A, need - 1, None) == 4
+    tr[4] = None
+    assert lib.call_status("gsa_backward_train", c, *tr, A, need, None) == 1
+    tr[4] = o  # the state aliasing dq
+    assert lib.call_status("gsa_backward_train", c, *tr, A, need, None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.call_status("gsa_train_state_size", c, ctypes.byref(n)) == 0 and n.value > 0
     assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, o, o + 4096, None, None, need, None) == 1
 
 

@@ -146,3 +146,58 @@ def test_backward_full_size_sum_identities(sh):
     torch.cuda.synchronize()
     for x, y in zip(first, (dq_, dk_, dv_, dwg_)):
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+# ---- the training pair: forward saving its state, backward reading it ----------
+
+TRAIN_SHAPES = ["tiny_f32", "odd_bf16", "mid_bf16", "s8", "s5", "p0", "ctx", "ctx_f32", "k40"]
+
+
+def train_pair(sh, q, k, v, wg, d_o):
+    cfg = gsa.GSAConfig.from_shape(sh)
+    dq, dk, dv, dw = (to_dev(x, sh.dtype) for x in (q, k, v, wg))
+    o = torch.zeros(sh.qkv_shape, dtype=dq.dtype, device=DEV)
+    state = torch.empty(gsa.gsa_train_state_size(cfg), dtype=torch.uint8, device=DEV)
+    gsa.gsa_forward_train(cfg, dq, dk, dv, dw, o, state, workspace(cfg, gsa.GSA_OP_FORWARD))
+    grads = [torch.empty(sh.qkv_shape, dtype=torch.float32, device=DEV) for _ in range(3)]
+    grads.append(torch.empty((sh.n_heads, sh.head_dim), dtype=torch.float32, device=DEV))
+    gsa.gsa_backward_train(cfg, dq, dk, dv, dw, state, to_dev(d_o, sh.dtype), *grads,
+                           workspace(cfg, gsa.GSA_OP_BACKWARD))
+    torch.cuda.synchronize()
+    idx = state[:sh.n_windows * sh.n_heads * sh.topk * 4].view(torch.int32).view(sh.n_windows, sh.n_heads, sh.topk)
+    return o, idx, grads
+
+
+@pytest.mark.parametrize("name", TRAIN_SHAPES)
+def test_training_pair(name):
+    """gsa_forward_train writes gsa_forward's output bit for bit and the top-k sets
+    of gsa_compressed_attn_topk; gsa_backward_train equals gsa_backward on those
+    sets (the only difference: the compressed output and its log-sum-exp come
+    from the forward's bound sweep instead of a plain sweep, a rounding-level
+    change); and, where the forward's sets equal the oracle's for every
+    (window, head), the gradients match the oracle's."""
+    from gsa_testlib import Case, same_sets
+    sh = SHAPES[name]
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    o, idx, grads = train_pair(sh, q, k, v, wg, d_o)
+    c = Case(sh, q=q, k=k, v=v, wg=wg)
+    assert torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o,
+                       (lambda x: x.view(torch.int16) if x.dtype == torch.bfloat16 else x)(c.forward()))
+    qc, kc, vc = c.pool()
+    _, idx_c, _ = c.compressed(qc, kc, vc, with_scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_c)
+    gidx = idx.cpu().numpy()
+    ref_gpu = gpu_backward(sh, q, k, v, wg, gidx, d_o)
+    for g_, r_, what in zip(grads, ref_gpu, ("dq", "dk", "dv", "dwg")):
+        g_, r_ = g_.cpu().numpy().astype(np.float64), r_.cpu().numpy().astype(np.float64)
+        scale = max(np.abs(r_).max(), 1e-30)
+        tol = 1e-5 if sh.dtype == F32 else 2e-3
+        assert np.abs(g_ - r_).max() <= tol * scale, (name, what, np.abs(g_ - r_).max() / scale)
+    oidx = oracle_topk(sh, q, k)
+    if not same_sets(gidx, oidx).all():
+        pytest.skip(f"{name}: the forward's top-k sets differ from the oracle's within the tie band")
+    ref = oracle.backward(sh, q, k, v, wg, oidx, d_o)
+    for g_, r_, what in zip(grads, ref, ("dq", "dk", "dv", "dwg")):
+        assert_grad_close(g_.cpu().numpy().reshape(r_.shape), r_, sh.dtype, f"{name} train {what}")
