@@ -808,7 +808,14 @@ __global__ __launch_bounds__(256) void sel_dkdv_kernel(SelBwdParams p) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) dk[b][m] = dv[b][m] = f32x4{0, 0, 0, 0};
   }
-  auto entry = [&](int64_t w) __attribute__((always_inline)) { return w < n_list ? list[w] : -1; };
+  // The list is read 64 entries at a time into one register per lane; the
+  // chunks then take their window ids from it with a lane permute (a chunk's
+  // windows never straddle two batches: 64 sb slots is a multiple of 32), so
+  // the gathers do not wait on a dependent global load.
+  int lent = -1;
+  auto entry = [&](int64_t w) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_bpermute((int)(w & 63) << 2, lent);
+  };
   auto load = [&](C& ch, int ci) __attribute__((always_inline)) {
     const int64_t ga = (int64_t)ci * 32 + 8 * (kl >> 2);
     const int ja = entry(ga / sb);
@@ -857,7 +864,14 @@ __global__ __launch_bounds__(256) void sel_dkdv_kernel(SelBwdParams p) {
   // One chunk in registers at a time (148 VGPRs, three waves per SIMD): the
   // other waves' gathers hide each wave's load latency; two chunks in flight
   // per wave would cost the occupancy (one wave per SIMD, 45 % slower).
+  int batch = -1;
   for (int ci = 0; ci < n_chunks; ++ci) {
+    const int b = (int)(((int64_t)ci * 32 / sb) >> 6);
+    if (b != batch) {  // uniform across the wave
+      batch = b;
+      const int64_t w = (int64_t)b * 64 + lane;
+      lent = w < n_list ? list[w] : -1;
+    }
     C A;
     load(A, ci);
     process(A);
