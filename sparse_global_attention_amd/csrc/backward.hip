@@ -569,19 +569,57 @@ __global__ __launch_bounds__(256) void inv_fill_kernel(InvParams p) {
 // One wave per list: each element's position is its rank (ties by fill
 // position, so repeated entries keep distinct slots); the result does not
 // depend on the order the fill kernel's atomics took.
+// Lists of 65 .. kSortMax entries are sorted by a bitonic network in a
+// wave-private LDS buffer (padded to a power of two); shorter and longer
+// lists by rank: the list is compared in chunks of 64 entries (one per
+// lane, loaded once) whose values are broadcast lane by lane (n^2 / 64
+// register compares per lane).  Equal entries are equal values, so every
+// method gives the same list.
+constexpr int kSortMax = 2048;
+__shared__ int32_t sort_buf[4][kSortMax];
 __global__ __launch_bounds__(256) void inv_sort_kernel(InvParams p) {
   const int64_t seg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (seg >= p.n_windows * p.n_heads) return;
+  if (seg >= p.n_windows * p.n_heads) return;  // whole waves
   const int lane = lane_id();
   const int32_t b = p.off[seg], n = p.off[seg + 1] - b;
-  for (int e = lane; e < n; e += 64) {
-    const int32_t x = p.raw[b + e];
-    int32_t rank = 0;
-    for (int f = 0; f < n; ++f) {
-      const int32_t y = p.raw[b + f];
-      rank += (y < x || (y == x && f < e)) ? 1 : 0;
+  if (n > 64 && n <= kSortMax) {
+    int32_t* a = sort_buf[threadIdx.x >> 6];
+    int N = 128;
+    while (N < n) N <<= 1;
+    for (int i = lane; i < N; i += 64) a[i] = i < n ? p.raw[b + i] : INT32_MAX;
+    // the wave's LDS operations complete in order; the waits keep the
+    // compiler from moving a stage's reads above the previous stage's writes
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    for (int k = 2; k <= N; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int t = lane; t < N / 2; t += 64) {
+          const int i = 2 * j * (t / j) + t % j, l = i + j;  // i has bit j clear
+          const int32_t x = a[i], y = a[l];
+          if ((x > y) == ((i & k) == 0)) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+      }
     }
-    p.list[b + rank] = x;
+    for (int i = lane; i < n; i += 64) p.list[b + i] = a[i];
+    return;
+  }
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane;
+    const int32_t x = e < n ? p.raw[b + e] : 0;
+    int32_t rank = 0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int32_t y = c0 + lane < n ? p.raw[b + c0 + lane] : INT32_MAX;
+      const int m = n - c0 < 64 ? n - c0 : 64;
+#pragma unroll 8
+      for (int f = 0; f < m; ++f) {
+        const int32_t yf = __builtin_amdgcn_readlane(y, f);
+        rank += (yf < x || (yf == x && c0 + f < e)) ? 1 : 0;
+      }
+    }
+    if (e < n) p.list[b + rank] = x;
   }
 }
 

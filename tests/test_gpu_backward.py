@@ -201,3 +201,44 @@ def test_training_pair(name):
     ref = oracle.backward(sh, q, k, v, wg, oidx, d_o)
     for g_, r_, what in zip(grads, ref, ("dq", "dk", "dv", "dwg")):
         assert_grad_close(g_.cpu().numpy().reshape(r_.shape), r_, sh.dtype, f"{name} train {what}")
+
+
+def test_backward_with_repeated_and_missing_windows():
+    """Caller-supplied top-k lists may repeat a window (its keys then enter the
+    softmax twice, as in the forward) and hold -1 or out-of-range entries
+    (skipped); the key side's inverse lists keep both copies.  Both sides get the
+    same lists."""
+    sh = SHAPES["odd_bf16"]
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    idx = oracle_topk(sh, q, k).copy()
+    idx[:, :, 1] = idx[:, :, 0]        # a repeated window in every list
+    idx[::2, :, 3] = -1                # missing entries
+    idx[1::3, 0, 4] = sh.n_windows + 7  # out of range: skipped
+    ref_idx = np.where(idx >= sh.n_windows, -1, idx).astype(np.int32)
+    got = [x.cpu().numpy() for x in gpu_backward(sh, q, k, v, wg, idx, d_o)]
+    ref = oracle.backward(sh, q, k, v, wg, ref_idx, d_o)
+    for g_, r_, what in zip(got, ref, ("dq", "dk", "dv", "dwg")):
+        assert_grad_close(g_.reshape(r_.shape), r_, sh.dtype, f"repeated/missing {what}")
+
+
+@pytest.mark.parametrize("sh", [
+    GSAShape("longlists 10f-16x16-h2-s4-k8", 10, 1, 16, 16, 2, 64, 4, 8, BF16, seed=43),
+    GSAShape("longlists 9f-16x16-h1-s1-k4", 9, 1, 16, 16, 1, 64, 1, 4, BF16, seed=44),
+], ids=["lists160", "lists2304"])
+def test_backward_long_inverse_lists(sh):
+    """Every image key row identical: all guide scores tie, every query window
+    selects the k lowest windows, and each of those is on the inverse list of
+    every query window -- 160 entries (sorted in LDS) or 2304 (beyond the LDS
+    sort, ranked), where the seeded lists hold about k."""
+    q, k, v, wg = gen.make_inputs(sh)
+    K = k.reshape(sh.n_frames, sh.tokens_per_frame, -1)
+    K[:, sh.n_special:] = K[0, sh.n_special]
+    k = K.reshape(sh.qkv_shape)
+    d_o = gen.make_output_grad(sh)
+    idx = oracle_topk(sh, q, k)
+    assert np.all(idx[..., :sh.topk] == np.arange(sh.topk))
+    got = [x.cpu().numpy() for x in gpu_backward(sh, q, k, v, wg, idx, d_o)]
+    ref = oracle.backward(sh, q, k, v, wg, idx, d_o)
+    for g_, r_, what in zip(got, ref, ("dq", "dk", "dv", "dwg")):
+        assert_grad_close(g_.reshape(r_.shape), r_, sh.dtype, f"{sh.name} {what}")
