@@ -59,6 +59,7 @@ def _load():
         lib.orc_special.argtypes = [cfgp, P, P, P, P, I64, P]
         lib.orc_frame.argtypes = [cfgp, P, P, P, P, I64, P]
         lib.orc_backward.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, P, P, P, P, P]
+        lib.orc_backward_dq_rows.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, P, P, I64, P]
         lib.orc_descriptor_count.argtypes = [cfgp]
         lib.orc_descriptor_count.restype = I64
         lib.orc_descriptor_set.argtypes = [cfgp, P, P]
@@ -69,7 +70,7 @@ def _load():
         lib.orc_gate_combine.argtypes = [cfgp, P, P, P, P, I64, P, P, P]
         lib.orc_window_token.argtypes = [cfgp, I64, ctypes.c_int]
         lib.orc_window_token.restype = I64
-        for f in ("orc_pool", "orc_special", "orc_frame", "orc_backward", "orc_descriptor_set", "orc_descriptor_attn", "orc_compressed", "orc_guide_scores", "orc_select",
+        for f in ("orc_pool", "orc_special", "orc_frame", "orc_backward", "orc_backward_dq_rows", "orc_descriptor_set", "orc_descriptor_attn", "orc_compressed", "orc_guide_scores", "orc_select",
                   "orc_gate_combine"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -121,6 +122,17 @@ def backward(sh, q, k, v, wg, idx: np.ndarray, d_o):
     _load().orc_backward(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(wg), _p(idx), idx.shape[-1],
                          _p(np.ascontiguousarray(d_o)), _p(dq), _p(dk), _p(dv), _p(dwg))
     return dq, dk, dv, dwg
+
+
+def backward_dq_rows(sh, q, k, v, wg, idx: np.ndarray, d_o, rows: np.ndarray) -> np.ndarray:
+    """dq of the listed token rows (backward with the top-k sets fixed at idx), one row at a
+    time, for workloads too large for the whole layer -> [n][H][d] float64."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
+    _load().orc_backward_dq_rows(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(wg), _p(idx), idx.shape[-1],
+                                 _p(np.ascontiguousarray(d_o)), _p(rows), rows.size, _p(out))
+    return out
 
 
 def frame(sh, q, k, v, rows: np.ndarray) -> np.ndarray:

@@ -590,6 +590,137 @@ void orc_backward(const orc_cfg* c, const void* q, const void* k, const void* v,
   free(Oc);
 }
 
+/* dq contribution of one query row (head h) attending the listed token rows
+ * of k/v (dtype arrays): adds scale * sum_j P_j (dO . v_j - D) k_j to o. */
+static void dq_over_rows(const orc_cfg* c, const void* k, const void* v, int h, double sc, const double* qrow,
+                         const double* dorow, const int64_t* rows, int64_t n, double* P, double* dP, double* o) {
+  const int d = c->head_dim;
+  double mx = -INFINITY, den = 0.0, D = 0.0;
+  for (int64_t u = 0; u < n; ++u) {
+    double s = 0.0;
+    for (int e = 0; e < d; ++e) s += qrow[e] * elem(k, c->dtype, row_off(c, rows[u], h) + e);
+    P[u] = sc * s;
+    if (P[u] > mx) mx = P[u];
+  }
+  for (int64_t u = 0; u < n; ++u) {
+    P[u] = exp(P[u] - mx);
+    den += P[u];
+  }
+  for (int64_t u = 0; u < n; ++u) {
+    P[u] /= den;
+    double dp = 0.0;
+    for (int e = 0; e < d; ++e) dp += dorow[e] * elem(v, c->dtype, row_off(c, rows[u], h) + e);
+    dP[u] = dp;
+    D += P[u] * dp;
+  }
+  for (int64_t u = 0; u < n; ++u) {
+    const double ds = P[u] * (dP[u] - D);
+    for (int e = 0; e < d; ++e) o[e] += sc * ds * elem(k, c->dtype, row_off(c, rows[u], h) + e);
+  }
+}
+
+/* dq of the listed token rows only (the same definition as orc_backward,
+ * evaluated per row, for workloads too large for the whole layer): a
+ * special row's attention backward over all M tokens; an image row's gate
+ * term, its selection backward (with fixed idx and the context frames), and
+ * 1/s^2 of its window's row of the compressed-attention backward (dO_comp of
+ * the window summed from its s^2 tokens).  rows are token ids; out: [n][H][d]. */
+void orc_backward_dq_rows(const orc_cfg* c, const void* q, const void* k, const void* v, const void* wg,
+                          const int32_t* idx, int kcols, const void* d_o, const int64_t* rows, int64_t n,
+                          double* out) {
+  const int H = c->n_heads, d = c->head_dim, s2 = c->pool * c->pool;
+  const int64_t M = n_tokens(c), tf = tokens_per_frame(c), nw = n_windows(c);
+  const double sc = scale_of(c);
+  const size_t nwel = (size_t)nw * H * d;
+  /* pooled rows, rounded as in the forward, widened to double */
+  float* pooled = (float*)malloc(sizeof(float) * nwel);
+  double* pq[3];
+  const void* src[3] = {q, k, v};
+  for (int x = 0; x < 3; ++x) {
+    pq[x] = (double*)malloc(sizeof(double) * nwel);
+    orc_pool(c, src[x], pooled);
+    for (size_t i = 0; i < nwel; ++i) pq[x][i] = pooled[i];
+  }
+  free(pooled);
+  const int64_t cap = (M > nw ? M : nw) + (int64_t)kcols * s2;
+#pragma omp parallel
+  {
+    int64_t* krows = (int64_t*)malloc(sizeof(int64_t) * cap);
+    double* P = (double*)malloc(sizeof(double) * cap);
+    double* dP = (double*)malloc(sizeof(double) * cap);
+    double qrow[512], grow[512], osel[512], oc[512], doc[512], dqc[512], dosel[512];
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t ih = 0; ih < n * H; ++ih) {
+      const int64_t t = rows[ih / H];
+      const int h = (int)(ih % H);
+      double* o = out + ih * d;
+      for (int e = 0; e < d; ++e) {
+        qrow[e] = elem(q, c->dtype, row_off(c, t, h) + e);
+        grow[e] = elem(d_o, c->dtype, row_off(c, t, h) + e);
+        o[e] = 0.0;
+      }
+      const int64_t f = t / tf, p = t % tf;
+      if (p < c->n_special) {  /* special row: attention over all M tokens */
+        for (int64_t u = 0; u < M; ++u) krows[u] = u;
+        dq_over_rows(c, k, v, h, sc, qrow, grow, krows, M, P, dP, o);
+        continue;
+      }
+      /* image row of window i */
+      const int64_t pix = p - c->n_special, y = pix / c->grid_w, x = pix % c->grid_w;
+      const int64_t i = f * windows_per_frame(c) + (y / c->pool) * windows_x(c) + x / c->pool;
+      /* O'_comp of window i, the gates of its tokens, dO_comp of window i */
+      for (int64_t j = 0; j < nw; ++j) krows[j] = j;
+      softmax_weights(d, H, h, sc, pq[0] + (i * H + h) * d, pq[1], krows, nw, P);
+      weighted_values(d, H, h, pq[2], krows, nw, P, oc);
+      double g_t = 0.0;
+      for (int e = 0; e < d; ++e) doc[e] = 0.0;
+      for (int kk = 0; kk < s2; ++kk) {
+        const int64_t tt = window_token(c, i, kk);
+        double z = 0.0;
+        for (int e = 0; e < d; ++e)
+          z += elem(wg, c->dtype, (int64_t)h * d + e) * elem(q, c->dtype, row_off(c, tt, h) + e);
+        const double g = 1.0 / (1.0 + exp(-z));
+        if (tt == t) g_t = g;
+        for (int e = 0; e < d; ++e) doc[e] += g * elem(d_o, c->dtype, row_off(c, tt, h) + e);
+      }
+      /* row i of the compressed-attention backward: dQc_i (P still holds row i's weights) */
+      for (int e = 0; e < d; ++e) dqc[e] = 0.0;
+      double D = 0.0;
+      for (int64_t j = 0; j < nw; ++j) {
+        dP[j] = dot_d(doc, pq[2] + (j * H + h) * d, d);
+        D += P[j] * dP[j];
+      }
+      for (int64_t j = 0; j < nw; ++j) {
+        const double ds = P[j] * (dP[j] - D);
+        for (int e = 0; e < d; ++e) dqc[e] += sc * ds * pq[1][(j * H + h) * d + e];
+      }
+      /* the row's selection set (+ context) and O_sel */
+      int64_t nt = 0;
+      for (int tt = 0; tt < kcols; ++tt) {
+        const int32_t j = idx[(i * H + h) * kcols + tt];
+        if (j < 0) continue;
+        for (int kk = 0; kk < s2; ++kk) krows[nt++] = window_token(c, j, kk);
+      }
+      for (int cf = 0; cf < c->n_ctx; ++cf)
+        for (int64_t pp = 0; pp < tf; ++pp) krows[nt++] = (int64_t)c->ctx_frames[cf] * tf + pp;
+      attend_tokens(c, qrow, k, v, krows, nt, h, P, osel);
+      /* gate term, pooled term, selection term */
+      double dg = 0.0;
+      for (int e = 0; e < d; ++e) dg += grow[e] * (oc[e] - osel[e]);
+      const double dz = dg * g_t * (1.0 - g_t);
+      for (int e = 0; e < d; ++e) {
+        o[e] += dz * elem(wg, c->dtype, (int64_t)h * d + e) + dqc[e] / s2;
+        dosel[e] = (1.0 - g_t) * grow[e];
+      }
+      dq_over_rows(c, k, v, h, sc, qrow, dosel, krows, nt, P, dP, o);
+    }
+    free(krows);
+    free(P);
+    free(dP);
+  }
+  for (int x = 0; x < 3; ++x) free(pq[x]);
+}
+
 /* ======================================================================== */
 /* Frame attention: the local step that alternates with GSA in the
  * aggregation transformer (Paper-Notes page, section "整体框架": blocks

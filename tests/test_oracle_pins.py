@@ -643,3 +643,17 @@ def test_backward_sum_identities(kw):
     G = flat(d_o, sh)
     np.testing.assert_allclose(dv.reshape(G.shape).sum(0), G.sum(0), rtol=0, atol=1e-10)
     np.testing.assert_allclose(dk.reshape(G.shape).sum(0), 0.0, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(ctx_frames=(1,), topk=2, dtype=BF16), dict(n_special=0, pool=4, topk=2)])
+def test_backward_dq_rows_equal_the_whole_layer_backward(kw):
+    """The per-row dq (for full-size checks) is the whole-layer backward's dq,
+    which the autograd and difference pins above fix."""
+    sh = shape(**kw)
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    idx = _fixed_topk(sh, 9)
+    dq = oracle.backward(sh, q, k, v, wg, idx, d_o)[0].reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    rows = np.arange(sh.m_tokens)
+    got = oracle.backward_dq_rows(sh, q, k, v, wg, idx, d_o, rows)
+    np.testing.assert_allclose(got, dq[rows], rtol=0, atol=1e-12 * max(1.0, np.abs(dq).max()))
