@@ -92,7 +92,10 @@ struct BwdStage {
       const int idx = tid + i * NT, row = idx / VPR, c = idx % VPR;
       const int64_t r = r0 + row;
       if (r < p.n_q) {
-        const int64_t tok = (r / p.qa) * p.qb + p.qc + r % p.qa;
+        // query rows and the map's period are below 2^31 (checked on the host):
+        // 32-bit division instead of the long 64-bit sequence, once per tile
+        const uint32_t ru = (uint32_t)r, qa = (uint32_t)p.qa, fr = ru / qa;
+        const int64_t tok = (int64_t)fr * p.qb + p.qc + (ru - fr * qa);
         const int64_t gtok = p.do_mapped ? tok : r;
         a[i] = ld16(Q + tok * p.row_stride + hoff + c * VE);
         b[i] = ld16(G + gtok * p.row_stride + hoff + c * VE);
