@@ -207,6 +207,11 @@ def main():
     # HBM view of the memory-bound steps (algorithmic bytes)
     pool_bytes = 3 * sh.m_img * H * d * esz + 3 * sh.n_windows * H * d * esz
     gather_bytes = sh.n_windows * H * sh.topk_eff * sh.pool ** 2 * 2 * d * esz
+    sb = (sh.pool ** 2 + 7) // 8 * 8
+    # gsa_select_attn also builds the blocked K / V^T copies it gathers from
+    select_bytes = (gather_bytes + sh.m_img * H * d * (esz + 4)                  # gathers, q in, O_sel out
+                    + 2 * sh.m_img * H * d * esz + 2 * sh.n_windows * H * sb * d * esz)  # the copies
+    combine_bytes = sh.m_img * H * d * (esz + 4 + esz) + sh.n_windows * H * d * 4
 
     detail = {
         "stage_ms": {k_: round(v_, 4) for k_, v_ in st.items()},
@@ -217,6 +222,13 @@ def main():
         "pool_hbm_gbs": round(pool_bytes / (st["pool"] * 1e-3) / 1e9, 1),
         "pool_frac_hbm": round(pool_bytes / (st["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "select_gather_bytes": gather_bytes,
+        # the standalone selection call (its blocked K/V copies, the gathers,
+        # q rows in, O_sel out) and combine (q, O_sel, O'_comp in; o out),
+        # algorithmic bytes over the entry point's time
+        "select_hbm_gbs": round(select_bytes / (st["select_standalone"] * 1e-3) / 1e9, 1),
+        "select_frac_hbm": round(select_bytes / (st["select_standalone"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "combine_hbm_gbs": round(combine_bytes / (st["gate_combine"] * 1e-3) / 1e9, 1),
+        "combine_frac_hbm": round(combine_bytes / (st["gate_combine"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "compressed_step": {"kernels": ["flash_kernel<bf16,4,bound>", "refine_kernel<bf16,4,64>"],
                             "ms": round(st["compressed_topk"], 4),
                             "flop": fl["compressed"] * 1.5,  # attention sweep + score-only sweep
