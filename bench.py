@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--pool", type=int, default=None, help="override the workload's window size s")
     ap.add_argument("--special", type=int, default=None, help="override the special tokens per frame P")
     ap.add_argument("--grid", type=int, nargs=2, default=None, metavar=("H", "W"), help="override the image grid")
+    ap.add_argument("--ctx", type=int, nargs="*", default=None, metavar="FRAME",
+                    help="override the fixed context frames (none: --ctx with no frames)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
@@ -116,11 +118,14 @@ def main():
     over = {k: v for k, v in (("topk", args.topk), ("pool", args.pool), ("n_special", args.special)) if v is not None}
     if args.grid:
         over.update(grid_h=args.grid[0], grid_w=args.grid[1])
+    if args.ctx is not None:
+        over.update(ctx_frames=tuple(args.ctx))
     if over:
         import dataclasses
         sh = dataclasses.replace(sh, **over)
+        ctx = "+ctx{" + ",".join(map(str, sh.ctx_frames)) + "}" if sh.ctx_frames else ""
         sh = dataclasses.replace(sh, name=f"{sh.name.split()[0]}-variant {sh.n_frames}f-{sh.grid_h}x{sh.grid_w}-"
-                                           f"h{sh.n_heads}-s{sh.pool}-k{sh.topk}-P{sh.n_special}")
+                                           f"h{sh.n_heads}-s{sh.pool}-k{sh.topk}-P{sh.n_special}{ctx}")
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 

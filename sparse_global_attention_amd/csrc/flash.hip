@@ -46,18 +46,23 @@ struct Cand {
   int j;
 };
 
-// Excluded keys of the 32-key tile starting at key0, as a bit mask (bit i =
-// key key0 + i).  Uniform across the wave.
-template <typename P>
-__device__ __forceinline__ uint32_t excluded_mask(const P& p, int64_t key0) {
-  uint32_t m = 0;
-  for (int x = 0; x < p.n_excl; ++x) {
-    const int64_t b = (int64_t)p.excl_frames[x] * p.wins_per_frame, e = b + p.wins_per_frame;
-    const int64_t lo = b > key0 ? b - key0 : 0, hi = e < key0 + kKT ? e - key0 : kKT;
-    if (lo < hi) m |= (uint32_t)((hi - lo == 32 ? 0xffffffffull : ((1ull << (hi - lo)) - 1)) << lo);
+// Excluded keys of a 32-key tile as a bit mask (bit i = key key0 + i),
+// uniform across the wave.  Tiles are visited in increasing key order, so a
+// cursor passes the ranges that end before the tile once and a tile usually
+// tests no range at all (scalar 32-bit arithmetic: key counts are int32).
+struct ExclCursor {
+  int x = 0;
+  template <typename P>
+  __device__ __forceinline__ uint32_t mask(const P& p, int key0) {
+    while (x < p.n_excl && p.excl_end[x] <= key0) ++x;
+    uint32_t m = 0;
+    for (int y = x; y < p.n_excl && p.excl_beg[y] < key0 + kKT; ++y) {
+      const int lo = max(p.excl_beg[y] - key0, 0), hi = min(p.excl_end[y] - key0, kKT);
+      m |= (hi - lo == kKT ? 0xffffffffu : (1u << (hi - lo)) - 1u) << lo;
+    }
+    return m;
   }
-  return m;
-}
+};
 
 // ---- the kernel ---------------------------------------------------------------
 // The ring of bf16 K/V tile buffers (three separate arrays, so the compiler
@@ -134,6 +139,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
   if (gend > n_tiles - 1) gend = n_tiles - 1;
   auto tile_rel = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
+  ExclCursor excl;  // kFlashBound: the excluded key ranges (single range from key 0)
 
   // One tile t from the K/V tile at kt (V follows K).  A step past the last
   // tile (the loops below run in whole unrolled rounds) sees only masked keys.
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       // The reference is added only when it changes (a rescale) and at the
       // group's end, and so is |m| folded into gm_abs.
       float mt = mu;
-      const uint32_t em = p.n_excl ? excluded_mask(p, cur0) : 0u;
+      const uint32_t em = p.n_excl ? excl.mask(p, (int)cur0) : 0u;
       if (em) {
         float x = -INFINITY;
 #pragma unroll
@@ -575,6 +581,7 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
   const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
   const int n_steps = (n_tiles + RSUB - 1) / RSUB;
   auto tile_key = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
+  ExclCursor excl;
   struct Stage {
     Loader l[RSUB];
   };
@@ -633,7 +640,7 @@ __global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
       // excluded keys of the tile, as this lane's bits (bit 4a+e = key 8a+4hf+e)
       unsigned ex = 0;
       if (p.n_excl) {
-        const uint32_t em = excluded_mask(p, cur0);
+        const uint32_t em = excl.mask(p, cur0);
 #pragma unroll
         for (int a = 0; a < 4; ++a) ex |= ((em >> (8 * a + 4 * hf)) & 15u) << (4 * a);
       }

@@ -3,6 +3,7 @@
 // Feed-forward 3D Reconstruction Models" (sections "全局稀疏注意力（GSA）核心设计",
 // "压缩分支", "选择分支", "门控聚合", "Speed3R-VGGT 适配"); see gsa.h for each
 // entry point's contract.
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -368,9 +369,23 @@ hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const v
   f.kend[0] = g.n_windows;
   f.oc = oc;
   f.part_lse = lse;
-  f.wins_per_frame = g.wpf;
-  f.n_excl = c.exclude ? c.n_ctx : 0;
-  for (int i = 0; i < f.n_excl; ++i) f.excl_frames[i] = c.ctx[i];
+  // the windows of excluded frames as ascending, merged key ranges
+  f.n_excl = 0;
+  if (c.exclude && c.n_ctx > 0) {
+    int fr[kMaxExcl];
+    for (int i = 0; i < c.n_ctx; ++i) fr[i] = c.ctx[i];
+    std::sort(fr, fr + c.n_ctx);
+    for (int i = 0; i < c.n_ctx; ++i) {
+      const int b = (int)(fr[i] * g.wpf), e = (int)((fr[i] + 1) * g.wpf);
+      if (f.n_excl > 0 && b <= f.excl_end[f.n_excl - 1]) {
+        f.excl_end[f.n_excl - 1] = std::max(f.excl_end[f.n_excl - 1], e);
+      } else {
+        f.excl_beg[f.n_excl] = b;
+        f.excl_end[f.n_excl] = e;
+        ++f.n_excl;
+      }
+    }
+  }
   f.gbound = reinterpret_cast<float*>(at(ws, pl.gbound));
   f.n_groups = pl.n_groups;
   f.group_tiles = pl.group_tiles;
@@ -387,9 +402,11 @@ hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const v
   r.gbound = f.gbound;
   r.n_groups = pl.n_groups;
   r.topk = c.topk;
-  r.wins_per_frame = g.wpf;
   r.n_excl = f.n_excl;
-  for (int i = 0; i < f.n_excl; ++i) r.excl_frames[i] = f.excl_frames[i];
+  for (int i = 0; i < f.n_excl; ++i) {
+    r.excl_beg[i] = f.excl_beg[i];
+    r.excl_end[i] = f.excl_end[i];
+  }
   r.topk_idx = idx;
   r.topk_score = score;
   return launch_refine(c.dtype, r, st);

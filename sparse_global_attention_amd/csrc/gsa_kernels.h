@@ -92,9 +92,10 @@ struct FlashParams {
   float* part_lse;
   // kFlashBound: oc [n_q][H][d] fp32 (and, if part_lse is set, the rows' log-sum-exp there)
   float* oc;
-  int64_t wins_per_frame;
-  int n_excl;                 // frames whose windows are not top-k candidates
-  int excl_frames[kMaxExcl];
+  // keys (windows) that are not top-k candidates: n_excl ranges
+  // [excl_beg[i], excl_end[i]), ascending, disjoint and not touching
+  int n_excl;
+  int excl_beg[kMaxExcl], excl_end[kMaxExcl];
   // kFlashBound: gbound [H][n_groups][n_q]; group g covers key tiles
   // [g*group_tiles, (g+1)*group_tiles) of the single key range
   float* gbound;
@@ -114,9 +115,8 @@ struct RefineParams {
   const float* gbound;
   int n_groups;
   int topk;
-  int64_t wins_per_frame;
-  int n_excl;
-  int excl_frames[kMaxExcl];
+  int n_excl;  // excluded key ranges, as in FlashParams
+  int excl_beg[kMaxExcl], excl_end[kMaxExcl];
   int32_t* topk_idx;
   float* topk_score;
 };

@@ -31,6 +31,10 @@ SHAPES = {
     "p0": GSAShape("p0 4f-8x12-h2-s4-k3", 4, 0, 8, 12, 2, 64, 4, 3, BF16, seed=26),
     "ctx": GSAShape("ctx 6f-8x8-h2-s4-k3+ctx{0,3}", 6, 2, 8, 8, 2, 64, 4, 3, BF16, ctx_frames=(0, 3), seed=27),
     "ctx_f32": GSAShape("ctx 5f-8x8-h1-s2-k6+ctx{4}", 5, 1, 8, 8, 1, 64, 2, 6, F32, ctx_frames=(4,), seed=28),
+    # adjacent context frames (merged into one excluded range) and 36 windows
+    # per frame, so excluded ranges start and end inside 32-key tiles
+    "ctx_adjacent": GSAShape("ctx 8f-12x12-h2-s2-k5+ctx{6,2,3,7}", 8, 1, 12, 12, 2, 64, 2, 5, BF16,
+                             ctx_frames=(6, 2, 3, 7), seed=38),
     "k_clamp": GSAShape("kclamp 2f-8x8-h2-s4-k64", 2, 1, 8, 8, 2, 64, 4, 64, BF16, seed=29),
     "k40": GSAShape("k40 10f-16x16-h2-s4-k40", 10, 1, 16, 16, 2, 64, 4, 40, BF16, seed=32),
     "k64": GSAShape("k64 10f-16x16-h2-s4-k64", 10, 1, 16, 16, 2, 64, 4, 64, BF16, seed=30),
