@@ -74,7 +74,7 @@ __shared__ __attribute__((aligned(16))) __bf16 ring2[kKT * kHeadDim * 2];
 
 // The bf16 bound mode asks for four workgroups per CU (at most 128 VGPRs),
 // the occupancy of the plain attention modes.
-template <typename T, int WAVES, int MODE>
+template <typename T, int WAVES, int MODE, bool RLOOP = false>
 __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ? 4 : 1) void flash_kernel(FlashParams p) {
   using TL = Tile<T>;
   using F = Frag32<T>;
@@ -94,8 +94,14 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   const int64_t hs = w / n_qt;
   const int h = (int)(hs % p.n_heads);
   const int64_t sb = hs / p.n_heads;
-  const int split = (int)(sb % p.n_splits);
-  const int64_t batch = sb / p.n_splits;
+  // RLOOP (kFlashPartial, range_loop set): the workgroup sweeps every split
+  // in turn into one partial (index 0); otherwise the grid holds one split each.
+  static_assert(!RLOOP || MODE == kFlashPartial, "range loop: partial mode only");
+  constexpr bool rloop = RLOOP;
+  const int grid_splits = rloop ? 1 : p.n_splits;
+  const int split = (int)(sb % grid_splits);
+  const int64_t batch = sb / grid_splits;
+  const int part = rloop ? 0 : split;
 
   const int64_t qrow = qt * QW + wv * 32 + r;
   const bool qvalid = qrow < p.n_q;
@@ -128,14 +134,19 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       (int)(slab < 0x7fffffff ? slab : 0x7fffffff), 0x00020000);
   const int gb_off = (int)(qrow * 4);
 
-  // Key tiles of this split: tile t covers keys kb + 32t .. kb + 32t + 31.
+  // Key tiles of split rs: tile t covers keys kb + 32t .. kb + 32t + 31.
   // Prefetches past the last tile re-read the last tile (never used), so the
   // load/store pattern has no branches and the compiler can keep two tiles of
   // loads in flight across the barriers.
   // Positions inside the range are int32 (the host keeps token counts below
   // 2^31 - 64), so the per-tile bookkeeping is scalar 32-bit arithmetic.
-  const int64_t kb = p.kbeg[split] + batch * p.k_bstride;
-  const int nk = (int)(p.kend[split] - p.kbeg[split]);
+  // Between two splits of a range loop the tile buffers are free: every wave
+  // has passed the last barrier after its last read, and a wave's loads
+  // still in flight write only the LDS chunks that wave loads.
+  const int rs_end = rloop ? p.n_splits : split + 1;
+  for (int rs = rloop ? 0 : split; rs < rs_end; ++rs) {
+  const int64_t kb = p.kbeg[rs] + batch * p.k_bstride;
+  const int nk = (int)(p.kend[rs] - p.kbeg[rs]);
   const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
   if (gend > n_tiles - 1) gend = n_tiles - 1;
   auto tile_rel = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
@@ -360,6 +371,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       step(t + 1, sa);
     }
   }
+  }  // splits of the range loop
 
   // ---- epilogue ----
   const float l = l_run + xor_lane(l_run, 32);
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
             *reinterpret_cast<f32x4*>(dst) = v4;
           }
         } else if constexpr (MODE == kFlashPartial) {
-          float* dst = p.part_o + ((split * p.n_q + qrow) * p.n_heads + h) * kHeadDim + dv0;
+          float* dst = p.part_o + ((part * p.n_q + qrow) * p.n_heads + h) * kHeadDim + dv0;
           *reinterpret_cast<f32x4*>(dst) = v4;
         } else {
           float* dst = p.oc + (qrow * p.n_heads + h) * kHeadDim + dv0;
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
     // only when asked (training state)
     if constexpr (MODE == kFlashPartial || MODE == kFlashBound) {
       if (hf == 0 && (MODE == kFlashPartial || p.part_lse))
-        p.part_lse[(split * p.n_q + qrow) * p.n_heads + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+        p.part_lse[(part * p.n_q + qrow) * p.n_heads + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
     }
   }
 
@@ -804,24 +816,28 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
 }
 
-template <typename T, int WAVES, int MODE>
+template <typename T, int WAVES, int MODE, bool RLOOP = false>
 static hipError_t launch_flash_t(const FlashParams& p, hipStream_t stream) {
   const int64_t n_qt = (p.n_q + WAVES * 32 - 1) / (WAVES * 32);
-  const int64_t blocks = n_qt * p.n_heads * p.n_splits * p.n_batch;
+  const int64_t grid_splits = RLOOP ? 1 : p.n_splits;
+  const int64_t blocks = n_qt * p.n_heads * grid_splits * p.n_batch;
   if (blocks == 0) return hipSuccess;
-  if (p.n_batch < 1 || (p.n_batch > 1 && MODE != kFlashFinal) || blocks > 0xffffffffLL) return hipErrorInvalidValue;
+  if (p.n_batch < 1 || (p.n_batch > 1 && MODE != kFlashFinal) || p.range_loop != (RLOOP ? 1 : 0) ||
+      blocks > 0xffffffffLL)
+    return hipErrorInvalidValue;
   size_t lds = sizeof(T) == 2 ? 0 : 2 * (size_t)Tile<T>::BYTES;  // bf16 tiles live in static LDS
-  const void* fn = reinterpret_cast<const void*>(&flash_kernel<T, WAVES, MODE>);
+  const void* fn = reinterpret_cast<const void*>(&flash_kernel<T, WAVES, MODE, RLOOP>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((flash_kernel<T, WAVES, MODE>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
+  hipLaunchKernelGGL((flash_kernel<T, WAVES, MODE, RLOOP>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_flash_dt(int mode, const FlashParams& p, hipStream_t stream) {
   if (mode == kFlashFinal) return launch_flash_t<T, 4, kFlashFinal>(p, stream);
-  if (mode == kFlashPartial) return launch_flash_t<T, 4, kFlashPartial>(p, stream);
+  if (mode == kFlashPartial)
+    return p.range_loop ? launch_flash_t<T, 4, kFlashPartial, true>(p, stream) : launch_flash_t<T, 4, kFlashPartial>(p, stream);
   if (mode == kFlashBound) return launch_flash_t<T, 4, kFlashBound>(p, stream);
   return hipErrorInvalidValue;
 }

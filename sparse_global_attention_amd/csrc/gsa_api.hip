@@ -191,6 +191,15 @@ int special_splits(const Call& c) {
   }
   return best;
 }
+// Context frames' partials: one sweep per query block over every context
+// frame (one partial) when the query blocks alone fill the chip several
+// times over, else one split and one partial per frame.
+bool ctx_range_loop(const Call& c) {
+  const int64_t n_qt = (c.g.m_img + 127) / 128;
+  return c.n_ctx > 1 && n_qt * c.g.n_heads >= 4096;
+}
+int ctx_parts(const Call& c) { return c.n_ctx == 0 ? 0 : ctx_range_loop(c) ? 1 : c.n_ctx; }
+
 
 Plan make_plan(const Call& c, gsa_op op) {
   const Geometry& g = c.g;
@@ -202,8 +211,8 @@ Plan make_plan(const Call& c, gsa_op op) {
   const int64_t blk = g.n_windows * g.n_heads * g.sb * kHeadDim * c.esz;
   const int64_t spec_o = (int64_t)p.n_split * g.m_spec * g.n_heads * kHeadDim * 4;
   const int64_t spec_lse = (int64_t)p.n_split * g.m_spec * g.n_heads * 4;
-  const int64_t ctx_o = (int64_t)c.n_ctx * g.m_img * g.n_heads * kHeadDim * 4;
-  const int64_t ctx_lse = (int64_t)c.n_ctx * g.m_img * g.n_heads * 4;
+  const int64_t ctx_o = (int64_t)ctx_parts(c) * g.m_img * g.n_heads * kHeadDim * 4;
+  const int64_t ctx_lse = (int64_t)ctx_parts(c) * g.m_img * g.n_heads * 4;
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
     int64_t at = off;
@@ -421,7 +430,8 @@ hipError_t run_context(const Call& c, const Plan& pl, const void* q, const void*
   f.qa = g.grid_h * g.grid_w;
   f.qb = g.tf;
   f.qc = g.n_special;
-  f.n_splits = c.n_ctx;  // one split (and one partial) per context frame
+  f.n_splits = c.n_ctx;  // one split per context frame
+  f.range_loop = ctx_range_loop(c) ? 1 : 0;
   for (int i = 0; i < c.n_ctx; ++i) {
     f.kbeg[i] = (int64_t)c.ctx[i] * g.tf;
     f.kend[i] = f.kbeg[i] + g.tf;
@@ -449,7 +459,7 @@ SelectParams select_base(const Call& c, const Plan& pl, const void* q, const int
   s.topk = c.topk;
   s.g = c.g;
   s.scale_log2 = c.scale * kLog2e;
-  s.n_ctx = c.n_ctx;
+  s.n_ctx = ctx_parts(c);
   if (c.n_ctx) {
     s.ctx_o = reinterpret_cast<const float*>(at(ws, pl.ctx_o));
     s.ctx_lse = reinterpret_cast<const float*>(at(ws, pl.ctx_lse));

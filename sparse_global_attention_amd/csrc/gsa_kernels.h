@@ -87,7 +87,9 @@ struct FlashParams {
   float scale_log2;  // softmax scale * log2(e)
   // kFlashFinal: normalised output in the input dtype at rows token(r) of o
   void* o;
-  // kFlashPartial: part_o [split][n_q][H][d] (normalised), part_lse [split][n_q][H] (natural log)
+  // kFlashPartial: part_o [split][n_q][H][d] (normalised), part_lse [split][n_q][H] (natural log);
+  // with range_loop = 1 one workgroup sweeps all splits and writes one partial (index 0)
+  int range_loop;
   float* part_o;
   float* part_lse;
   // kFlashBound: oc [n_q][H][d] fp32 (and, if part_lse is set, the rows' log-sum-exp there)
@@ -150,7 +152,7 @@ struct SelectParams {
   int topk;
   Geometry g;
   float scale_log2;
-  int n_ctx;            // context partials (one per context frame), 0 if none
+  int n_ctx;            // context partials (one per context frame, or one for all), 0 if none
   const float* ctx_o;   // [n_ctx][M_img][H][d] (normalised)
   const float* ctx_lse; // [n_ctx][M_img][H] log-sum-exp
   float* osel;          // standalone output [M_img][H][d]; fused path: optional copy of O_sel
