@@ -14,7 +14,10 @@ times (gsa_forward), checked on sampled outputs the oracle computes one by one:
   key/value set bit for bit, sampled tokens x all heads.
 
 Workloads: VGGT-style 128 frames with fixed context {0, 100}; the pi^3-style
-1000-frame sequence; the peaky clustered 1024-frame sequence.
+1000-frame sequence; the peaky clustered 1024-frame sequence; an fp32
+32-frame sequence with two context frames, large enough (4 096 query blocks x
+heads) that one workgroup sweeps both context frames, as in the bf16
+VGGT-style workload.
 """
 import sys
 import time
@@ -25,13 +28,16 @@ import torch
 
 import gen
 import oracle
-from gen.configs import PEAKY, PI3_LONG, VGGT_CTX
+from gen.configs import F32, PEAKY, PI3_LONG, VGGT_CTX, GSAShape
 from gsa_testlib import (Case, assert_close, assert_close_rows, check_topk, same_sets, special_token_ids, to_host,
                          window_token_ids)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-WORKLOADS = {"vggt_ctx": (VGGT_CTX, 1024), "pi3_long": (PI3_LONG, 512), "peaky": (PEAKY, 512)}
+CTX_F32 = GSAShape("ctx-f32 32f-32x32-h16-s4-k16+ctx{17,3}", 32, 1, 32, 32, 16, 64, 4, 16, F32,
+                   ctx_frames=(17, 3), seed=1005)
+WORKLOADS = {"vggt_ctx": (VGGT_CTX, 1024), "pi3_long": (PI3_LONG, 512), "peaky": (PEAKY, 512),
+             "ctx_f32": (CTX_F32, 512)}
 N_SPECIAL_ROWS = 64
 
 
