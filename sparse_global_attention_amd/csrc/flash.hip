@@ -15,9 +15,7 @@
 //                   top-k (section "选择分支").  S is never written out.
 //
 // Work decomposition: a workgroup of WAVES wavefronts owns 32*WAVES query
-// rows of one head and one key split (in the range-loop instance of
-// kFlashPartial: every split in turn, one partial); each wavefront owns 32
-// query rows.  Key
+// rows of one head and one key split; each wavefront owns 32 query rows.  Key
 // tiles of 32 keys are staged once per workgroup in LDS (K as rows, V
 // transposed so the PV operand is a contiguous read) and shared by all its
 // waves.  Per tile and wave:
