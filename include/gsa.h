@@ -54,7 +54,7 @@ typedef enum {
   GSA_OK = 0,
   GSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad k, bad context frame, aliasing */
   GSA_ERR_SHAPE = 2,       /* h or w not divisible by s, non-positive sizes, size overflow
-                              (M' > 2^31 - 1 windows, M >= 2^31 - 64 tokens, M*H*d > 2^40) */
+                              (M' >= 2^29 windows, M >= 2^31 - 64 tokens, M*H*d > 2^40) */
   GSA_ERR_UNSUPPORTED = 3, /* d != 64, s > 8, k > 128, unknown dtype */
   GSA_ERR_WORKSPACE = 4,   /* workspace smaller than gsa_workspace_size() */
   GSA_ERR_HIP = 5          /* a HIP launch failed */
@@ -111,10 +111,13 @@ gsa_status gsa_pool(const gsa_config* cfg, const void* q, const void* k, const v
  * windows, minus the context frames' windows when ctx_exclude_from_topk is
  * set), per head.  Writes oc, topk_idx and, if not NULL, topk_score.
  * The attention sweep also records a lower bound of the best score in each
- * group of key tiles; a score-only sweep then keeps the keys that reach the
- * k-th best bound and ranks them (exact for any input: a query whose
- * candidate slots fill up keeps its k best so far and raises its threshold).
- * Workspace: GSA_OP_COMPRESSED bytes.
+ * group of key tiles; theta = the query's k-th best bound is at most its k-th
+ * best score.  Only the groups whose bound comes within the bound's error of
+ * theta can hold a key scoring >= theta; those keys are re-scored, collected
+ * and ranked.  Exact for any input: query tiles where a query's candidate
+ * list would overflow (e.g. many tied scores), or with fewer than k finite
+ * bounds, are re-swept over every key, keeping the k best so far whenever the
+ * slots fill up.  Workspace: GSA_OP_COMPRESSED bytes.
  */
 gsa_status gsa_compressed_attn_topk(const gsa_config* cfg, const void* qc, const void* kc,
                                     const void* vc, float* oc, int32_t* topk_idx,

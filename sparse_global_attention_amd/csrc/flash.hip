@@ -40,30 +40,6 @@ constexpr float kLazyRescale = 8.0f; // rescale only when the max grows by > 2^8
 // only when its weights against the running reference sum to 2^64 or more.
 constexpr float kSumLimit = 0x1p64f;
 
-// ---- candidates of the exact top-k ------------------------------------------
-struct Cand {
-  float s;
-  int j;
-};
-
-// Excluded keys of a 32-key tile as a bit mask (bit i = key key0 + i),
-// uniform across the wave.  Tiles are visited in increasing key order, so a
-// cursor passes the ranges that end before the tile once and a tile usually
-// tests no range at all (scalar 32-bit arithmetic: key counts are int32).
-struct ExclCursor {
-  int x = 0;
-  template <typename P>
-  __device__ __forceinline__ uint32_t mask(const P& p, int key0) {
-    while (x < p.n_excl && p.excl_end[x] <= key0) ++x;
-    uint32_t m = 0;
-    for (int y = x; y < p.n_excl && p.excl_beg[y] < key0 + kKT; ++y) {
-      const int lo = max(p.excl_beg[y] - key0, 0), hi = min(p.excl_end[y] - key0, kKT);
-      m |= (hi - lo == kKT ? 0xffffffffu : (1u << (hi - lo)) - 1u) << lo;
-    }
-    return m;
-  }
-};
-
 // ---- the kernel ---------------------------------------------------------------
 // The ring of bf16 K/V tile buffers (three separate arrays, so the compiler
 // can tell which buffer a global-to-LDS load writes and wait only for that).
@@ -122,16 +98,14 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
 
   // kFlashBound: running max over the current group of fl(tile max u + m),
   // the largest |m| seen in the group, the group's last tile and its index.
-  // The bounds of this head are written with buffer stores: scalar base (the
-  // head's slab) and group offset, one per-lane offset (the query row).
+  // The bounds are written with buffer stores: scalar base (the group's row
+  // of this head, 64-bit pointer arithmetic), one per-lane offset (the query
+  // row; the host keeps n_q * 4 below 2^31).
   // gbu: this lane's max of u since the reference m_run last changed (so
-  // fl(gbu + m_run) is the max of fl(u + m_run), adding m being monotonic)
-  float gb = -INFINITY, gbu = -INFINITY, gm_abs = 0.0f;
+  // fl(gbu + m_run) is the max of fl(u + m_run), adding m being monotonic);
+  // emax: the largest error term of the query's finite group bounds.
+  float gb = -INFINITY, gbu = -INFINITY, gm_abs = 0.0f, emax = 0.0f;
   int gend = p.group_tiles - 1, gi = 0;
-  const int64_t slab = MODE == kFlashBound ? (int64_t)p.n_groups * p.n_q * 4 : 0;
-  const __amdgpu_buffer_rsrc_t gbr = __builtin_amdgcn_make_buffer_rsrc(
-      MODE == kFlashBound ? p.gbound + (int64_t)h * p.n_groups * p.n_q : nullptr, (short)0,
-      (int)(slab < 0x7fffffff ? slab : 0x7fffffff), 0x00020000);
   const int gb_off = (int)(qrow * 4);
 
   // Key tiles of split rs: tile t covers keys kb + 32t .. kb + 32t + 31.
@@ -246,10 +220,13 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
         gb = fmaxf(gb, gbu + m_run);
         gm_abs = fmaxf(gm_abs, fabsf(m_run));
         const float gq = fmaxf(gb, xor_lane(gb, 32));  // uniform branch: every lane takes part
+        const float a = gq * rc;
+        const float e = ldexpf(fabsf(a) + gm_abs * rc, -20);
+        if (a > -INFINITY) emax = fmaxf(emax, e);  // a group of excluded keys only has no bound
         if (hf == 0 && qvalid) {
-          const float a = gq * rc;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a - ldexpf(fabsf(a) + gm_abs * rc, -20)), gbr, gb_off,
-                                                (int)((int64_t)gi * p.n_q * 4), 0);
+          const __amdgpu_buffer_rsrc_t gbr = __builtin_amdgcn_make_buffer_rsrc(
+              p.gbound + ((int64_t)h * p.n_groups + gi) * p.n_q, (short)0, (int)(p.n_q * 4), 0x00020000);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a - e), gbr, gb_off, 0, 0);
         }
         gb = -INFINITY;
         gbu = -INFINITY;
@@ -406,372 +383,14 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
       if (hf == 0 && (MODE == kFlashPartial || p.part_lse))
         p.part_lse[(part * p.n_q + qrow) * p.n_heads + h] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
     }
-  }
-
-}
-
-// ---- exact top-k from the group bounds ---------------------------------------
-// Order-preserving map of floats to unsigned keys and back.
-__device__ __forceinline__ uint32_t order_key(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-// The next float above x (x finite or -inf): "y > x" is "y >= next_up(x)".
-// (both zeros map to +0 first, so the result is the smallest positive value)
-__device__ __forceinline__ float next_up(float x) { return key_value(order_key(x == 0.0f ? 0.0f : x) + 1u); }
-
-
-// theta = the k-th largest of the query's group bounds.  Each group bound is
-// at most the score of one distinct candidate key, so the k-th best candidate
-// score is >= theta, and every top-k key scores >= theta.  Radix select over
-// the order keys, bit by bit from the top; the two lanes of a query hold the
-// even and the odd groups (n_groups <= 2 * kMaxGroupsPerLane).  Returns -inf
-// when there are fewer than k finite bounds (then every candidate qualifies).
-template <int kMaxGroupsPerLane>
-__device__ float kth_bound(const RefineParams& p, int64_t qrow, int h, int hf, bool qvalid) {
-  const int NG = p.n_groups;
-  const int per = (NG - hf + 1) / 2;
-  const float* src = p.gbound + (int64_t)h * NG * p.n_q + (qvalid ? qrow : 0);
-  uint32_t kv[kMaxGroupsPerLane];
-#pragma unroll
-  for (int i = 0; i < kMaxGroupsPerLane; ++i) {
-    // clamped, unconditional loads; out-of-range slots become key 0, which no
-    // candidate key below reaches (every candidate key has a bit set)
-    const int g = min(2 * i + hf, NG - 1);
-    const float x = src[(int64_t)g * p.n_q];
-    kv[i] = (qvalid && i < per) ? order_key(x) : 0u;
-  }
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxGroupsPerLane; ++i) cnt += kv[i] >= cand ? 1 : 0;
-    cnt = sum_halves(cnt);
-    if (cnt >= p.topk) T = cand;
-  }
-  return T > order_key(-INFINITY) ? key_value(T) : -INFINITY;
-}
-
-__device__ __forceinline__ bool cand_better(Cand a, Cand b) { return a.s > b.s || (a.s == b.s && a.j < b.j); }
-
-// Candidate slots of one wave in LDS: slot i of query r at buf[i * 32 + r],
-// kRefineSlots slots per query.  The even lane of a query fills slots upwards
-// from 0 (its entries are [0, lo)), the odd lane downwards from the top (its
-// entries are (hi, kRefineSlots)); the slots between are free.  Within each
-// lane's range the entries are in ascending key order.
-struct CandSlots {
-  Cand* buf;
-  int r, hf;
-  int fp;      // this lane's next free slot (even lane: lo, odd lane: hi)
-  int dir;     // +1 for the even lane, -1 for the odd lane
-  int nslots;  // slots per query (a compile-time constant of the kernel)
-  __device__ __forceinline__ int count() const { return hf ? nslots - 1 - fp : fp; }
-  __device__ __forceinline__ int slot(int i) const { return hf ? nslots - 1 - i : i; }  // i-th own entry
-};
-
-// Keep only the k best candidates (score desc, index asc) of every query of the
-// wave; returns the k-th best score (-inf if fewer than k).  Radix select on the
-// order keys of the scores; ties at the cut are decided by the lowest indices
-// with a second select on the index bits.  Entries move only inside their own
-// lane's range (a lane reads slot i before writing slot <= i), so the
-// compaction is done in place.  Every lane of the wave must call it.
-__device__ float compact_slots(CandSlots& cs, int K, bool& cut) {
-  const int c = cs.count();
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = T | (1u << b);
-    int cnt = 0;
-    for (int i = 0; i < c; ++i) cnt += order_key(cs.buf[cs.slot(i) * 32 + cs.r].s) >= cand ? 1 : 0;
-    cnt = sum_halves(cnt);
-    if (cnt >= K) T = cand;
-  }
-  // entries strictly above the cut score, and those equal to it
-  int gt = 0, eq = 0;
-  for (int i = 0; i < c; ++i) {
-    const uint32_t k = order_key(cs.buf[cs.slot(i) * 32 + cs.r].s);
-    gt += k > T ? 1 : 0;
-    eq += k == T ? 1 : 0;
-  }
-  gt = sum_halves(gt);
-  eq = sum_halves(eq);
-  // among the entries equal to the cut score keep the (K - gt) lowest indices:
-  // J = the largest index kept (smallest J with #{equal, index <= J} >= K - gt)
-  uint32_t J = 0xffffffffu;
-  const bool straddle = gt < K && gt + eq > K;
-  if (wave_any(straddle)) {
-    uint32_t lowJ = 0;  // build the answer from the top bit: count(index < lowJ + bit) < need -> set bit
-    for (int b = 31; b >= 0; --b) {
-      const uint32_t probe = lowJ | (1u << b);
-      int cnt = 0;
-      for (int i = 0; i < c; ++i) {
-        const Cand x = cs.buf[cs.slot(i) * 32 + cs.r];
-        cnt += (order_key(x.s) == T && (uint32_t)x.j < probe) ? 1 : 0;
-      }
-      cnt = sum_halves(cnt);
-      if (cnt < K - gt) lowJ = probe;
-    }
-    if (straddle) J = lowJ;
-  }
-  // squeeze the kept entries of this lane's range towards its end
-  int w = 0;
-  for (int i = 0; i < c; ++i) {
-    const Cand x = cs.buf[cs.slot(i) * 32 + cs.r];
-    const uint32_t k = order_key(x.s);
-    if (k > T || (k == T && (uint32_t)x.j <= J)) {
-      cs.buf[cs.slot(w) * 32 + cs.r] = x;
-      ++w;
+    // The true best score of a group lies within 1.25 e (+ an ulp) of its
+    // stored bound a - e (|fl(fl(u + m) / c) - s| <= 2^-22 |s| + 2^-24 |m / c|);
+    // 4 e also covers the rounding of theta - E when the hot groups are picked.
+    if constexpr (MODE == kFlashBound) {
+      if (hf == 0) p.gerr[(int64_t)h * p.n_q + qrow] = 4.0f * emax;
     }
   }
-  cs.fp = cs.slot(w);
-  cut = gt + eq >= K;
-  return cut ? key_value(T) : -INFINITY;
-}
 
-// One workgroup: WAVES x 32 queries of one head against all M' keys.  Key
-// tiles are staged in LDS, RSUB tiles of 32 keys at a time, and only
-// S^T = K Q^T is formed.  Keys with score >= theta are
-// appended to the query's LDS slots; when the slots run low, the query keeps
-// only its current k best (so the slots never overflow) and from then on a key
-// must beat the k-th best score strictly (an equal score loses: it has a
-// higher index than every kept key).  At the end the candidates are ranked and
-// the first k written, sorted.  Requires k <= kRefineMaxK.
-// One LDS stage of RSUB key tiles: the waves test all RSUB tiles, meet at a
-// barrier, store the next stage (loaded into registers during the tests) and
-// meet again.  A wave's candidate work varies from tile to tile, and every
-// wave waits for the slowest at a barrier; four tiles per test phase average
-// that out better than two tiles per barrier with two stages (which LDS
-// allows only up to two tiles: the candidate slots take 64 KB).
-constexpr int RSUB = 4;
-template <typename T, int WAVES, int SLOTS>
-__global__ __launch_bounds__(WAVES * 64) void refine_kernel(RefineParams p) {
-  constexpr int kRefineSlots = SLOTS;
-  using TL = Tile<T>;
-  using F = Frag32<T>;
-  using Loader = TileLoader<T, WAVES * 64>;
-  constexpr int KBYTES = TL::K_ELEMS * (int)sizeof(T);
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  // the stage buffer: RSUB key tiles, then the candidate slots
-  auto tile_buf = [&](int j) { return reinterpret_cast<T*>(smem + j * KBYTES); };
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r = lane & 31, hf = lane >> 5;
-  CandSlots cs;
-  cs.buf = reinterpret_cast<Cand*>(smem + RSUB * KBYTES) + wv * kRefineSlots * 32;
-  cs.r = r;
-  cs.hf = hf;
-  cs.nslots = kRefineSlots;
-  cs.fp = hf ? kRefineSlots - 1 : 0;
-  cs.dir = hf ? -1 : 1;
-  constexpr int QW = WAVES * 32;
-  const int64_t n_qt = (p.n_q + QW - 1) / QW;
-  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t qt = w % n_qt;
-  const int h = (int)(w / n_qt);
-  const int64_t qrow = qt * QW + wv * 32 + r;
-  const bool qvalid = qrow < p.n_q;
-  const int64_t hoff = (int64_t)h * kHeadDim;
-  const int Kk = p.topk;
-  const T* K = static_cast<const T*>(p.k);
-  typename F::Q qf = F::load_q(qvalid ? static_cast<const T*>(p.q) + qrow * p.row_stride + hoff : nullptr, hf);
-  // a key is a candidate when its score is >= tlo: theta at first, then just
-  // above the k-th best kept score (an equal score loses to the kept keys,
-  // which all have lower indices)
-  float tlo = kth_bound<kRefineGroups(SLOTS) / 2>(p, qrow, h, hf, qvalid);
-  if (!qvalid) tlo = INFINITY;
-  int ntot = 0;  // candidates held for this lane's query (both lanes)
-  __builtin_amdgcn_s_waitcnt(0);
-  // compare raw scores as integers when every threshold of the wave is
-  // positive (order-preserving on the bit patterns then), else as floats;
-  // thresholds only grow, so the choice stays valid
-  const bool as_int = !wave_any(!(tlo > 0.0f));
-
-  const int nk = (int)p.n_q;  // window counts are int32 (checked on the host)
-  const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
-  const int n_steps = (n_tiles + RSUB - 1) / RSUB;
-  auto tile_key = [&](int t) { return (t < n_tiles ? t : n_tiles - 1) * kKT; };
-  ExclCursor excl;
-  struct Stage {
-    Loader l[RSUB];
-  };
-  auto stage_load = [&](Stage& st, int u) {
-#pragma unroll
-    for (int j = 0; j < RSUB; ++j) {
-      const int key0 = tile_key(u * RSUB + j);
-      st.l[j].load_k(K, p.row_stride, hoff, key0, min(nk - key0, kKT), tid);
-    }
-  };
-  auto stage_store = [&](const Stage& st) {
-#pragma unroll
-    for (int j = 0; j < RSUB; ++j) st.l[j].store_k(tile_buf(j), tid);
-  };
-  Stage st;
-  stage_load(st, 0);
-  stage_store(st);
-  stage_load(st, 1);
-  lds_barrier();
-
-  // The sweep, compiled once for integer and once for float comparisons.
-  auto sweep = [&](auto int_tag) {
-    constexpr bool AS_INT = decltype(int_tag)::value;
-    // candidates of one 32-key tile t, from its scores s (S^T)
-    auto tile = [&](int t, f32x16 s) {
-      const int cur0 = t * kKT;
-      if (t >= n_full) {
-        const int lim = nk - cur0 - 4 * hf;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (8 * (i / 4) + (i % 4) >= lim) s[i] = -INFINITY;
-      }
-      // a score passes when >= tlo (and is not -inf: keys past the end)
-      const int tlo_bits = __float_as_int(tlo);
-      auto pass = [&](float x) {
-        if constexpr (AS_INT) return __float_as_int(x) >= tlo_bits;
-        else return x >= tlo && x != -INFINITY;
-      };
-      // 4-key group maxima first (the exact per-key test follows)
-      bool g[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        if constexpr (AS_INT) {
-          const int m = max(max(__float_as_int(s[4 * a]), __float_as_int(s[4 * a + 1])),
-                            max(__float_as_int(s[4 * a + 2]), __float_as_int(s[4 * a + 3])));
-          g[a] = m >= tlo_bits;
-        } else {
-          const float m = fmaxf(fmaxf(s[4 * a], s[4 * a + 1]), fmaxf(s[4 * a + 2], s[4 * a + 3]));
-          g[a] = m >= tlo && m != -INFINITY;
-        }
-      }
-      if (!wave_any(g[0] || g[1] || g[2] || g[3])) return;
-      // groups with a passing key in some lane of the wave (uniform)
-      const unsigned gany = (wave_any(g[0]) ? 1u : 0u) | (wave_any(g[1]) ? 2u : 0u) |
-                            (wave_any(g[2]) ? 4u : 0u) | (wave_any(g[3]) ? 8u : 0u);
-      // excluded keys of the tile, as this lane's bits (bit 4a+e = key 8a+4hf+e)
-      unsigned ex = 0;
-      if (p.n_excl) {
-        const uint32_t em = excl.mask(p, cur0);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) ex |= ((em >> (8 * a + 4 * hf)) & 15u) << (4 * a);
-      }
-      auto key_of = [&](int a, int e) { return (int)(cur0 + 8 * a + 4 * hf + e); };
-      // exact tests of group a: bit e = key 8a+4hf+e is a candidate
-      auto group_keep = [&](int a) {
-        unsigned gm = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gm |= (pass(s[4 * a + e]) ? 1u : 0u) << e;
-        return gm & ~(ex >> (4 * a)) & 15u;
-      };
-      // Whole group: every lane writes the group's 4 keys, its kept keys
-      // compacted at its fill pointer and the others at pointer + e.  A kept
-      // key's slot is at most its own e, so a later kept key may overwrite an
-      // earlier dropped one but never the reverse; the dropped keys land in
-      // free slots (needs >= 8 free, so the two ends never meet).
-      auto append_group = [&](int a, unsigned gm) {
-        int kb = 0;  // kept keys of the group so far
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool kept = (gm >> e) & 1u;
-          cs.buf[(cs.fp + cs.dir * (kept ? kb : e)) * 32 + r] = Cand{s[4 * a + e], key_of(a, e)};
-          kb += kept ? 1 : 0;
-        }
-        cs.fp += cs.dir * kb;
-      };
-      // a passing group adds at most 8 candidates to a query (4 per lane)
-      if (!wave_any(ntot + 8 * __builtin_popcount(gany) + 8 > kRefineSlots)) {
-        // common case: room for whole groups, test and append in one pass
-        int need = 0;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if ((gany >> a) & 1u) {
-            const unsigned gm = group_keep(a);
-            append_group(a, gm);
-            need += __builtin_popcount(gm);
-          }
-        }
-        ntot += sum_halves(need);  // outside any condition: every lane takes part
-        return;
-      }
-      // slots running low: one group at a time, keeping the k best first when
-      // the group might not fit (a group adds at most 8; k + 8 + 8 <= slots)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        if ((gany >> a) & 1u) {
-          unsigned gm = group_keep(a);
-          int need = sum_halves(__builtin_popcount(gm));  // the query's new candidates
-          if (wave_any(ntot + need + 8 > kRefineSlots)) {
-            bool cut;
-            const float kth = compact_slots(cs, Kk, cut);
-            if (cut) {
-              tlo = next_up(kth);
-              ntot = Kk;
-            }
-            gm = group_keep(a);
-            need = sum_halves(__builtin_popcount(gm));
-          }
-          append_group(a, gm);
-          ntot += need;
-        }
-      }
-    };
-
-    // stage u: scores two tiles at a time (the second tile's matrix-core
-    // work runs while the first is tested), then the stage swap
-    for (int u = 0; u < n_steps; ++u) {
-#pragma unroll
-      for (int j = 0; j < RSUB; j += 2) {
-        const f32x16 s0 = F::qk(tile_buf(j), r, hf, qf);
-        const f32x16 s1 = F::qk(tile_buf(j + 1), r, hf, qf);
-        tile(u * RSUB + j, s0);
-        tile(u * RSUB + j + 1, s1);
-      }
-      lds_barrier();
-      stage_store(st);
-      stage_load(st, u + 2);
-      lds_barrier();
-    }
-  };
-  if (as_int)
-    sweep(std::integral_constant<bool, true>{});
-  else
-    sweep(std::integral_constant<bool, false>{});
-
-  // rank this lane's candidates against all of the query's and write the first k
-  const int c_me = cs.count(), c_ot = xor_lane(c_me, 32);
-  const int n = c_me + c_ot;
-  if (qvalid) {
-    int32_t* di = p.topk_idx + (qrow * p.n_heads + h) * Kk;
-    float* ds = p.topk_score ? p.topk_score + (qrow * p.n_heads + h) * Kk : nullptr;
-    const int lo0 = hf ? c_ot : c_me;  // the even lane's entries are slots [0, lo0)
-    for (int i0 = 0; i0 < c_me; i0 += 16) {
-      Cand x[16];
-      int rk[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        x[j] = i0 + j < c_me ? cs.buf[cs.slot(i0 + j) * 32 + r] : Cand{-INFINITY, 0x7fffffff};
-        rk[j] = 0;
-      }
-      for (int y = 0; y < n; ++y) {
-        const int sl = y < lo0 ? y : kRefineSlots - 1 - (y - lo0);
-        const Cand cy = cs.buf[sl * 32 + r];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) rk[j] += cand_better(cy, x[j]) ? 1 : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (i0 + j < c_me && rk[j] < Kk) {
-          di[rk[j]] = x[j].j;
-          if (ds) ds[rk[j]] = x[j].s;
-        }
-      }
-    }
-    for (int t = n + hf; t < Kk; t += 2) {
-      di[t] = -1;
-      if (ds) ds[t] = -INFINITY;
-    }
-  }
 }
 
 // Combine split partials: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max).
@@ -844,28 +463,6 @@ static hipError_t launch_flash_dt(int mode, const FlashParams& p, hipStream_t st
 
 hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t stream) {
   return dtype == kBF16 ? launch_flash_dt<__bf16>(mode, p, stream) : launch_flash_dt<float>(mode, p, stream);
-}
-
-template <typename T, int SLOTS>
-static hipError_t launch_refine_s(const RefineParams& p, hipStream_t stream) {
-  constexpr int WAVES = 4;
-  const int64_t blocks = (p.n_q + WAVES * 32 - 1) / (WAVES * 32) * p.n_heads;
-  if (blocks == 0) return hipSuccess;
-  const size_t lds = RSUB * (size_t)Tile<T>::K_ELEMS * sizeof(T) + (size_t)WAVES * SLOTS * 32 * sizeof(Cand);
-  const void* fn = reinterpret_cast<const void*>(&refine_kernel<T, WAVES, SLOTS>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((refine_kernel<T, WAVES, SLOTS>), dim3((unsigned)blocks), dim3(WAVES * 64), lds, stream, p);
-  return hipGetLastError();
-}
-template <typename T>
-static hipError_t launch_refine_t(const RefineParams& p, hipStream_t stream) {
-  if (p.topk <= kRefineSlotsSmall - 16) return launch_refine_s<T, kRefineSlotsSmall>(p, stream);
-  return launch_refine_s<T, kRefineSlotsLarge>(p, stream);
-}
-
-hipError_t launch_refine(int dtype, const RefineParams& p, hipStream_t stream) {
-  return dtype == kBF16 ? launch_refine_t<__bf16>(p, stream) : launch_refine_t<float>(p, stream);
 }
 
 hipError_t launch_merge(int dtype, const MergeParams& p, hipStream_t stream) {

@@ -281,4 +281,24 @@ struct TileLoader {
   }
 };
 
+// Excluded keys of a 32-key tile as a bit mask (bit i = key key0 + i),
+// uniform across the wave, for parameter blocks holding the excluded key
+// ranges n_excl, excl_beg, excl_end (FlashParams, TopkParams).  Tiles are
+// visited in increasing key order, so a cursor passes the ranges that end
+// before the tile once and a tile usually tests no range at all (scalar
+// 32-bit arithmetic: key counts are int32).
+struct ExclCursor {
+  int x = 0;
+  template <typename P>
+  __device__ __forceinline__ uint32_t mask(const P& p, int key0) {
+    while (x < p.n_excl && p.excl_end[x] <= key0) ++x;
+    uint32_t m = 0;
+    for (int y = x; y < p.n_excl && p.excl_beg[y] < key0 + kKT; ++y) {
+      const int lo = max(p.excl_beg[y] - key0, 0), hi = min(p.excl_end[y] - key0, kKT);
+      m |= (hi - lo == kKT ? 0xffffffffu : (1u << (hi - lo)) - 1u) << lo;
+    }
+    return m;
+  }
+};
+
 }  // namespace gsa

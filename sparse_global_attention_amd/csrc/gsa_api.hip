@@ -69,7 +69,9 @@ gsa_status check_cfg(const gsa_config* c, Call* out) {
   g.sb = (g.pool * g.pool + 7) / 8 * 8;
   // window ids are int32 in topk_idx, key positions inside a kernel's key range
   // are int32, and every element count stays well inside int64
-  if (g.n_windows > INT32_MAX || g.m_tokens > INT32_MAX - 64 ||
+  // (per-head rows of window bounds are addressed with 32-bit byte offsets:
+  // M' * 4 < 2^31)
+  if (g.n_windows >= ((int64_t)1 << 29) || g.m_tokens > INT32_MAX - 64 ||
       g.m_tokens > ((int64_t)1 << 40) / (g.n_heads * kHeadDim))
     return GSA_ERR_SHAPE;
 
@@ -112,7 +114,8 @@ struct Plan {
   int n_split;  // special-attention key splits
   int64_t qc, kc, vc, oc, topk, kblk, vblk, spec_o, spec_lse, ctx_o, ctx_lse, total;
   int n_groups, group_tiles;  // compressed step: key-tile groups of the score bounds
-  int64_t gbound;
+  int n_words, cap, n_chunks;  // top-k: hot-mask words, list entries per query, query chunks
+  int64_t gbound, gerr, theta, hot, cnt, cand;
   // backward
   int ctx_qsplits;  // query splits of the context frames' key-side pass
   int64_t qblk, qT, kT, vrow, lse_c, spec_o32, spec_l2, spec_dd, osel, l2sel, doblk, doT, l2blk, dblk,
@@ -156,17 +159,27 @@ int ctx_query_splits(const Call& c) {
   return (int)z;
 }
 
-// Groups of key tiles for the score bounds: at most refine_groups_for_k(k)
-// groups (128 for k <= 48, 512 beyond; a lane of the refine kernel holds half
-// of them), so that the k-th best group bound sits close to the k-th best
-// score and few keys pass it.
+// Groups of key tiles for the score bounds: at most topk_groups_for_k(k)
+// groups, so that the k-th best group bound sits close to the k-th best score
+// and about k groups per query are hot.
 void bound_groups(const Call& c, int* n_groups, int* group_tiles) {
   const int64_t tiles = (c.g.n_windows + 31) / 32;
-  const int64_t target = refine_groups_for_k(c.topk);
+  const int64_t target = topk_groups_for_k(c.topk);
   int64_t gt = (tiles + target - 1) / target;
   if (gt < 1) gt = 1;
   *group_tiles = (int)gt;
   *n_groups = (int)((tiles + gt - 1) / gt);
+}
+// Query chunks of the hot-group pass: a chunk's query rows (128 bytes each in
+// bf16) stay within about 2 MB, so the workgroups of one (head, chunk) that
+// run together on an XCD share them through its L2, and the grid holds at
+// least 4096 workgroups.
+int hot_chunks(const Call& c, int n_groups) {
+  int64_t nc = (c.g.n_windows + 16383) / 16384;
+  const int64_t fill = (4096 + c.g.n_heads * n_groups - 1) / (c.g.n_heads * n_groups);
+  if (nc < fill) nc = fill;
+  if (nc > c.g.n_windows) nc = c.g.n_windows;
+  return (int)(nc < 1 ? 1 : nc);
 }
 
 // Key splits of the special-token attention.  Every workgroup of a split
@@ -207,6 +220,9 @@ Plan make_plan(const Call& c, gsa_op op) {
   memset(&p, 0, sizeof(p));
   p.n_split = special_splits(c);
   bound_groups(c, &p.n_groups, &p.group_tiles);
+  p.n_words = (p.n_groups + 31) / 32;
+  p.cap = topk_list_cap(c.topk);
+  p.n_chunks = hot_chunks(c, p.n_groups);
   const int64_t pooled = g.n_windows * g.n_heads * kHeadDim * c.esz;
   const int64_t blk = g.n_windows * g.n_heads * g.sb * kHeadDim * c.esz;
   const int64_t spec_o = (int64_t)p.n_split * g.m_spec * g.n_heads * kHeadDim * 4;
@@ -226,8 +242,15 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.oc = take(g.n_windows * g.n_heads * kHeadDim * 4);
     p.topk = take(g.n_windows * g.n_heads * (int64_t)c.topk * 4);
   }
-  if (op == GSA_OP_FORWARD || op == GSA_OP_COMPRESSED)
-    p.gbound = take((int64_t)p.n_groups * g.n_heads * g.n_windows * 4);
+  if (op == GSA_OP_FORWARD || op == GSA_OP_COMPRESSED) {
+    const int64_t qh = g.n_heads * g.n_windows;
+    p.gbound = take((int64_t)p.n_groups * qh * 4);
+    p.gerr = take(qh * 4);
+    p.theta = take(qh * 4);
+    p.hot = take((int64_t)p.n_words * qh * 4);
+    p.cnt = take(qh * 4);
+    p.cand = take(qh * p.cap * 8);
+  }
   if (op == GSA_OP_FORWARD || op == GSA_OP_SELECT) {
     p.kblk = take(blk);
     p.vblk = take(blk);
@@ -363,10 +386,11 @@ hipError_t run_special(const Call& c, const Plan& pl, const void* q, const void*
   return launch_merge(c.dtype, m, st);
 }
 
-// Compressed attention + exact top-k (k <= kRefineMaxK = 128), two launches:
+// Compressed attention + exact top-k (k <= kTopkMaxK = 128):
 //  1. flash attention over all M' windows, also writing per-group score bounds;
-//  2. refine_kernel: theta from the bounds, score-only sweep collecting the
-//     keys >= theta, ranking -> topk.
+//  2. launch_topk: theta and the hot groups from the bounds, the hot groups'
+//     keys >= theta as candidates, ranking -> topk (with a full score sweep
+//     for the query tiles whose candidate lists overflow).
 hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const void* kc, const void* vc, float* oc,
                           int32_t* idx, float* score, void* ws, hipStream_t st, float* lse = nullptr) {
   const Geometry& g = c.g;
@@ -396,12 +420,13 @@ hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const v
     }
   }
   f.gbound = reinterpret_cast<float*>(at(ws, pl.gbound));
+  f.gerr = reinterpret_cast<float*>(at(ws, pl.gerr));
   f.n_groups = pl.n_groups;
   f.group_tiles = pl.group_tiles;
   hipError_t e = launch_flash(c.dtype, kFlashBound, f, st);
   if (e != hipSuccess) return e;
 
-  RefineParams r;
+  TopkParams r;
   memset(&r, 0, sizeof(r));
   r.q = qc;
   r.k = kc;
@@ -409,8 +434,17 @@ hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const v
   r.n_heads = f.n_heads;
   r.n_q = g.n_windows;
   r.gbound = f.gbound;
+  r.gerr = f.gerr;
   r.n_groups = pl.n_groups;
+  r.group_tiles = pl.group_tiles;
   r.topk = c.topk;
+  r.theta = reinterpret_cast<float*>(at(ws, pl.theta));
+  r.hot = reinterpret_cast<uint32_t*>(at(ws, pl.hot));
+  r.n_words = pl.n_words;
+  r.cnt = reinterpret_cast<int32_t*>(at(ws, pl.cnt));
+  r.cand = reinterpret_cast<uint2*>(at(ws, pl.cand));
+  r.cap = pl.cap;
+  r.n_chunks = pl.n_chunks;
   r.n_excl = f.n_excl;
   for (int i = 0; i < f.n_excl; ++i) {
     r.excl_beg[i] = f.excl_beg[i];
@@ -418,7 +452,7 @@ hipError_t run_compressed(const Call& c, const Plan& pl, const void* qc, const v
   }
   r.topk_idx = idx;
   r.topk_score = score;
-  return launch_refine(c.dtype, r, st);
+  return launch_topk(c.dtype, r, st);
 }
 
 // Context frames' part of the selection softmax: image queries over all T_f tokens of each context frame.

@@ -54,21 +54,29 @@ hipError_t launch_pool(int dtype, const PoolParams& p, int n_tensors, hipStream_
 constexpr int kMaxRanges = 64;
 constexpr int kMaxExcl = 16;
 // kFlashBound: compressed attention that also records, per group of key
-// tiles, a lower bound of the group's best candidate score (input of
-// refine_kernel, which turns them into the exact top-k, k <= kRefineMaxK).
+// tiles, a lower bound of the group's best candidate score (input of the
+// exact top-k kernels below, k <= kTopkMaxK).
 enum FlashMode { kFlashFinal = 0, kFlashPartial = 1, kFlashBound = 3 };
-// refine_kernel: LDS candidate slots per query.  64 slots (80 KB per
+// refine_kernel (the fallback sweep for queries whose candidate list
+// overflowed): LDS candidate slots per query.  64 slots (80 KB per
 // workgroup, two per CU) serve k <= 48; 144 slots (the whole 160 KB, one
 // workgroup per CU) serve k <= 128.  A query needs its k best + one 4-key
 // group of each lane (8) + 8 spare slots for whole-group writes.
 constexpr int kRefineSlotsSmall = 64;
 constexpr int kRefineSlotsLarge = 144;
-constexpr int kRefineMaxK = kRefineSlotsLarge - 16;
+constexpr int kTopkMaxK = kRefineSlotsLarge - 16;
 // Groups of key tiles for the score bounds (at most; fewer when there are
-// fewer tiles).  The threshold is the k-th largest group bound, so it needs
-// groups well beyond k: 128 for k <= 48, 512 for larger k.
-constexpr int kRefineGroups(int slots) { return slots == kRefineSlotsSmall ? 128 : 512; }
-inline int refine_groups_for_k(int k) { return kRefineGroups(k <= kRefineSlotsSmall - 16 ? kRefineSlotsSmall : kRefineSlotsLarge); }
+// fewer tiles).  The threshold is the k-th largest group bound, so groups
+// must well outnumber k; the more groups, the fewer keys each hot group
+// holds.  8k groups, between 128 and 512.
+inline int topk_groups_for_k(int k) { return k * 8 < 128 ? 128 : k * 8 > 512 ? 512 : k * 8; }
+constexpr int kTopkMaxGroups = 512;
+// Candidate list entries per query: about k + k^2/(2 * groups) keys reach the
+// threshold on unstructured inputs; lists that overflow go to refine_kernel.
+inline int topk_list_cap(int k) {
+  const int c = (2 * k + 32 + 31) / 32 * 32;
+  return c < 64 ? 64 : c;
+}
 
 struct FlashParams {
   const void* q;
@@ -99,30 +107,50 @@ struct FlashParams {
   int n_excl;
   int excl_beg[kMaxExcl], excl_end[kMaxExcl];
   // kFlashBound: gbound [H][n_groups][n_q]; group g covers key tiles
-  // [g*group_tiles, (g+1)*group_tiles) of the single key range
+  // [g*group_tiles, (g+1)*group_tiles) of the single key range; gerr [H][n_q]
+  // receives 4x the largest error term of the query's finite bounds
   float* gbound;
+  float* gerr;
   int n_groups, group_tiles;
 };
 hipError_t launch_flash(int dtype, int mode, const FlashParams& p, hipStream_t stream);
 
-// Exact top-k from the group bounds: theta = k-th best bound per query; a
-// score-only sweep keeps the candidate keys with score >= theta in LDS
-// (compacting to the current k best when the slots run low) and ranks them.
-struct RefineParams {
+// Exact top-k of the compressed step, from the group bounds of the bound sweep:
+//  threshold_kernel  theta = the k-th largest group bound of each query (every
+//                    top-k key scores >= theta), a bit mask of the query's hot
+//                    groups (those whose bound comes within the bound error of
+//                    theta: only they can hold a key scoring >= theta), and
+//                    the list counters (cap + 1 marks a query for the fallback);
+//  hot_group_kernel  per (head, key group): every query for which the group is
+//                    hot is scored against the group's keys; keys >= theta are
+//                    appended to the query's candidate list;
+//  rank_kernel       ranks each list (score desc, key asc), writes the top-k;
+//  refine_kernel     fallback for the query tiles holding a query whose list
+//                    overflowed or whose theta is -inf (fewer than k finite
+//                    bounds): the full score-only sweep with compaction.
+struct TopkParams {
   const void* q;
   const void* k;
   int64_t row_stride;
   int n_heads;
-  int64_t n_q;      // queries = keys = M'
-  const float* gbound;
-  int n_groups;
+  int64_t n_q;          // queries = keys = M'
+  const float* gbound;  // [H][n_groups][n_q] lower bounds of each group's best score
+  const float* gerr;    // [H][n_q] bound on |bound - group max| + rounding slack
+  int n_groups, group_tiles;
   int topk;
-  int n_excl;  // excluded key ranges, as in FlashParams
+  float* theta;         // [H][n_q]
+  uint32_t* hot;        // [H][n_words][n_q], bit g%32 of word g/32: group g is hot
+  int n_words;          // ceil(n_groups / 32)
+  int32_t* cnt;         // [H][n_q] list lengths (> cap: fallback)
+  uint2* cand;          // [H][n_q][cap] (score bits, key)
+  int cap;
+  int n_chunks;         // hot_group_kernel: query chunks per (head, group)
+  int n_excl;           // excluded key ranges, as in FlashParams
   int excl_beg[kMaxExcl], excl_end[kMaxExcl];
-  int32_t* topk_idx;
-  float* topk_score;
+  int32_t* topk_idx;    // [n_q][H][topk]
+  float* topk_score;    // [n_q][H][topk] or null
 };
-hipError_t launch_refine(int dtype, const RefineParams& p, hipStream_t stream);
+hipError_t launch_topk(int dtype, const TopkParams& p, hipStream_t stream);
 
 // Combine split partials into the final rows of o (input dtype).
 struct MergeParams {

@@ -170,6 +170,13 @@ def check_topk(sh, gpu_idx: np.ndarray, orc_idx: np.ndarray, orc_sc: np.ndarray,
     banded = 0
     n, H, _ = gpu_idx.shape
     assert np.all(gpu_idx[..., kp:] == -1), "slots past k' must be -1"
+    # every pick is a candidate window: in range and, when the context frames
+    # are excluded, not one of their windows (checked for every row, in or out
+    # of the tie band)
+    cand = candidate_windows(sh)
+    picks = gpu_idx[..., :kp]
+    assert np.all((picks >= 0) & (picks < sh.n_windows)), "window id out of range"
+    assert np.all(cand[picks]), "a pick is not a candidate window (excluded context frame)"
     for i in range(n):
         for h in range(H):
             g = gpu_idx[i, h, :kp]
@@ -191,6 +198,17 @@ def check_topk(sh, gpu_idx: np.ndarray, orc_idx: np.ndarray, orc_sc: np.ndarray,
             s = gpu_s[i, h, :kp]
             assert np.all(np.diff(s) <= TIE_REL * np.abs(s[:-1]) + TIE_ABS * absmax[i, h] + 1e-12), (i, h, s)
     return banded
+
+
+def candidate_windows(sh) -> np.ndarray:
+    """[M'] mask of the top-k candidate windows: all windows, minus those of the
+    context frames when they are excluded (section "Speed3R-VGGT 适配": the
+    dynamic top-k comes from the non-reference frames)."""
+    cand = np.ones(sh.n_windows, bool)
+    if sh.ctx_exclude:
+        for f in sh.ctx_frames:
+            cand[f * sh.windows_per_frame:(f + 1) * sh.windows_per_frame] = False
+    return cand
 
 
 def same_sets(gpu_idx: np.ndarray, orc_idx: np.ndarray) -> np.ndarray:

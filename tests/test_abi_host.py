@@ -164,6 +164,16 @@ def test_workspace_validation(lib):
     assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, o, o + 4096, None, None, need, None) == 1
 
 
+def test_window_count_limit(lib):
+    """Per-head rows of window bounds are addressed with 32-bit byte offsets,
+    so M' must stay below 2^29 windows: the boundary is rejected on the host."""
+    at = cfg(lib, n_frames=1, n_special=0, grid_h=1 << 14, grid_w=1 << 15, n_heads=1, pool=1, topk=4)
+    assert lib.call_status("gsa_workspace_size", ctypes.byref(at), lib.GSA_OP_FORWARD,
+                           ctypes.byref(ctypes.c_size_t(0))) == lib.GSA_ERR_SHAPE
+    below = cfg(lib, n_frames=1, n_special=0, grid_h=(1 << 14) - 1, grid_w=1 << 15, n_heads=1, pool=1, topk=4)
+    assert lib.gsa_workspace_size(below, lib.GSA_OP_COMPRESSED) > 0
+
+
 def test_binding_raises_gsa_error(lib):
     with pytest.raises(lib.GSAError) as e:
         lib.gsa_workspace_size(cfg(lib, grid_h=7), lib.GSA_OP_FORWARD)

@@ -13,8 +13,8 @@ import torch
 import gen
 import oracle
 from gen.configs import BF16, F32, SMALL_BF16, TINY_F32, GSAShape
-from gsa_testlib import (DEV, Case, assert_close, assert_close_rows, check_topk, same_sets, special_token_ids,
-                         to_dev, to_host, window_image_ids, window_token_ids)
+from gsa_testlib import (DEV, F32_MAX_ABS, Case, assert_close, assert_close_rows, check_topk, same_sets,
+                         special_token_ids, to_dev, to_host, window_image_ids, window_token_ids)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,15 @@ SHAPES = {
     "k40": GSAShape("k40 10f-16x16-h2-s4-k40", 10, 1, 16, 16, 2, 64, 4, 40, BF16, seed=32),
     "k64": GSAShape("k64 10f-16x16-h2-s4-k64", 10, 1, 16, 16, 2, 64, 4, 64, BF16, seed=30),
     "k128": GSAShape("k128 10f-16x16-h1-s4-k128", 10, 1, 16, 16, 1, 64, 4, 128, BF16, seed=31),
+    # enough key tiles for at least k groups: theta is finite and the top-k
+    # comes from the hot groups' candidate lists (the shapes above with fewer
+    # groups than k, or k beyond the candidates, take the full-sweep path)
+    "hot_k4": GSAShape("hot 24f-16x16-h2-s2-k4", 24, 1, 16, 16, 2, 64, 2, 4, BF16, seed=50),
+    "hot_ragged_ctx": GSAShape("hot 20f-12x12-h2-s2-k6+ctx{3,11}", 20, 2, 12, 12, 2, 64, 2, 6, BF16,
+                               ctx_frames=(3, 11), seed=51),
+    "hot_k40": GSAShape("hot 48f-24x24-h1-s4-k40", 48, 1, 24, 24, 1, 64, 4, 40, BF16, seed=52),
+    "hot_k64": GSAShape("hot 64f-16x16-h1-s2-k64", 64, 0, 16, 16, 1, 64, 2, 64, BF16, seed=53),
+    "hot_f32": GSAShape("hot 16f-16x16-h2-s2-k5 fp32", 16, 1, 16, 16, 2, 64, 2, 5, F32, seed=54),
 }
 
 
@@ -230,6 +239,32 @@ def test_topk_ties_beyond_the_candidate_slots(k):
     check_topk(sh, gi, ridx, rsc, amax, oracle.guide_scores(sh, q64, k64, wins, gi))
 
 
+def test_topk_hot_lists_and_full_sweep_mixed():
+    """Query rows of two frames are zero, so their guide scores all tie (at 0)
+    and every key reaches their threshold: their candidate lists overflow and
+    their query tiles take the full sweep (ties to the lower window: the answer
+    is the k lowest windows), while every other query's top-k comes from its
+    hot-group list.  Both must match the oracle."""
+    sh = GSAShape("mixed 24f-16x16-h2-s2-k4", 24, 1, 16, 16, 2, 64, 2, 4, BF16, seed=55)
+    q, k, v, wg = gen.make_inputs(sh)
+    q = q.copy()
+    q[[3, 17]] = 0  # every token of frames 3 and 17 (bf16 +0)
+    c = Case(sh, q=q)
+    qc, kc, vc = c.pool()
+    oc, idx, sc = c.compressed(qc, kc, vc)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    wpf = sh.windows_per_frame
+    zero_rows = np.concatenate([np.arange(3 * wpf, 4 * wpf), np.arange(17 * wpf, 18 * wpf)])
+    assert np.all(gi[zero_rows] == np.arange(sh.topk, dtype=np.int32))
+    wins = np.arange(sh.n_windows)
+    pq, pk, pv = (oracle.pool(sh, x) for x in (c.q, c.k, c.v))
+    roc, ridx, rsc, amax = oracle.compressed(sh, pq, pk, pv, wins)
+    assert np.all(ridx[zero_rows] == np.arange(sh.topk))
+    assert_close(to_host(oc), roc, sh.dtype, "mixed O'_comp")
+    check_topk(sh, gi, ridx, rsc, amax, oracle.guide_scores(sh, pq, pk, wins, gi))
+
+
 @pytest.mark.parametrize("name", ["small_bf16", "odd_f32"])
 def test_dense_comparator_rows(name):
     sh = SHAPES[name]
@@ -299,6 +334,89 @@ def test_scores_growing_along_the_keys():
         w = np.exp(s - s.max(1, keepdims=True))
         ref = (w / w.sum(1, keepdims=True)) @ V[:, h]
         assert_close(gdense[:, h], ref, sh.dtype, f"grow dense head {h}")
+
+
+def test_scores_growing_along_the_keys_fp32():
+    """The growing-key case for fp32 inputs: the fp32 attention template's
+    reference moves (redone tiles, lazy rescales) run against the oracle.
+
+    Tolerance, from fp32 score rounding: a score is a 64-term fp32 matrix-core
+    sum, so |s_gpu - s| <= 64 u sum_d |q_d k_d| (u = 2^-24).  A logit error e
+    moves a softmax output by at most 2 e max|v| (numerator and denominator),
+    so the outputs may differ by 2 scale 64 u max_{q,k} sum_d |q_d k_d| max|v|
+    beyond the plain fp32 tolerance (the pooled tensors' products are
+    smaller, so the same bound covers the compressed branch)."""
+    sh = GSAShape("grow 8f-8x8-h2-s2-k4 fp32", 8, 2, 8, 8, 2, 64, 2, 4, F32, seed=43)
+    c = Case(sh, k=_growing_keys(sh, Case(sh), 150.0))
+    Q, K, V = (gen.to_f32(x, sh.dtype).astype(np.float64).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+               for x in (c.q, c.k, c.v))
+    prod = max(float((np.abs(Q[:, h]) @ np.abs(K[:, h]).T).max()) for h in range(sh.n_heads))
+    tol = F32_MAX_ABS + 2 * 0.125 * 64 * 2.0 ** -24 * prod * float(np.abs(V).max())
+    wins = np.arange(sh.n_windows)
+    gqc, gkc, gvc = c.pool()
+    goc, gidx, gsc = c.compressed(gqc, gkc, gvc)
+    gspec = c.special()
+    gout = c.forward()
+    gdense = to_host(c.dense()).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    torch.cuda.synchronize()
+    qc, kc, vc = (oracle.pool(sh, x) for x in (c.q, c.k, c.v))
+    oc, idx, sc, amax = oracle.compressed(sh, qc, kc, vc, wins)
+    errs = {}
+
+    def close(got, ref, what):
+        err = float(np.abs(np.asarray(got, np.float64) - ref).max())
+        errs[what] = err
+        assert np.all(np.isfinite(got)) and err <= tol, f"{what}: max {err:.3g} > {tol:.3g}"
+
+    close(to_host(goc), oc, "O'_comp")
+    gi = gidx.cpu().numpy()
+    check_topk(sh, gi, idx, sc, amax, oracle.guide_scores(sh, qc, kc, wins, gi))
+    spec = oracle.special(sh, c.q, c.k, c.v, np.arange(sh.m_spec))
+    got = to_host(gspec).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    close(got[special_token_ids(sh)], spec, "O_spec")
+    same = same_sets(gi, idx)
+    assert (~same).sum() <= 2
+    osel = oracle.select(sh, c.q, c.k, c.v, wins, idx)
+    oimg = oracle.gate_combine(sh, c.q, c.wg, wins, oc, osel)
+    got = to_host(gout).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)[window_token_ids(sh)]
+    mask = np.broadcast_to(same[:, None, :, None], got.shape)
+    close(got[mask], oimg[mask], "O_img")
+    for h in range(sh.n_heads):
+        sc_ = Q[:, h] @ K[:, h].T / 8.0
+        w = np.exp(sc_ - sc_.max(1, keepdims=True))
+        close(gdense[:, h], (w / w.sum(1, keepdims=True)) @ V[:, h], f"dense head {h}")
+    print(f"fp32 growing keys: tolerance {tol:.3g}; max errors " +
+          ", ".join(f"{k} {v:.2g}" for k, v in errs.items()))
+
+
+def _special_splits(sh):
+    """The special-token sweep's key-split count, restated from the library's
+    rule (fill the last round of 1024 resident workgroups; at most 64 splits
+    of at least 4 key tiles)."""
+    per = sh.n_heads * ((sh.m_spec + 127) // 128)
+    best, best_t = 1, None
+    for n in range(1, min((sh.m_tokens + 127) // 128, 64) + 1):
+        t = ((per * n + 1023) // 1024) / n
+        if best_t is None or t < best_t * (1 - 1e-9):
+            best, best_t = n, t
+    return best
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "odd_bf16", "odd_f32", "s2_bf16", "hot_k40"])
+def test_special_attention_split_invariance(name):
+    """Special-token attention as split-K partials + merge (the split count
+    the library picks for the shape) against the same rows of the dense
+    comparator, which sweeps all keys in one pass: the split count must not
+    move the result beyond the tolerance."""
+    sh = SHAPES[name]
+    if sh.n_special == 0:
+        pytest.skip("no special tokens")
+    c = Case(sh)
+    spec = to_host(c.special()).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)[special_token_ids(sh)]
+    dense = to_host(c.dense()).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)[special_token_ids(sh)]
+    n = _special_splits(sh)
+    mx, mean, _ = assert_close(spec, dense, sh.dtype, f"{name}: {n} key splits vs one")
+    print(f"{name}: {n} key splits vs one sweep: max {mx:.2e} mean {mean:.2e}")
 
 
 # ---- frame attention (section "整体框架": the per-frame step beside GSA) ----
