@@ -37,8 +37,10 @@
  * Otherwise it enqueues kernels on `stream` (a hipStream_t; NULL = the
  * default stream) of the current device and returns GSA_OK without
  * synchronising.  A failed kernel launch returns GSA_ERR_HIP.  Results are
- * bitwise deterministic for a given configuration and device.  The library
- * keeps no mutable global state, so calls from several threads are safe.
+ * bitwise deterministic for a given configuration and device.  The only
+ * mutable global state is the per-device address table of the static scratch
+ * used by gsa_forward_noalloc (filled once, under a lock), so calls from
+ * several threads are safe (gsa_forward_noalloc: see its contract).
  */
 #ifndef GSA_H_
 #define GSA_H_
@@ -254,6 +256,24 @@ gsa_status gsa_descriptor_set(const gsa_config* cfg, const void* k, const void* 
  * row of o ([N][T_f][H][d]).  No workspace. */
 gsa_status gsa_descriptor_attn(const gsa_config* cfg, const void* q, const void* kd, const void* vd, void* o,
                                void* stream);
+
+/*
+ * The forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and result as gsa_forward, with the workspace taken from a
+ * static device array of GSA_NOALLOC_SCRATCH_BYTES (256 MiB) that each device
+ * holds from the first call until the process ends.  The call allocates
+ * nothing and frees nothing; q, k, v, wg and o are as for gsa_forward.
+ * Returns GSA_ERR_WORKSPACE when the config's GSA_OP_FORWARD workspace is
+ * larger than the array (e.g. 32 frames of 32 x 32 tokens with 16 heads,
+ * s = 4, k = 16 fit; 128 frames of 36 x 36 do not).  Every call on a device
+ * shares that device's array and no kernel relies on its previous contents:
+ * calls that overlap on one device (several streams or host threads) race
+ * and must be serialised by the caller.
+ */
+#define GSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+gsa_status gsa_forward_noalloc(const gsa_config* cfg, const void* q, const void* k, const void* v,
+                               const void* wg, void* o, void* stream);
 
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status status);

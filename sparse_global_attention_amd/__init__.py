@@ -32,7 +32,9 @@ GSA_MAX_CTX_FRAMES = 16
 EXPORTS = ("gsa_workspace_size", "gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn",
            "gsa_special_attn", "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn",
            "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_backward",
-           "gsa_train_state_size", "gsa_forward_train", "gsa_backward_train", "gsa_status_string")
+           "gsa_train_state_size", "gsa_forward_train", "gsa_backward_train", "gsa_forward_noalloc",
+           "gsa_status_string")
+GSA_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class GSAConfig(ctypes.Structure):
@@ -93,6 +95,7 @@ _sig = {
     "gsa_train_state_size": [_CFG, ctypes.POINTER(ctypes.c_size_t)],
     "gsa_forward_train": [_CFG, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_backward_train": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "gsa_forward_noalloc": [_CFG, _P, _P, _P, _P, _P, _P],
 }
 for _name, _args in _sig.items():
     getattr(_lib, _name).argtypes = _args
@@ -223,6 +226,11 @@ def gsa_backward_train(cfg, q, k, v, wg, state, d_o, dq, dk, dv, dwg, ws, ws_byt
     _check(_lib.gsa_backward_train(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(state), _ptr(d_o),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwg), _ptr(ws), wsb, _stream(stream)),
            "gsa_backward_train")
+
+
+def gsa_forward_noalloc(cfg, q, k, v, wg, o, stream=None):
+    _check(_lib.gsa_forward_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(o),
+                                    _stream(stream)), "gsa_forward_noalloc")
 
 
 def call_status(fn: str, *args) -> int:

@@ -5,6 +5,7 @@
 // entry point's contract.
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <string.h>
 
 #include "gsa.h"
@@ -1161,6 +1162,54 @@ gsa_status gsa_backward_train(const gsa_config* cfg, const void* q, const void* 
                               void* ws, size_t ws_bytes, void* stream) {
   if (state == nullptr) return GSA_ERR_INVALID_ARG;
   return backward_impl(cfg, q, k, v, wg, nullptr, state, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- gsa_forward_noalloc: the forward's workspace in a static device array ----
+// Every device the library runs on holds its own copy of `scratch` from the
+// first launch on that device until the process ends.  In host code the name
+// is only a stand-in: the device address comes from hipGetSymbolAddress, once
+// per device, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[GSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+gsa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gsa_status gsa_forward_noalloc(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
+                               void* o, void* stream) {
+  Call c;
+  gsa_status s = check_cfg(cfg, &c);
+  if (s != GSA_OK) return s;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(wg) || !ptr_ok(o)) return GSA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v) return GSA_ERR_INVALID_ARG;
+  const int64_t need = make_plan(c, GSA_OP_FORWARD).total;
+  if (need > (int64_t)GSA_NOALLOC_SCRATCH_BYTES) return GSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != GSA_OK) return s;
+  return forward_impl(cfg, q, k, v, wg, o, nullptr, ws, (size_t)GSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

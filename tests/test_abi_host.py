@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     for want in ("gsa_pool", "gsa_compressed_attn_topk", "gsa_select_attn", "gsa_special_attn",
                  "gsa_gate_combine", "gsa_forward", "gsa_dense_attn", "gsa_frame_attn", "gsa_workspace_size",
                  "gsa_descriptor_count", "gsa_descriptor_set", "gsa_descriptor_attn", "gsa_backward",
-                 "gsa_train_state_size", "gsa_forward_train", "gsa_backward_train", "gsa_status_string"):
+                 "gsa_train_state_size", "gsa_forward_train", "gsa_backward_train", "gsa_forward_noalloc",
+                 "gsa_status_string"):
         assert want in fns
 
 
@@ -162,6 +163,24 @@ def test_workspace_validation(lib):
     n = ctypes.c_size_t(0)
     assert lib.call_status("gsa_train_state_size", c, ctypes.byref(n)) == 0 and n.value > 0
     assert lib.call_status("gsa_compressed_attn_topk", c, A, A, A, o, o + 4096, None, None, need, None) == 1
+
+
+def test_noalloc_forward_validation(lib):
+    """The allocation-free forward rejects, on the host, configs whose forward
+    workspace exceeds its static scratch, and bad pointers, before any launch."""
+    small = cfg(lib)
+    assert lib.gsa_workspace_size(small, lib.GSA_OP_FORWARD) <= lib.GSA_NOALLOC_SCRATCH_BYTES
+    mid = cfg(lib, n_frames=32, n_special=5, grid_h=32, grid_w=32, n_heads=16, pool=4, topk=16)
+    assert lib.gsa_workspace_size(mid, lib.GSA_OP_FORWARD) <= lib.GSA_NOALLOC_SCRATCH_BYTES
+    big = cfg(lib, n_frames=128, n_special=5, grid_h=36, grid_w=36, n_heads=16, pool=4, topk=32)
+    assert lib.gsa_workspace_size(big, lib.GSA_OP_FORWARD) > lib.GSA_NOALLOC_SCRATCH_BYTES
+    o = A + (1 << 20)
+    assert lib.call_status("gsa_forward_noalloc", ctypes.byref(big), A, A, A, A, o, None) == 4
+    c = ctypes.byref(small)
+    assert lib.call_status("gsa_forward_noalloc", c, None, A, A, A, o, None) == 1
+    assert lib.call_status("gsa_forward_noalloc", c, A, A, A, A + 8, o, None) == 1  # wg misaligned
+    assert lib.call_status("gsa_forward_noalloc", c, A, A, A, A, A, None) == 1  # o aliases q
+    assert lib.call_status("gsa_forward_noalloc", ctypes.byref(cfg(lib, grid_h=7)), A, A, A, A, o, None) == 2
 
 
 def test_window_count_limit(lib):
