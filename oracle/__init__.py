@@ -58,8 +58,10 @@ def _load():
         lib.orc_pool.argtypes = [cfgp, P, P]
         lib.orc_special.argtypes = [cfgp, P, P, P, P, I64, P]
         lib.orc_frame.argtypes = [cfgp, P, P, P, P, I64, P]
+        lib.orc_dense.argtypes = [cfgp, P, P, P, P, I64, P]
         lib.orc_backward.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, P, P, P, P, P]
         lib.orc_backward_dq_rows.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, P, P, I64, P]
+        lib.orc_backward_dkdv_rows.argtypes = [cfgp, P, P, P, P, P, ctypes.c_int, P, P, I64, P, P]
         lib.orc_descriptor_count.argtypes = [cfgp]
         lib.orc_descriptor_count.restype = I64
         lib.orc_descriptor_set.argtypes = [cfgp, P, P]
@@ -70,7 +72,8 @@ def _load():
         lib.orc_gate_combine.argtypes = [cfgp, P, P, P, P, I64, P, P, P]
         lib.orc_window_token.argtypes = [cfgp, I64, ctypes.c_int]
         lib.orc_window_token.restype = I64
-        for f in ("orc_pool", "orc_special", "orc_frame", "orc_backward", "orc_backward_dq_rows", "orc_descriptor_set", "orc_descriptor_attn", "orc_compressed", "orc_guide_scores", "orc_select",
+        for f in ("orc_pool", "orc_special", "orc_frame", "orc_dense", "orc_backward", "orc_backward_dq_rows",
+                  "orc_backward_dkdv_rows", "orc_descriptor_set", "orc_descriptor_attn", "orc_compressed", "orc_guide_scores", "orc_select",
                   "orc_gate_combine"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -111,6 +114,15 @@ def special(sh, q, k, v, rows: np.ndarray) -> np.ndarray:
     return out
 
 
+def dense(sh, q, k, v, rows: np.ndarray) -> np.ndarray:
+    """Dense global attention of the listed token rows (special or image) over all tokens
+    -> [n][H][d] float64 (the benchmark comparator's definition)."""
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
+    _load().orc_dense(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(rows), rows.size, _p(out))
+    return out
+
+
 def backward(sh, q, k, v, wg, idx: np.ndarray, d_o):
     """Gradients of sum(d_o * forward(q, k, v, wg)) with the top-k window sets fixed at
     idx [M'][H][k] -> (dq, dk, dv [N][T_f][H][d] float64, dwg [H][d] float64).
@@ -133,6 +145,21 @@ def backward_dq_rows(sh, q, k, v, wg, idx: np.ndarray, d_o, rows: np.ndarray) ->
     _load().orc_backward_dq_rows(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(wg), _p(idx), idx.shape[-1],
                                  _p(np.ascontiguousarray(d_o)), _p(rows), rows.size, _p(out))
     return out
+
+
+def backward_dkdv_rows(sh, q, k, v, wg, idx: np.ndarray, d_o, rows: np.ndarray):
+    """dK and dV of the listed token rows (backward with the top-k sets fixed at idx), per
+    key row, for workloads too large for the whole layer; query rows whose incoming
+    gradient is exactly zero are skipped (they contribute exactly zero), so the cost
+    follows the non-zero rows of d_o -> ([n][H][d], [n][H][d]) float64."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    rows = np.ascontiguousarray(rows, np.int64)
+    assert np.unique(rows).size == rows.size, "rows must be distinct"
+    dk = np.empty((rows.size, sh.n_heads, sh.head_dim), np.float64)
+    dv = np.empty_like(dk)
+    _load().orc_backward_dkdv_rows(ctypes.byref(cfg_of(sh)), _p(q), _p(k), _p(v), _p(wg), _p(idx), idx.shape[-1],
+                                   _p(np.ascontiguousarray(d_o)), _p(rows), rows.size, _p(dk), _p(dv))
+    return dk, dv
 
 
 def frame(sh, q, k, v, rows: np.ndarray) -> np.ndarray:

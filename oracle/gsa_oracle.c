@@ -721,6 +721,217 @@ void orc_backward_dq_rows(const orc_cfg* c, const void* q, const void* k, const 
   for (int x = 0; x < 3; ++x) free(pq[x]);
 }
 
+/* dK and dV of the listed token rows only (the same definition as
+ * orc_backward, evaluated per key row, for workloads too large for the whole
+ * layer).  A key/value row t collects, for head h:
+ *   - from every special query i: scale P_it (dP_it - D_i) q_i and P_it dO_i
+ *     (softmax of q_i over all M tokens, dP_it = dO_i . v_t, D_i = sum_u P_iu dP_iu);
+ *   - from every window i as a compressed query, when t is an image token of
+ *     window j: 1/s^2 of scale P_ij (dP_ij - D_i) Qc_i and of P_ij dOc_i
+ *     (softmax of Qc_i over all M' pooled rows, dOc_i = sum of g dO over the
+ *     tokens of window i, dP_ij = dOc_i . Vc_j);
+ *   - from every image query u whose selection set (the tokens of its
+ *     window's top-k windows, then every token of the context frames) holds
+ *     t, once per occurrence: scale P_ut (dP_ut - D_u) q_u and P_ut dOsel_u
+ *     (dOsel_u = (1 - g_u) dO_u).
+ * A query whose incoming gradient (dO_i, dOc_i or dOsel_u) is exactly zero
+ * contributes exactly zero and is skipped, so the cost follows the rows where
+ * d_o is non-zero.  rows are distinct token ids; dk_out, dv_out: [n][H][d]. */
+/* g = sigmoid(W_g[h] . q_t) of token row t, head h. */
+static double gate_of(const orc_cfg* c, const void* q, const void* wg, int64_t t, int h) {
+  const int d = c->head_dim;
+  double z = 0.0;
+  for (int e = 0; e < d; ++e) z += elem(wg, c->dtype, (int64_t)h * d + e) * elem(q, c->dtype, row_off(c, t, h) + e);
+  return 1.0 / (1.0 + exp(-z));
+}
+
+void orc_backward_dkdv_rows(const orc_cfg* c, const void* q, const void* k, const void* v, const void* wg,
+                            const int32_t* idx, int kcols, const void* d_o, const int64_t* rows, int64_t n,
+                            double* dk_out, double* dv_out) {
+  const int H = c->n_heads, d = c->head_dim, s2 = c->pool * c->pool;
+  const int64_t M = n_tokens(c), tf = tokens_per_frame(c), nw = n_windows(c);
+  const double sc = scale_of(c);
+  const size_t nwel = (size_t)nw * H * d;
+  /* listed[t] = position of token t in rows, or -1 */
+  int64_t* listed = (int64_t*)malloc(sizeof(int64_t) * M);
+  for (int64_t t = 0; t < M; ++t) listed[t] = -1;
+  for (int64_t r = 0; r < n; ++r) listed[rows[r]] = r;
+  for (size_t i = 0; i < (size_t)n * H * d; ++i) dk_out[i] = dv_out[i] = 0.0;
+  /* pooled rows, rounded as in the forward, widened to double */
+  float* pooled = (float*)malloc(sizeof(float) * nwel);
+  double* pq[3];
+  const void* src[3] = {q, k, v};
+  for (int x = 0; x < 3; ++x) {
+    pq[x] = (double*)malloc(sizeof(double) * nwel);
+    orc_pool(c, src[x], pooled);
+    for (size_t i = 0; i < nwel; ++i) pq[x][i] = pooled[i];
+  }
+  free(pooled);
+  const int64_t cap = (M > nw ? M : nw) + (int64_t)kcols * s2 + (int64_t)c->n_ctx * tf;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int h = 0; h < H; ++h) {
+    int64_t* krows = (int64_t*)malloc(sizeof(int64_t) * cap);
+    double* P = (double*)malloc(sizeof(double) * cap);
+    double* dP = (double*)malloc(sizeof(double) * cap);
+    double qrow[512], grow[512], doc[512], dosel[512];
+    /* 1. special queries over all M tokens */
+    for (int64_t f = 0; f < c->n_frames; ++f)
+      for (int pp = 0; pp < c->n_special; ++pp) {
+        const int64_t i = f * tf + pp;
+        int nz = 0;
+        for (int e = 0; e < d; ++e) {
+          qrow[e] = elem(q, c->dtype, row_off(c, i, h) + e);
+          grow[e] = elem(d_o, c->dtype, row_off(c, i, h) + e);
+          nz |= grow[e] != 0.0;
+        }
+        if (!nz) continue;
+        double mx = -INFINITY, den = 0.0, D = 0.0;
+        for (int64_t t = 0; t < M; ++t) {
+          double sdot = 0.0, gdot = 0.0;
+          for (int e = 0; e < d; ++e) {
+            sdot += qrow[e] * elem(k, c->dtype, row_off(c, t, h) + e);
+            gdot += grow[e] * elem(v, c->dtype, row_off(c, t, h) + e);
+          }
+          P[t] = sc * sdot;
+          dP[t] = gdot;
+          if (P[t] > mx) mx = P[t];
+        }
+        for (int64_t t = 0; t < M; ++t) {
+          P[t] = exp(P[t] - mx);
+          den += P[t];
+        }
+        for (int64_t t = 0; t < M; ++t) {
+          P[t] /= den;
+          D += P[t] * dP[t];
+        }
+        for (int64_t r = 0; r < n; ++r) {
+          const int64_t t = rows[r];
+          const double ds = P[t] * (dP[t] - D);
+          for (int e = 0; e < d; ++e) {
+            dk_out[(r * H + h) * d + e] += sc * ds * qrow[e];
+            dv_out[(r * H + h) * d + e] += P[t] * grow[e];
+          }
+        }
+      }
+    /* 2. windows as compressed queries over all M' pooled rows */
+    for (int64_t j = 0; j < nw; ++j) krows[j] = j;
+    for (int64_t i = 0; i < nw; ++i) {
+      int nz = 0;
+      for (int e = 0; e < d; ++e) doc[e] = 0.0;
+      for (int kk = 0; kk < s2; ++kk) {
+        const int64_t tt = window_token(c, i, kk);
+        const double g = gate_of(c, q, wg, tt, h);
+        for (int e = 0; e < d; ++e) doc[e] += g * elem(d_o, c->dtype, row_off(c, tt, h) + e);
+      }
+      for (int e = 0; e < d; ++e) nz |= doc[e] != 0.0;
+      if (!nz) continue;
+      softmax_weights(d, H, h, sc, pq[0] + (i * H + h) * d, pq[1], krows, nw, P);
+      double D = 0.0;
+      for (int64_t j = 0; j < nw; ++j) {
+        dP[j] = dot_d(doc, pq[2] + (j * H + h) * d, d);
+        D += P[j] * dP[j];
+      }
+      for (int64_t r = 0; r < n; ++r) {
+        const int64_t t = rows[r], f = t / tf, p = t % tf;
+        if (p < c->n_special) continue;
+        const int64_t pix = p - c->n_special, y = pix / c->grid_w, x = pix % c->grid_w;
+        const int64_t j = f * windows_per_frame(c) + (y / c->pool) * windows_x(c) + x / c->pool;
+        const double ds = P[j] * (dP[j] - D);
+        for (int e = 0; e < d; ++e) {
+          dk_out[(r * H + h) * d + e] += sc * ds * pq[0][(i * H + h) * d + e] / s2;
+          dv_out[(r * H + h) * d + e] += P[j] * doc[e] / s2;
+        }
+      }
+    }
+    /* 3. image queries over their selection sets (+ context) */
+    for (int64_t i = 0; i < nw; ++i) {
+      int64_t nt = 0;
+      for (int tt = 0; tt < kcols; ++tt) {
+        const int32_t j = idx[(i * H + h) * kcols + tt];
+        if (j < 0 || j >= nw) continue;
+        for (int kk = 0; kk < s2; ++kk) krows[nt++] = window_token(c, j, kk);
+      }
+      for (int cf = 0; cf < c->n_ctx; ++cf)
+        for (int64_t pp = 0; pp < tf; ++pp) krows[nt++] = (int64_t)c->ctx_frames[cf] * tf + pp;
+      for (int qq = 0; qq < s2; ++qq) {
+        const int64_t u = window_token(c, i, qq);
+        int nz = 0;
+        for (int e = 0; e < d; ++e) {
+          grow[e] = elem(d_o, c->dtype, row_off(c, u, h) + e);
+          nz |= grow[e] != 0.0;
+        }
+        if (!nz) continue;
+        const double g = gate_of(c, q, wg, u, h);
+        for (int e = 0; e < d; ++e) {
+          qrow[e] = elem(q, c->dtype, row_off(c, u, h) + e);
+          dosel[e] = (1.0 - g) * grow[e];
+        }
+        double mx = -INFINITY, den = 0.0, D = 0.0;
+        for (int64_t e2 = 0; e2 < nt; ++e2) {
+          double sdot = 0.0, gdot = 0.0;
+          for (int e = 0; e < d; ++e) {
+            sdot += qrow[e] * elem(k, c->dtype, row_off(c, krows[e2], h) + e);
+            gdot += dosel[e] * elem(v, c->dtype, row_off(c, krows[e2], h) + e);
+          }
+          P[e2] = sc * sdot;
+          dP[e2] = gdot;
+          if (P[e2] > mx) mx = P[e2];
+        }
+        for (int64_t e2 = 0; e2 < nt; ++e2) {
+          P[e2] = exp(P[e2] - mx);
+          den += P[e2];
+        }
+        for (int64_t e2 = 0; e2 < nt; ++e2) {
+          P[e2] /= den;
+          D += P[e2] * dP[e2];
+        }
+        for (int64_t e2 = 0; e2 < nt; ++e2) {
+          const int64_t r = listed[krows[e2]];
+          if (r < 0) continue;
+          const double ds = P[e2] * (dP[e2] - D);
+          for (int e = 0; e < d; ++e) {
+            dk_out[(r * H + h) * d + e] += sc * ds * qrow[e];
+            dv_out[(r * H + h) * d + e] += P[e2] * dosel[e];
+          }
+        }
+      }
+    }
+    free(krows);
+    free(P);
+    free(dP);
+  }
+  for (int x = 0; x < 3; ++x) free(pq[x]);
+  free(listed);
+}
+
+/* Dense global attention, the attention GSA replaces (Paper-Notes page,
+ * section "研究背景与动机"): each listed token (special or image) attends,
+ * in one softmax with the config scale, to all M tokens.  rows are token
+ * ids t in [0, M); out: [n][H][d].  (For the benchmark comparator's
+ * sampled rows.) */
+void orc_dense(const orc_cfg* c, const void* q, const void* k, const void* v, const int64_t* rows, int64_t n,
+               double* out) {
+  const int H = c->n_heads, d = c->head_dim;
+  const int64_t M = n_tokens(c);
+#pragma omp parallel
+  {
+    int64_t* toks = (int64_t*)malloc(sizeof(int64_t) * M);
+    double* logits = (double*)malloc(sizeof(double) * M);
+    double* qrow = (double*)malloc(sizeof(double) * d);
+    for (int64_t t = 0; t < M; ++t) toks[t] = t;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t ih = 0; ih < n * H; ++ih) {
+      const int64_t i = ih / H;
+      const int h = (int)(ih % H);
+      for (int e = 0; e < d; ++e) qrow[e] = elem(q, c->dtype, row_off(c, rows[i], h) + e);
+      attend_tokens(c, qrow, k, v, toks, M, h, logits, out + (i * H + h) * d);
+    }
+    free(toks);
+    free(logits);
+    free(qrow);
+  }
+}
+
 /* ======================================================================== */
 /* Frame attention: the local step that alternates with GSA in the
  * aggregation transformer (Paper-Notes page, section "整体框架": blocks

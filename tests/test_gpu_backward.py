@@ -4,9 +4,11 @@ gradients.  The top-k window sets both sides hold fixed come from the
 oracle's own top-k of the same inputs (or, at full size, from a seeded
 generator), so no oracle input comes from the GPU.  At the full workload
 sizes (too large for the whole-layer oracle) dq is checked on sampled rows
-the oracle evaluates one by one, and dK/dV through properties that hold at
-any size: sum_t dV_t = sum_t dO_t and sum_t dK_t = 0 per head and channel;
-plus finite values and determinism.
+the oracle evaluates one by one, dK/dV on listed rows for an output gradient
+that is non-zero on a few rows only (the oracle then evaluates those rows one
+by one too), and through properties that hold at any size: sum_t dV_t =
+sum_t dO_t and sum_t dK_t = 0 per head and channel; plus finite values and
+determinism.
 """
 import numpy as np
 import pytest
@@ -157,6 +159,64 @@ def test_backward_full_size(sh):
     torch.cuda.synchronize()
     for x, y in zip(first, (dq_, dk_, dv_, dwg_)):
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1100)
+@pytest.mark.parametrize("sh", [VGGT_CTX, PI3_LONG], ids=["vggt_ctx", "pi3_long"])
+def test_backward_full_size_dkdv_rows(sh):
+    """dK and dV rows at the full sizes.  The output gradient is the seeded one on
+    a few rows (6 special tokens and every token of 24 windows) and zero
+    elsewhere: the backward is linear in dO, so every key row's gradient is
+    still defined, and the oracle evaluates listed key rows one by one from
+    the non-zero rows only.  Listed rows: every token of the windows that the
+    top-k sets of two of those windows select (all heads; they receive the
+    selection-branch gradients through the inverse top-k lists), tokens of the
+    context frames, special tokens and random rows -- so a contribution routed
+    to a wrong key row shows up.  Seeded window sets, the same on both sides."""
+    from gsa_testlib import Case
+    rng = np.random.default_rng(sh.seed + 21)
+    idx = rng.integers(0, sh.n_windows, size=(sh.n_windows, sh.n_heads, sh.topk)).astype(np.int32)
+    if sh.ctx_frames and sh.ctx_exclude:  # candidates only (any sets define the backward; keep them valid)
+        wpf = sh.windows_per_frame
+        bad = np.isin(idx // wpf, sh.ctx_frames)
+        idx[bad] = (idx[bad] + wpf) % sh.n_windows
+        assert not np.isin(idx // wpf, sh.ctx_frames).any()
+    c = Case(sh)
+    tf = sh.tokens_per_frame
+    grid = np.arange(sh.m_tokens).reshape(sh.n_frames, tf)
+    wtok = grid[:, sh.n_special:].reshape(sh.n_frames, sh.grid_h // sh.pool, sh.pool, sh.grid_w // sh.pool, sh.pool)
+    wtok = wtok.transpose(0, 1, 3, 2, 4).reshape(sh.n_windows, sh.pool ** 2)
+    wins = rng.choice(sh.n_windows, 24, replace=False)
+    keep = np.zeros(sh.m_tokens, bool)
+    keep[wtok[wins].reshape(-1)] = True
+    keep[rng.choice(sh.n_frames, 6, replace=False) * tf + rng.integers(0, sh.n_special, 6)] = True
+    d_o_h = gen.make_output_grad(sh).reshape(sh.m_tokens, -1).copy()
+    d_o_h[~keep] = 0
+    d_o_h = d_o_h.reshape(sh.qkv_shape)
+    d_o = to_dev(d_o_h, sh.dtype)
+    dq_, dk_, dv_ = (torch.empty(sh.qkv_shape, dtype=torch.float32, device=DEV) for _ in range(3))
+    dwg_ = torch.empty((sh.n_heads, sh.head_dim), dtype=torch.float32, device=DEV)
+    ws = workspace(c.cfg, gsa.GSA_OP_BACKWARD)
+    gsa.gsa_backward(c.cfg, c.dq, c.dk, c.dv, c.dwg, torch.from_numpy(idx).to(DEV), d_o, dq_, dk_, dv_, dwg_, ws)
+    torch.cuda.synchronize()
+    del ws
+    selected = np.unique(idx[wins[:2]].reshape(-1))
+    parts = [wtok[selected].reshape(-1), rng.choice(sh.m_tokens, 512, replace=False),
+             grid[:, :sh.n_special].reshape(-1)[:64], wtok[wins[:2]].reshape(-1)]
+    for f in sh.ctx_frames:
+        parts.append(f * tf + rng.choice(tf, 128, replace=False))
+    rows = np.unique(np.concatenate(parts))
+    shp = (sh.m_tokens, sh.n_heads, sh.head_dim)
+    sel = torch.from_numpy(rows).to(DEV)
+    got_k = dk_.view(shp).index_select(0, sel).cpu().numpy()
+    got_v = dv_.view(shp).index_select(0, sel).cpu().numpy()
+    ref_k, ref_v = oracle.backward_dkdv_rows(sh, c.q, c.k, c.v, c.wg, idx, d_o_h, rows)
+    for got, ref, what in ((got_k, ref_k, "dK"), (got_v, ref_v, "dV")):
+        mx, mean = assert_grad_close(got, ref, sh.dtype, f"{sh.name} sampled {what} rows")
+        nz = int((np.abs(ref).max(axis=(1, 2)) > 0).sum())
+        print(f"{sh.name}: {what} of {rows.size} rows ({nz} with non-zero gradients) max {mx:.3g} "
+              f"mean {mean:.3g} of the largest |ref|")
 
 
 # ---- the training pair: forward saving its state, backward reading it ----------

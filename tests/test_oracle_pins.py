@@ -111,6 +111,24 @@ def test_special_equals_dense_attention(dtype):
         np.testing.assert_allclose(got[:, h], ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_dense_rows_equal_sdpa_over_all_tokens(dtype):
+    """Dense global attention (the benchmark comparator's definition) of listed
+    rows, special and image, in any order: float64 SDPA over every token."""
+    sh = shape(n_special=2, dtype=dtype)
+    q, k, v, _ = gen.make_inputs(sh)
+    rows = np.random.default_rng(4).permutation(sh.m_tokens)[:40]
+    got = oracle.dense(sh, q, k, v, rows)
+    Q, K, V = flat(q, sh), flat(k, sh), flat(v, sh)
+    for h in range(sh.n_heads):
+        ref = sdpa(Q[rows, h], K[:, h], V[:, h], sh.head_dim ** -0.5)
+        np.testing.assert_allclose(got[:, h], ref, rtol=0, atol=1e-12)
+    # the special rows equal the special-token attention's
+    spec = special_token_ids(sh)
+    np.testing.assert_allclose(oracle.dense(sh, q, k, v, spec), oracle.special(sh, q, k, v, np.arange(sh.m_spec)),
+                               rtol=0, atol=1e-14)
+
+
 def test_special_custom_scale_is_applied():
     sh = shape(n_special=2)
     q, k, v, _ = gen.make_inputs(sh)
@@ -522,7 +540,7 @@ def _fixed_topk(sh, seed):
     """A valid top-k set per (window, head): distinct candidate windows, -1 padded."""
     rng = np.random.default_rng(seed)
     wpf = (sh.grid_h // sh.pool) * (sh.grid_w // sh.pool)
-    cand = np.array([j for j in range(sh.n_windows) if j // wpf not in sh.ctx_frames])
+    cand = np.array([j for j in range(sh.n_windows) if not (sh.ctx_exclude and j // wpf in sh.ctx_frames)])
     kk = min(sh.topk, cand.size)
     idx = np.full((sh.n_windows, sh.n_heads, sh.topk), -1, np.int32)
     for i in range(sh.n_windows):
@@ -657,3 +675,45 @@ def test_backward_dq_rows_equal_the_whole_layer_backward(kw):
     rows = np.arange(sh.m_tokens)
     got = oracle.backward_dq_rows(sh, q, k, v, wg, idx, d_o, rows)
     np.testing.assert_allclose(got, dq[rows], rtol=0, atol=1e-12 * max(1.0, np.abs(dq).max()))
+
+
+def _sparse_output_grad(sh, d_o, seed):
+    """d_o with most rows set to zero: a few special rows and the tokens of a
+    few windows keep their seeded values."""
+    rng = np.random.default_rng(seed)
+    keep = np.zeros(sh.m_tokens, bool)
+    tf = sh.tokens_per_frame
+    if sh.n_special:
+        keep[rng.choice(sh.n_frames, 2) * tf + rng.integers(0, sh.n_special, 2)] = True
+    img = np.arange(sh.m_tokens).reshape(sh.n_frames, tf)[:, sh.n_special:]
+    keep[rng.choice(img.reshape(-1), 5, replace=False)] = True
+    out = d_o.copy().reshape(sh.m_tokens, -1)
+    out[~keep] = 0
+    return out.reshape(d_o.shape)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(ctx_frames=(1,), topk=2, dtype=BF16), dict(n_special=0, pool=4, topk=2),
+                                dict(n_frames=3, ctx_frames=(0, 2), ctx_exclude=0, topk=3)])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_backward_dkdv_rows_equal_the_whole_layer_backward(kw, sparse):
+    """The per-row dK/dV (for full-size checks) are the whole-layer backward's,
+    which the autograd and difference pins above fix, for a dense output
+    gradient and for one that is zero on most rows (the per-row version skips
+    queries with a zero incoming gradient); rows listed in a shuffled order.
+    With ctx_exclude = 0 a context frame's windows may also be selected, so a
+    key can sit twice in one selection set."""
+    sh = shape(**kw)
+    q, k, v, wg = gen.make_inputs(sh)
+    d_o = gen.make_output_grad(sh)
+    if sparse:
+        d_o = _sparse_output_grad(sh, d_o, 13)
+    idx = _fixed_topk(sh, 10)
+    _, dk, dv, _ = oracle.backward(sh, q, k, v, wg, idx, d_o)
+    dk = dk.reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    dv = dv.reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    rows = np.random.default_rng(3).permutation(sh.m_tokens)
+    gk, gv = oracle.backward_dkdv_rows(sh, q, k, v, wg, idx, d_o, rows)
+    np.testing.assert_allclose(gk, dk[rows], rtol=0, atol=1e-12 * max(1.0, np.abs(dk).max()))
+    np.testing.assert_allclose(gv, dv[rows], rtol=0, atol=1e-12 * max(1.0, np.abs(dv).max()))
+    if sparse:
+        assert np.abs(dk).max() > 0 and np.abs(dv).max() > 0
