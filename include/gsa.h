@@ -196,14 +196,16 @@ gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, con
  * (workspace: GSA_OP_FORWARD bytes).  gsa_backward_train computes what
  * gsa_backward computes for the state's top-k sets, from the saved
  * quantities (workspace: GSA_OP_BACKWARD bytes; the state must come from
- * gsa_forward_train on the same inputs and config).
+ * gsa_forward_train on the same inputs and config).  Both calls take the
+ * state's size in bytes and return GSA_ERR_WORKSPACE, without touching the
+ * device, when it is smaller than gsa_train_state_size.
  */
 gsa_status gsa_train_state_size(const gsa_config* cfg, size_t* bytes);
 gsa_status gsa_forward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
-                             void* o, void* state, void* ws, size_t ws_bytes, void* stream);
+                             void* o, void* state, size_t state_bytes, void* ws, size_t ws_bytes, void* stream);
 gsa_status gsa_backward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
-                              const void* state, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
-                              void* ws, size_t ws_bytes, void* stream);
+                              const void* state, size_t state_bytes, const void* d_o, float* dq, float* dk,
+                              float* dv, float* dwg, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Dense global attention of all M tokens over all M tokens at the same shape

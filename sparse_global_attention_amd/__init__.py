@@ -93,8 +93,9 @@ _sig = {
     "gsa_descriptor_attn": [_CFG, _P, _P, _P, _P, _P],
     "gsa_backward": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsa_train_state_size": [_CFG, ctypes.POINTER(ctypes.c_size_t)],
-    "gsa_forward_train": [_CFG, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
-    "gsa_backward_train": [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "gsa_forward_train": [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P],
+    "gsa_backward_train": [_CFG, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                           _P],
     "gsa_forward_noalloc": [_CFG, _P, _P, _P, _P, _P, _P],
 }
 for _name, _args in _sig.items():
@@ -215,16 +216,19 @@ def gsa_train_state_size(cfg) -> int:
     return out.value
 
 
-def gsa_forward_train(cfg, q, k, v, wg, o, state, ws, ws_bytes=None, stream=None):
+def gsa_forward_train(cfg, q, k, v, wg, o, state, ws, ws_bytes=None, stream=None, state_bytes=None):
     wsb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    stb = _nbytes(state) if state_bytes is None else state_bytes
     _check(_lib.gsa_forward_train(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(o), _ptr(state),
-                                  _ptr(ws), wsb, _stream(stream)), "gsa_forward_train")
+                                  stb, _ptr(ws), wsb, _stream(stream)), "gsa_forward_train")
 
 
-def gsa_backward_train(cfg, q, k, v, wg, state, d_o, dq, dk, dv, dwg, ws, ws_bytes=None, stream=None):
+def gsa_backward_train(cfg, q, k, v, wg, state, d_o, dq, dk, dv, dwg, ws, ws_bytes=None, stream=None,
+                       state_bytes=None):
     wsb = _nbytes(ws) if ws_bytes is None else ws_bytes
-    _check(_lib.gsa_backward_train(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(state), _ptr(d_o),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwg), _ptr(ws), wsb, _stream(stream)),
+    stb = _nbytes(state) if state_bytes is None else state_bytes
+    _check(_lib.gsa_backward_train(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(wg), _ptr(state), stb,
+                                   _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dwg), _ptr(ws), wsb, _stream(stream)),
            "gsa_backward_train")
 
 

@@ -618,7 +618,7 @@ namespace {
 
 // gsa_forward and gsa_forward_train (state: the training state, or null).
 gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg, void* o,
-                        void* state, void* ws, size_t ws_bytes, void* stream) {
+                        void* state, size_t state_bytes, void* ws, size_t ws_bytes, void* stream) {
   Call c;
   gsa_status s = check_cfg(cfg, &c);
   if (s != GSA_OK) return s;
@@ -630,6 +630,7 @@ gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, con
   if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const TrainState ts = state_plan(c);
+  if (state && (int64_t)state_bytes < ts.total) return GSA_ERR_WORKSPACE;
   auto saved = [&](int64_t off) { return state ? reinterpret_cast<float*>(at(state, off)) : nullptr; };
 
   // 1. pooling of Q/K/V plus the blocked K / transposed-V copies for the gather
@@ -672,7 +673,7 @@ extern "C" {
 
 gsa_status gsa_forward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg, void* o,
                        void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(cfg, q, k, v, wg, o, nullptr, ws, ws_bytes, stream);
+  return forward_impl(cfg, q, k, v, wg, o, nullptr, 0, ws, ws_bytes, stream);
 }
 
 gsa_status gsa_train_state_size(const gsa_config* cfg, size_t* bytes) {
@@ -685,9 +686,9 @@ gsa_status gsa_train_state_size(const gsa_config* cfg, size_t* bytes) {
 }
 
 gsa_status gsa_forward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
-                             void* o, void* state, void* ws, size_t ws_bytes, void* stream) {
+                             void* o, void* state, size_t state_bytes, void* ws, size_t ws_bytes, void* stream) {
   if (state == nullptr) return GSA_ERR_INVALID_ARG;
-  return forward_impl(cfg, q, k, v, wg, o, state, ws, ws_bytes, stream);
+  return forward_impl(cfg, q, k, v, wg, o, state, state_bytes, ws, ws_bytes, stream);
 }
 
 gsa_status gsa_dense_attn(const gsa_config* cfg, const void* q, const void* k, const void* v, void* o, void* ws,
@@ -779,14 +780,15 @@ namespace {
 // gsa_backward (state null: the forward quantities are recomputed) and
 // gsa_backward_train (top-k sets and forward quantities read from the state).
 gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
-                         const int32_t* topk_idx, const void* state, const void* d_o, float* dq, float* dk,
-                         float* dv, float* dwg, void* ws, size_t ws_bytes, void* stream) {
+                         const int32_t* topk_idx, const void* state, size_t state_bytes, const void* d_o, float* dq,
+                         float* dk, float* dv, float* dwg, void* ws, size_t ws_bytes, void* stream) {
   Call c;
   gsa_status s = check_cfg(cfg, &c);
   if (s != GSA_OK) return s;
   const TrainState ts = state_plan(c);
   if (state) {
     if (((uintptr_t)state & (kAlign - 1)) != 0) return GSA_ERR_INVALID_ARG;
+    if ((int64_t)state_bytes < ts.total) return GSA_ERR_WORKSPACE;
     topk_idx = reinterpret_cast<const int32_t*>(at(const_cast<void*>(state), ts.topk));
   }
   auto saved = [&](int64_t off) { return reinterpret_cast<float*>(at(const_cast<void*>(state), off)); };
@@ -1154,14 +1156,14 @@ extern "C" {
 gsa_status gsa_backward(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
                         const int32_t* topk_idx, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
                         void* ws, size_t ws_bytes, void* stream) {
-  return backward_impl(cfg, q, k, v, wg, topk_idx, nullptr, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream);
+  return backward_impl(cfg, q, k, v, wg, topk_idx, nullptr, 0, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream);
 }
 
 gsa_status gsa_backward_train(const gsa_config* cfg, const void* q, const void* k, const void* v, const void* wg,
-                              const void* state, const void* d_o, float* dq, float* dk, float* dv, float* dwg,
-                              void* ws, size_t ws_bytes, void* stream) {
+                              const void* state, size_t state_bytes, const void* d_o, float* dq, float* dk, float* dv,
+                              float* dwg, void* ws, size_t ws_bytes, void* stream) {
   if (state == nullptr) return GSA_ERR_INVALID_ARG;
-  return backward_impl(cfg, q, k, v, wg, nullptr, state, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream);
+  return backward_impl(cfg, q, k, v, wg, nullptr, state, state_bytes, d_o, dq, dk, dv, dwg, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
@@ -1209,7 +1211,7 @@ gsa_status gsa_forward_noalloc(const gsa_config* cfg, const void* q, const void*
   if (need > (int64_t)GSA_NOALLOC_SCRATCH_BYTES) return GSA_ERR_WORKSPACE;
   void* ws = nullptr;
   if ((s = scratch_address(&ws)) != GSA_OK) return s;
-  return forward_impl(cfg, q, k, v, wg, o, nullptr, ws, (size_t)GSA_NOALLOC_SCRATCH_BYTES, stream);
+  return forward_impl(cfg, q, k, v, wg, o, nullptr, 0, ws, (size_t)GSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -147,15 +147,22 @@ def test_workspace_validation(lib):
     bw = [A + 16 * i for i in range(6)] + [o, o + 4096, o + 8192, o + 12288]
     assert lib.call_status("gsa_backward", c, *bw, A, need - 1, None) == 4
     assert lib.call_status("gsa_backward", c, *bw, None, need, None) == 1
-    # the training pair: a null, misaligned or aliased state is rejected before any launch
+    # the training pair: a null, misaligned, aliased or undersized state is
+    # rejected before any launch
     need_f = lib.gsa_workspace_size(cc, lib.GSA_OP_FORWARD)
+    sb = lib.gsa_train_state_size(cc)
     st = A + (1 << 24)
-    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, None, A, need_f, None) == 1
-    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st + 16, A, need_f, None) == 1
-    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, o, A, need_f, None) == 1
-    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st, A, need_f - 1, None) == 4
-    tr = [A, A + 16, A + 32, A + 48, st, A + 64, o, o + 4096, o + 8192, o + 12288]
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, None, sb, A, need_f, None) == 1
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st + 16, sb, A, need_f, None) == 1
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, o, sb, A, need_f, None) == 1
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st, sb, A, need_f - 1, None) == 4
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st, sb - 1, A, need_f, None) == 4
+    assert lib.call_status("gsa_forward_train", c, A, A, A, A, o, st, 0, A, need_f, None) == 4
+    tr = [A, A + 16, A + 32, A + 48, st, sb, A + 64, o, o + 4096, o + 8192, o + 12288]
     assert lib.call_status("gsa_backward_train", c, *tr, A, need - 1, None) == 4
+    tr[5] = sb - 1
+    assert lib.call_status("gsa_backward_train", c, *tr, A, need, None) == 4
+    tr[5] = sb
     tr[4] = None
     assert lib.call_status("gsa_backward_train", c, *tr, A, need, None) == 1
     tr[4] = o  # the state aliasing dq
