@@ -81,6 +81,11 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
 
   const int64_t qrow = qt * QW + wv * 32 + r;
   const bool qvalid = qrow < p.n_q;
+  // A wave whose 32 query rows all lie past the end (the last query tile of a
+  // batch, e.g. 21 of a frame's 128-row tail tile) still loads its share of
+  // every key tile and meets the others at each barrier, but skips the
+  // matrix-core and softmax work, leaving its SIMD to the other workgroups.
+  const bool wave_live = wave_any(qvalid);
   const int64_t hoff = (int64_t)h * kHeadDim;
   const int64_t qtok = batch * p.q_bstride + (qrow / p.qa) * p.qb + p.qc + qrow % p.qa;
   const T* K = static_cast<const T*>(p.k);
@@ -129,6 +134,7 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   // One tile t from the K/V tile at kt (V follows K).  A step past the last
   // tile (the loops below run in whole unrolled rounds) sees only masked keys.
   auto compute = [&](int t, const T* kt) __attribute__((always_inline)) {
+    if (!wave_live) return;
     const int64_t cur0 = kb + (int64_t)t * kKT;
     const T* vt = kt + TL::K_ELEMS;
     f32x16 s = F::qk(kt, r, hf, qf);

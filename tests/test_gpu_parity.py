@@ -442,6 +442,67 @@ def test_frame_attention(name):
     assert_close(got[rows], ref, sh.dtype, f"{name} frame attention")
 
 
+def _forward_rows_vs_oracle(sh, gout, res, gidx, what):
+    """The forward's rows against the oracle's: every special row, and the image
+    rows of (window, head) pairs whose GPU top-k set equals the oracle's (the
+    others must be rare: valid choices inside a tie)."""
+    same = same_sets(gidx, res["topk"])
+    assert same.mean() >= 0.99, f"{what}: {(~same).sum()} rows with other sets"
+    got = to_host(gout).reshape(sh.m_tokens, sh.n_heads, sh.head_dim)
+    ref = res["o"].reshape(got.shape)
+    assert_close_rows(got[window_token_ids(sh)], ref[window_token_ids(sh)], same, sh.dtype, f"{what} O_img")
+    if sh.m_spec:
+        assert_close(got[special_token_ids(sh)], ref[special_token_ids(sh)], sh.dtype, f"{what} O_spec")
+
+
+def test_frame_attention_then_gsa_in_sequence():
+    """One alternating pair (section "整体框架": blocks alternate intra-frame
+    attention and GSA), launched back to back on one stream with no host
+    synchronisation in between, each step against the oracle.
+
+    fp32 chain: GSA's queries are the frame attention's output times 32 (an
+    exact power of two standing in for the projection between the two steps);
+    the oracle runs the same chain on its own frame output, rounded to fp32,
+    so the two sides' inputs to GSA differ only by fp32 rounding -- far inside
+    the top-k tie band.  bf16: frame attention, then GSA on the seeded inputs,
+    in one stream."""
+    import sparse_global_attention_amd as gsa
+    sh = GSAShape("chain 6f-16x16-h2-s4-k5 fp32", 6, 2, 16, 16, 2, 64, 4, 5, F32, seed=56)
+    c = Case(sh)
+    of = torch.empty_like(c.dq)
+    gsa.gsa_frame_attn(c.cfg, c.dq, c.dk, c.dv, of)
+    q2 = of * 32.0
+    o = torch.zeros_like(c.dq)
+    ws = torch.empty(gsa.gsa_workspace_size(c.cfg, gsa.GSA_OP_FORWARD), dtype=torch.uint8, device=DEV)
+    gsa.gsa_forward(c.cfg, q2, c.dk, c.dv, c.dwg, o, ws)
+    shp = (sh.n_windows, sh.n_heads, sh.head_dim)
+    qc, kc, vc = (torch.empty(shp, dtype=torch.float32, device=DEV) for _ in range(3))
+    gsa.gsa_pool(c.cfg, q2, c.dk, c.dv, qc, kc, vc)
+    oc = torch.empty(shp, dtype=torch.float32, device=DEV)
+    idx = torch.empty((sh.n_windows, sh.n_heads, sh.topk), dtype=torch.int32, device=DEV)
+    gsa.gsa_compressed_attn_topk(c.cfg, qc, kc, vc, oc, idx, None,
+                                 torch.empty(gsa.gsa_workspace_size(c.cfg, gsa.GSA_OP_COMPRESSED),
+                                             dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    ofr = oracle.frame(sh, c.q, c.k, c.v, np.arange(sh.m_tokens))
+    assert_close(to_host(of).reshape(ofr.shape), ofr, sh.dtype, "chain: frame attention")
+    q2r = (ofr.astype(np.float32) * np.float32(32.0)).reshape(sh.qkv_shape)
+    res = oracle.forward(sh, q2r, c.k, c.v, c.wg)
+    _forward_rows_vs_oracle(sh, o, res, idx.cpu().numpy(), "chain: GSA on the frame output")
+
+    shb = GSAShape("pair 6f-16x16-h2-s4-k5", 6, 2, 16, 16, 2, 64, 4, 5, BF16, seed=57)
+    cb = Case(shb)
+    ofb = torch.empty_like(cb.dq)
+    gsa.gsa_frame_attn(cb.cfg, cb.dq, cb.dk, cb.dv, ofb)
+    ob = cb.forward()
+    _, idxb, _ = cb.compressed(*cb.pool())
+    torch.cuda.synchronize()
+    ofbr = oracle.frame(shb, cb.q, cb.k, cb.v, np.arange(shb.m_tokens))
+    assert_close(to_host(ofb).reshape(ofbr.shape), ofbr, shb.dtype, "pair: frame attention")
+    _forward_rows_vs_oracle(shb, ob, oracle.forward(shb, cb.q, cb.k, cb.v, cb.wg), idxb.cpu().numpy(),
+                            "pair: GSA")
+
+
 # ---- FlashVGGT descriptor attention (Paper-Notes page "FlashVGGT: Efficient and
 # Scalable Visual Geometry Transformers with Compressed Descriptor Attention") ----
 
