@@ -328,8 +328,8 @@ def main():
     idx_bytes = sh.n_windows * H * sh.topk * 4
     # standalone selection: q rows in, the gathers, the index lists, O_sel (fp32) out
     select_bytes = gather_bytes + sh.m_img * H * d * (esz + 4) + idx_bytes
-    # its overhead: the blocked K / V^T copies it builds first (K, V read; copies written)
-    select_copy_bytes = 2 * sh.m_img * H * d * esz + 2 * sh.n_windows * H * sb * d * esz
+    # its overhead: the blocked V^T copy it builds first (V read, copy written)
+    select_copy_bytes = sh.m_img * H * d * esz + sh.n_windows * H * sb * d * esz
     # the forward's fused selection launch: q in, gathers, lists, O'_comp in, o out
     select_fused_bytes = gather_bytes + 2 * sh.m_img * H * d * esz + idx_bytes + sh.n_windows * H * d * 4
     combine_bytes = sh.m_img * H * d * (esz + 4 + esz) + sh.n_windows * H * d * 4
@@ -340,7 +340,7 @@ def main():
         "flash_kernel<bf16,4,bound>": ("mfma", fl["compressed"], "compressed attention sweep (+ score bounds)"),
         "flash_kernel<bf16,4,partial>": ("mfma", fl["special"], "special-token attention partials"),
         "select_kernel<bf16,1>": ("hbm", select_fused_bytes, "selection attention + fused upsample/gate (forward)"),
-        "pool_kernel<bf16>": ("hbm", pool_bytes, "pooling (the forward's launch also writes the blocked copies)"),
+        "pool_kernel<bf16>": ("hbm", pool_bytes, "pooling (the forward's launch also writes the blocked V^T copy)"),
         "hot_group_kernel<bf16,8>": ("overhead", None, "top-k: re-scoring of the hot key groups"),
         "threshold_kernel<64>": ("overhead", None, "top-k: theta and hot-group masks"),
         "rank_kernel": ("overhead", None, "top-k: ranking of the candidate lists"),
@@ -377,8 +377,8 @@ def main():
         "pool_frac_hbm": round(pool_bytes / (st["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "select_gather_bytes": gather_bytes,
         # the standalone selection call: algorithmic bytes (q rows in, gathers,
-        # lists, O_sel out) over the entry point's time; the blocked copies it
-        # builds first are overhead, reported beside
+        # lists, O_sel out) over the entry point's time; the blocked V^T copy it
+        # builds first is overhead, reported beside
         "select_bytes": select_bytes,
         "select_copy_overhead_bytes": select_copy_bytes,
         "select_hbm_gbs": round(select_bytes / (st["select_standalone"] * 1e-3) / 1e9, 1),

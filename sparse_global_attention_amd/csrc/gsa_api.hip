@@ -253,7 +253,6 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.cand = take(qh * p.cap * 8);
   }
   if (op == GSA_OP_FORWARD || op == GSA_OP_SELECT) {
-    p.kblk = take(blk);
     p.vblk = take(blk);
     p.ctx_o = take(ctx_o);
     p.ctx_lse = take(ctx_lse);
@@ -484,11 +483,11 @@ PoolParams pool_base(const Call& c) {
   return p;
 }
 
-SelectParams select_base(const Call& c, const Plan& pl, const void* q, const int32_t* idx, void* ws) {
+SelectParams select_base(const Call& c, const Plan& pl, const void* q, const void* k, const int32_t* idx, void* ws) {
   SelectParams s;
   memset(&s, 0, sizeof(s));
   s.q = q;
-  s.kblk = at(ws, pl.kblk);
+  s.k = k;
   s.vblk = at(ws, pl.vblk);
   s.topk_idx = idx;
   s.topk = c.topk;
@@ -566,16 +565,15 @@ gsa_status gsa_select_attn(const gsa_config* cfg, const void* q, const void* k, 
   Plan pl = make_plan(c, GSA_OP_SELECT);
   if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // the transposed V blocks the selection gathers (K rows come from k itself)
   PoolParams pp = pool_base(c);
-  pp.src[1] = k;
   pp.src[2] = v;
-  pp.rows[1] = at(ws, pl.kblk);
   pp.trans[2] = at(ws, pl.vblk);
-  pp.first_tensor = 1;
-  hipError_t e = launch_pool(c.dtype, pp, 2, st);
+  pp.first_tensor = 2;
+  hipError_t e = launch_pool(c.dtype, pp, 1, st);
   if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
   if (e != hipSuccess) return GSA_ERR_HIP;
-  SelectParams sp = select_base(c, pl, q, topk_idx, ws);
+  SelectParams sp = select_base(c, pl, q, k, topk_idx, ws);
   sp.osel = o_sel;
   return hip_status(launch_select(c.dtype, sp, st));
 }
@@ -633,7 +631,7 @@ gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, con
   if (state && (int64_t)state_bytes < ts.total) return GSA_ERR_WORKSPACE;
   auto saved = [&](int64_t off) { return state ? reinterpret_cast<float*>(at(state, off)) : nullptr; };
 
-  // 1. pooling of Q/K/V plus the blocked K / transposed-V copies for the gather
+  // 1. pooling of Q/K/V plus the transposed V blocks for the gather
   PoolParams pp = pool_base(c);
   pp.src[0] = q;
   pp.src[1] = k;
@@ -641,7 +639,6 @@ gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, con
   pp.dst[0] = at(ws, pl.qc);
   pp.dst[1] = at(ws, pl.kc);
   pp.dst[2] = at(ws, pl.vc);
-  pp.rows[1] = at(ws, pl.kblk);
   pp.trans[2] = at(ws, pl.vblk);
   pp.first_tensor = 0;
   hipError_t e = launch_pool(c.dtype, pp, 3, st);
@@ -656,7 +653,7 @@ gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, con
   if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
   // 5. selection + upsample + gate
   if (e == hipSuccess) {
-    SelectParams sp = select_base(c, pl, q, idx, ws);
+    SelectParams sp = select_base(c, pl, q, k, idx, ws);
     sp.wg = wg;
     sp.oc = oc;
     sp.o = o;
@@ -910,7 +907,7 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   float* l2sel = state ? saved(ts.l2sel) : reinterpret_cast<float*>(at(ws, pl.l2sel));
   if (!state) {
     if (c.n_ctx && e == hipSuccess) ok(run_context(c, pl, q, k, v, ws, st));
-    SelectParams sp = select_base(c, pl, q, topk_idx, ws);
+    SelectParams sp = select_base(c, pl, q, k, topk_idx, ws);
     sp.osel = osel;
     sp.l2 = l2sel;
     ok(launch_select(c.dtype, sp, st));

@@ -174,8 +174,8 @@ hipError_t launch_merge(int dtype, const MergeParams& p, hipStream_t stream);
 // ---- selection attention over gathered top-k windows ------------------------
 struct SelectParams {
   const void* q;        // token layout
-  const void* kblk;     // [M'][H][sb][d]
-  const void* vblk;     // [M'][H][d][sb]
+  const void* k;        // token layout (K rows are gathered from it directly)
+  const void* vblk;     // [M'][H][d][sb] transposed V blocks
   const int32_t* topk_idx;  // [M'][H][topk]
   int topk;
   Geometry g;

@@ -11,10 +11,12 @@
 //  * section "压缩分支" (nearest-neighbour upsampling) and section "门控聚合"
 //    (g = sigmoid(W_g q), O = g O_comp + (1 - g) O_sel): fused epilogue.
 //
-// Gather-bound.  The K/V of a selected (window, head) are read from two
-// contiguous blocks written by the pooling pass -- K rows [sb][d] and V
-// transposed [d][sb] -- so every lane issues 16-byte loads that land directly
-// in matrix-core operand layout (no LDS, no barriers; waves are independent).
+// Gather-bound.  The K rows of a selected (window, head) are read straight
+// from the token layout (a lane reads 32 bytes of one 128-byte row, the same
+// access a blocked copy would give), V from the contiguous transposed block
+// [d][sb] the pooling pass writes (slots contiguous per channel, as the PV
+// operand needs), so every lane issues 16-byte loads that land directly in
+// matrix-core operand layout (no LDS, no barriers; waves are independent).
 // A chunk is 32 key slots (two windows at s = 4); the next chunk's loads are
 // issued before the current chunk's matrix-core work.
 //   S^T[32 slots x 16 q] : 2 tiles x 2 x v_mfma_f32_16x16x32_bf16 (K = d)
@@ -39,22 +41,50 @@ struct SelChunk {
   int kkv0;  // window-local key of the first of them
 };
 
+// Token row of the first (top-left) token of top-k entry t's window, from
+// the two registers holding that of entries lane and lane+64 (-1: skipped).
+__device__ __forceinline__ int64_t topk_base(int64_t tb0, int64_t tb1, int t) {
+  const int lo0 = __builtin_amdgcn_ds_bpermute((t & 63) << 2, (int)tb0);
+  const int hi0 = __builtin_amdgcn_ds_bpermute((t & 63) << 2, (int)(tb0 >> 32));
+  const int lo1 = __builtin_amdgcn_ds_bpermute((t & 63) << 2, (int)tb1);
+  const int hi1 = __builtin_amdgcn_ds_bpermute((t & 63) << 2, (int)(tb1 >> 32));
+  const int lo = t < 64 ? lo0 : lo1, hi = t < 64 ? hi0 : hi1;
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Token row of window j's first token (-1 for a skipped entry).
+__device__ __forceinline__ int64_t window_base(const Geometry& g, int j) {
+  if (j < 0) return -1;
+  const int64_t f = j / g.wpf, r = j - f * g.wpf;
+  const int64_t wy = r / g.wx, wxx = r - wy * g.wx;
+  return f * g.tf + g.n_special + wy * g.pool * g.grid_w + wxx * g.pool;
+}
+
 template <typename T>
 __device__ __forceinline__ void load_chunk(SelChunk<T>& ch, const SelectParams& p, int64_t h, int c, int ql,
-                                           int g, int tr0, int tr1) {
+                                           int g, int tr0, int tr1, int64_t tb0, int64_t tb1) {
   using C = SelChunk<T>;
   const int64_t sb = p.g.sb, H = p.g.n_heads;
-  const T* kblk = static_cast<const T*>(p.kblk);
+  const int s = (int)p.g.pool, s2 = s * s;
+  const T* K = static_cast<const T*>(p.k);
   const T* vblk = static_cast<const T*>(p.vblk);
-  // K operand: A-row ql of tile tau is slot 8*(ql/4) + 4*tau + ql%4 of the chunk
+  // K operand: A-row ql of tile tau is slot 8*(ql/4) + 4*tau + ql%4 of the
+  // chunk, i.e. key kka + 4 tau (row-major in the s x s window) of top-k
+  // entry ga / sb; keys past s^2 (padding slots) read the window's first
+  // token instead -- their scores are masked below.
   const int64_t ga = (int64_t)c * 32 + 8 * (ql >> 2);
-  const int ja = topk_entry(tr0, tr1, (int)(ga / sb), p.topk, p.g.n_windows);
-  const int64_t kka = ga % sb + (ql & 3);
-  const T* kb = kblk + (((int64_t)(ja < 0 ? 0 : ja) * H + h) * sb + kka) * kHeadDim + 16 * g;
+  const int64_t base = topk_base(tb0, tb1, (int)(ga / sb));
+  const int kka = (int)(ga % sb) + (ql & 3);
+  const int64_t row0 = base < 0 ? 0 : base;
+  const int m16 = (65536 + s - 1) / s;  // kk / s = (kk * m16) >> 16 exactly for kk < 64, s <= 8
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau)
+  for (int tau = 0; tau < 2; ++tau) {
+    const int kk = kka + 4 * tau < s2 ? kka + 4 * tau : 0;
+    const int dy = (kk * m16) >> 16, dx = kk - dy * s;
+    const T* kb = K + ((row0 + dy * p.g.grid_w + dx) * H + h) * kHeadDim + 16 * g;
 #pragma unroll
-    for (int x = 0; x < C::KV; ++x) ch.k[tau][x] = ld16(kb + 4 * tau * kHeadDim + x * C::VE);
+    for (int x = 0; x < C::KV; ++x) ch.k[tau][x] = ld16(kb + x * C::VE);
+  }
   // V^T operand and S^T rows of this lane: slots 8g .. 8g+7 of the chunk
   const int64_t gv = (int64_t)c * 32 + 8 * g;
   ch.jv = topk_entry(tr0, tr1, (int)(gv / sb), p.topk, p.g.n_windows);
@@ -92,6 +122,9 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
   const int32_t* trow = p.topk_idx + (win * geo.n_heads + h) * K;
   const int tr0 = lane < K ? trow[lane] : -1;
   const int tr1 = lane + 64 < K ? trow[lane + 64] : -1;
+  // first token of each entry's window (entries outside [0, M') skipped)
+  const int64_t tb0 = window_base(geo, tr0 < geo.n_windows ? tr0 : -1);
+  const int64_t tb1 = window_base(geo, tr1 < geo.n_windows ? tr1 : -1);
   const int n_chunks = (int)((K * geo.sb + 31) / 32);
 
   {
@@ -155,17 +188,17 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
     // Two chunk buffers alternate so that two chunks of gathers are always in
     // flight; no register copies (a copy would wait for its loads).
     SelChunk<T> A, B;
-    load_chunk<T>(A, p, h, 0, ql, g, tr0, tr1);
-    load_chunk<T>(B, p, h, 1, ql, g, tr0, tr1);
+    load_chunk<T>(A, p, h, 0, ql, g, tr0, tr1, tb0, tb1);
+    load_chunk<T>(B, p, h, 1, ql, g, tr0, tr1, tb0, tb1);
     int ci = 0;
     for (; ci + 3 < n_chunks; ci += 2) {
       process(A);
-      load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1);
+      load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1, tb0, tb1);
       process(B);
-      load_chunk<T>(B, p, h, ci + 3, ql, g, tr0, tr1);
+      load_chunk<T>(B, p, h, ci + 3, ql, g, tr0, tr1, tb0, tb1);
     }
     process(A);
-    if (ci + 2 < n_chunks) load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1);
+    if (ci + 2 < n_chunks) load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1, tb0, tb1);
     if (ci + 1 < n_chunks) process(B);
     if (ci + 2 < n_chunks) process(A);
 
