@@ -154,6 +154,13 @@ struct BwdLds {
   }
 };
 
+// bf16 dQ pass: a ring of three (K, V) tile buffers fed by global-to-LDS
+// loads, as in the forward flash kernel (separate arrays, so the compiler can
+// tell which buffer a load writes).
+__shared__ __attribute__((aligned(16))) __bf16 bq_ring0[kKT * kHeadDim * 2];
+__shared__ __attribute__((aligned(16))) __bf16 bq_ring1[kKT * kHeadDim * 2];
+__shared__ __attribute__((aligned(16))) __bf16 bq_ring2[kKT * kHeadDim * 2];
+
 template <typename T, int WAVES, int KIND>
 __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p) {
   using F = Frag32<T>;
@@ -189,7 +196,76 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
     const int nk = (int)(p.kend[split] - kb);
     const int n_tiles = (nk + kKT - 1) / kKT, n_full = nk / kKT;
     f32x16 acc[2] = {{}, {}};
+    // one 32-key tile: dS = P (dO . v - D), acc^T += K^T dS^T
+    auto tile_dq = [&](int t, const T* kt, const T* vt) __attribute__((always_inline)) {
+      f32x16 s = F::qk(kt, r, hf, qf);
+      if (t >= n_full) {
+        const int lim = nk - t * kKT - 4 * hf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i / 4) + (i % 4) >= lim) s[i] = -INFINITY;
+      }
+      f32x16 pm;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pm[i] = fast_exp2(fmaf(s[i], c, -L2));
+      const f32x16 dp = F::qk(vt, r, hf, gf);
+      f32x16 ds;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = pm[i] * (dp[i] - D);
+      F::pv(kt, lane, BwdOp<T>::make(ds), acc);
+    };
 
+    if constexpr (sizeof(T) == 2) {
+      // Ring of three tile buffers (see flash_kernel): step t loads tile t+2
+      // into the buffer tile t-1 used, computes tile t, waits for its own
+      // loads of tile t+1 and meets the other waves at a barrier (no fence).
+      // Tiles past the last one re-read it (their keys are masked).
+      constexpr int NDMA = (2 * kKT * kHeadDim / 8) / (WAVES * 64);
+      static_assert(NDMA >= 1 && NDMA * WAVES * 64 == 2 * kKT * kHeadDim / 8, "tile must split evenly");
+      using TL = Tile<T>;
+      const int wu = __builtin_amdgcn_readfirstlane(wv);
+      int goff[NDMA];
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int ch = (64 * (WAVES * j + wu) + lane) & 255, row = ch >> 3;
+        goff[j] = (int)(row * p.row_stride * 2 + (((ch & 7) ^ TL::swz(row)) << 4));
+      }
+      auto dma_tile = [&](__bf16* b, int t) __attribute__((always_inline)) {
+        const int rel = (t < n_tiles ? t : n_tiles - 1) * kKT, valid = min(nk - rel, kKT);
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(K, p.row_stride, hoff, kb + rel, valid);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(V, p.row_stride, hoff, kb + rel, valid);
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) {
+          const int c0 = 64 * (WAVES * j + wu);
+          lds_load16(c0 < 256 ? rk : rv, b + 8 * c0, goff[j]);
+        }
+      };
+      auto ring_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x70 | NDMA);  // vmcnt(NDMA) lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // the query and dO fragments land before any tile load is issued, so
+      // the loop never drains the load queue to be sure of them
+      __builtin_amdgcn_s_waitcnt(0);
+      dma_tile(bq_ring0, 0);
+      dma_tile(bq_ring1, 1);
+      ring_barrier();
+      auto step = [&](int t, const __bf16* cur, __bf16* fill) __attribute__((always_inline)) {
+        dma_tile(fill, t + 2);
+        tile_dq(t, cur, cur + TL::K_ELEMS);
+        ring_barrier();
+      };
+      for (int t = 0; t < n_tiles; t += 3) {
+        step(t, bq_ring0, bq_ring2);
+        step(t + 1, bq_ring1, bq_ring0);
+        step(t + 2, bq_ring2, bq_ring1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x70);  // the last prefetches land before the LDS is handed on
+    } else {
     st.load_range(K, V, p.row_stride, hoff, kb, min(nk, kKT), tid);
     {
       const L b0 = buf(0);
@@ -200,26 +276,30 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
       if (t + 1 < n_tiles) st.load_range(K, V, p.row_stride, hoff, kb + (int64_t)(t + 1) * kKT,
                                          min(nk - (t + 1) * kKT, kKT), tid);
       const L cur = buf(t);
-      f32x16 s = F::qk(cur.a_rows, r, hf, qf);
-      if (t >= n_full) {
-        const int lim = nk - t * kKT - 4 * hf;
+      // fp32: K rows, V rows and K transposed (the PV operand) in LDS
+      {
+        f32x16 s = F::qk(cur.a_rows, r, hf, qf);
+        if (t >= n_full) {
+          const int lim = nk - t * kKT - 4 * hf;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (8 * (i / 4) + (i % 4) >= lim) s[i] = -INFINITY;
+          for (int i = 0; i < 16; ++i)
+            if (8 * (i / 4) + (i % 4) >= lim) s[i] = -INFINITY;
+        }
+        f32x16 pm;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pm[i] = fast_exp2(fmaf(s[i], c, -L2));
+        const f32x16 dp = F::qk(cur.b_rows, r, hf, gf);
+        f32x16 ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = pm[i] * (dp[i] - D);
+        F::pv(cur.a_tr, lane, BwdOp<T>::make(ds), acc);
       }
-      f32x16 pm;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pm[i] = fast_exp2(fmaf(s[i], c, -L2));
-      const f32x16 dp = F::qk(cur.b_rows, r, hf, gf);
-      f32x16 ds;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = pm[i] * (dp[i] - D);
-      F::pv(cur.a_tr, lane, BwdOp<T>::make(ds), acc);
       if (t + 1 < n_tiles) {
         const L nx = buf(t + 1);
         st.store(nx.a_rows, nx.a_tr, nx.b_rows, nullptr, nullptr, nullptr, tid);
       }
       lds_barrier();
+    }
     }
     if (qvalid) {
 #pragma unroll
@@ -317,7 +397,8 @@ static hipError_t launch_flash_bwd_t(const FlashBwdParams& p, hipStream_t stream
   }
   if (blocks == 0) return hipSuccess;
   if (blocks > 0xffffffffLL || p.n_splits < 1 || p.n_qsplits < 1) return hipErrorInvalidValue;
-  const size_t lds = 2 * (size_t)BwdLds<T>::STAGE_BYTES;
+  // (the bf16 dQ pass uses the static tile ring instead)
+  const size_t lds = (KIND == kBwdDQ && sizeof(T) == 2) ? 0 : 2 * (size_t)BwdLds<T>::STAGE_BYTES;
   const void* fn = reinterpret_cast<const void*>(&flash_bwd_kernel<T, WAVES, KIND>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
