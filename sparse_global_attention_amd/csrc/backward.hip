@@ -25,6 +25,8 @@
 // All sums run in a fixed order, so the gradients are deterministic.
 #include <math.h>
 
+#include <algorithm>
+
 #include "flash_frag.h"
 #include "gsa_device.h"
 #include "gsa_kernels.h"
@@ -160,6 +162,25 @@ struct BwdLds {
 __shared__ __attribute__((aligned(16))) __bf16 bq_ring0[kKT * kHeadDim * 2];
 __shared__ __attribute__((aligned(16))) __bf16 bq_ring1[kKT * kHeadDim * 2];
 __shared__ __attribute__((aligned(16))) __bf16 bq_ring2[kKT * kHeadDim * 2];
+
+// bf16 key-side pass: the same ring over (Q, dO) query tiles, and beside
+// each buffer every wave's own copy of the tile's L2 and D values (64 floats
+// each, of which the tile uses the first 32).  Every buffer is an array of
+// its own: the compiler then knows that reading one does not wait for the
+// loads still filling another.
+constexpr int kBkvQdoElems = kKT * kHeadDim * 2;  // Q rows, then dO rows
+constexpr int kBkvRowVals = 64;                   // L2 / D values one wave loads
+constexpr int kBkvVals = 2 * 4 * kBkvRowVals;     // L2 of 4 waves, then D of 4 waves
+__shared__ __attribute__((aligned(16))) __bf16 bk_ring0[kBkvQdoElems];
+__shared__ __attribute__((aligned(16))) __bf16 bk_ring1[kBkvQdoElems];
+__shared__ __attribute__((aligned(16))) __bf16 bk_ring2[kBkvQdoElems];
+__shared__ __attribute__((aligned(16))) float bk_vals0[kBkvVals];
+__shared__ __attribute__((aligned(16))) float bk_vals1[kBkvVals];
+__shared__ __attribute__((aligned(16))) float bk_vals2[kBkvVals];
+
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t rs, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
 
 template <typename T, int WAVES, int KIND>
 __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p) {
@@ -330,7 +351,118 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
     const int64_t n_qt = (p.n_q + kKT - 1) / kKT;
     const int64_t t0 = n_qt * z / p.n_qsplits, t1 = n_qt * (z + 1) / p.n_qsplits;
     f32x16 dk[2] = {{}, {}}, dv[2] = {{}, {}};
+    // one 32-query tile: P^T and dS^T for this wave's 32 keys, dV += P^T dO, dK += dS^T Q
+    auto tile_kv = [&](const T* qt, const T* qtr, const T* gt, const T* gtr, const float* l2s, const float* dds)
+        __attribute__((always_inline)) {
+      // element i: query row 8 (i/4) + 4 hf + i%4 of the tile, key r of this wave
+      const f32x16 s = F::qk(qt, r, hf, kf);
+      const f32x16 dp = F::qk(gt, r, hf, vf);
+      f32x16 pm, ds;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 8 * a + 4 * hf);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dds + 8 * a + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pm[4 * a + e] = fast_exp2(fmaf(s[4 * a + e], c, -l4[e]));
+          ds[4 * a + e] = pm[4 * a + e] * (dp[4 * a + e] - d4[e]);
+        }
+      }
+      F::pv(gtr, lane, BwdOp<T>::make(pm), dv);
+      F::pv(qtr, lane, BwdOp<T>::make(ds), dk);
+    };
 
+    if constexpr (sizeof(T) == 2) {
+      // Ring of three (Q, dO, L2, D) buffers as in the query-side pass: step t
+      // loads tile t+2 into the buffer tile t-1 used, computes tile t (tiles
+      // past the split are loaded, not computed), waits for its own loads of
+      // tile t+1 and meets the other waves at a barrier.  Lane l loads chunk
+      // l % 8 of query row 8 w + l / 8 of both Q and dO; it follows that row
+      // through the query map with a running (frame, remainder) pair, so no
+      // tile needs a division.  Offsets are relative to the wave's first row
+      // (the host bounds them below 2^31); rows from n_q on get an offset past
+      // the buffer's limit and read as zeros, as do their L2 and D, and such a
+      // row adds nothing (P = 1 but dO = 0 and dP - D = 0).  The L2 values are
+      // log2 denominators (lse_mul = 1, checked on the host).
+      constexpr int NDMA = 4;  // Q chunk, dO chunk, L2 values, D values
+      using TL = Tile<T>;
+      const int wu = __builtin_amdgcn_readfirstlane(wv);
+      const int rowl = 8 * wu + (lane >> 3);
+      const uint32_t cbyte = (uint32_t)(((lane & 7) ^ TL::swz(rowl)) << 4);
+      const uint32_t qa = (uint32_t)p.qa, qb = (uint32_t)p.qb;
+      const uint32_t df = (uint32_t)kKT / qa, dr = (uint32_t)kKT % qa;
+      const uint32_t nq = (uint32_t)p.n_q;
+      const uint32_t stride_b = (uint32_t)(p.row_stride * 2);
+      uint32_t rr = (uint32_t)(t0 * kKT) + (uint32_t)rowl;  // this lane's row in the next tile loaded
+      uint32_t fr = rr / qa, rem = rr - fr * qa;
+      const T* Qb = static_cast<const T*>(p.q) + p.qc * p.row_stride + hoff;
+      const T* Gb = static_cast<const T*>(p.d_o) + (p.do_mapped ? p.qc * p.row_stride : 0) + hoff;
+      const uint32_t lane_lin = (uint32_t)(lane >> 3) * stride_b + cbyte;  // dO rows by index
+      const uint32_t lrow_off = (uint32_t)lane * (uint32_t)H * 4u;
+      auto dma_tile = [&](__bf16* b, float* bv, int64_t t) __attribute__((always_inline)) {
+        const bool valid = rr < nq;
+        const uint32_t fr0 = __builtin_amdgcn_readfirstlane(fr), rem0 = __builtin_amdgcn_readfirstlane(rem);
+        const bool valid0 = (uint32_t)(t * kKT) + (uint32_t)(8 * wu) < nq;
+        const int64_t tok0 = valid0 ? (int64_t)fr0 * qb + rem0 : 0;
+        const uint32_t dq_rows = (fr - fr0) * qb + rem - rem0;  // token rows past the wave's first
+        const uint32_t oq = valid ? dq_rows * stride_b + cbyte : 0x80000000u;
+        const int64_t r_first = valid0 ? t * kKT + 8 * wu : 0;
+        const uint32_t og = valid ? (p.do_mapped ? oq : lane_lin) : 0x80000000u;
+        const __amdgpu_buffer_rsrc_t rq =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Qb + tok0 * p.row_stride), (short)0, 0x7fffffff, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(Gb + (p.do_mapped ? tok0 : r_first) * p.row_stride), (short)0, 0x7fffffff, 0x00020000);
+        const int64_t r0 = t * kKT;
+        const int nrec = r0 < p.n_q ? (int)(((p.n_q - r0 - 1) * H + 1) * 4) : 0;
+        const int64_t lo = r0 < p.n_q ? r0 * H + h : 0;
+        const __amdgpu_buffer_rsrc_t rl =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.lse + lo), (short)0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rd =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.dd + lo), (short)0, nrec, 0x00020000);
+        lds_load16(rq, b + 512 * wu, (int)oq);
+        lds_load16(rg, b + kKT * kHeadDim + 512 * wu, (int)og);
+        lds_load4(rl, bv + kBkvRowVals * wu, (int)lrow_off);
+        lds_load4(rd, bv + kBkvRowVals * (4 + wu), (int)lrow_off);
+        // the next tile's row
+        rr += kKT;
+        fr += df;
+        rem += dr;
+        if (rem >= qa) {
+          rem -= qa;
+          fr += 1;
+        }
+      };
+      auto ring_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x70 | NDMA);  // vmcnt(NDMA) lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto step = [&](int64_t t, const __bf16* cur, const float* curv, __bf16* fill, float* fillv)
+          __attribute__((always_inline)) {
+        dma_tile(fill, fillv, t + 2);
+        if (t < t1) {
+          const float* l2s = curv + kBkvRowVals * wu;
+          tile_kv(cur, cur, cur + kKT * kHeadDim, cur + kKT * kHeadDim, l2s, l2s + 4 * kBkvRowVals);
+        }
+        ring_barrier();
+      };
+      if (t0 < t1) {
+        // the key and value fragments land before any tile load is issued
+        __builtin_amdgcn_s_waitcnt(0);
+        dma_tile(bk_ring0, bk_vals0, t0);
+        dma_tile(bk_ring1, bk_vals1, t0 + 1);
+        ring_barrier();
+        for (int64_t t = t0; t < t1; t += 3) {
+          step(t, bk_ring0, bk_vals0, bk_ring2, bk_vals2);
+          step(t + 1, bk_ring1, bk_vals1, bk_ring0, bk_vals0);
+          step(t + 2, bk_ring2, bk_vals2, bk_ring1, bk_vals1);
+        }
+        __builtin_amdgcn_s_waitcnt(0x70);  // the last prefetches land before the LDS is handed on
+      }
+    } else {
     if (t0 < t1) {
       st.load_queries(p, hoff, h, t0 * kKT, tid);
       const L b0 = buf(0);
@@ -340,27 +472,13 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
     for (int64_t t = t0; t < t1; ++t) {
       if (t + 1 < t1) st.load_queries(p, hoff, h, (t + 1) * kKT, tid);
       const L cur = buf(t - t0);
-      // element i: query row 8 (i/4) + 4 hf + i%4 of the tile, key r of this wave
-      const f32x16 s = F::qk(cur.a_rows, r, hf, kf);
-      const f32x16 dp = F::qk(cur.b_rows, r, hf, vf);
-      f32x16 pm, ds;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(cur.l2s + 8 * a + 4 * hf);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(cur.dds + 8 * a + 4 * hf);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pm[4 * a + e] = fast_exp2(fmaf(s[4 * a + e], c, -l4[e]));
-          ds[4 * a + e] = pm[4 * a + e] * (dp[4 * a + e] - d4[e]);
-        }
-      }
-      F::pv(cur.b_tr, lane, BwdOp<T>::make(pm), dv);
-      F::pv(cur.a_tr, lane, BwdOp<T>::make(ds), dk);
+      tile_kv(cur.a_rows, cur.a_tr, cur.b_rows, cur.b_tr, cur.l2s, cur.dds);
       if (t + 1 < t1) {
         const L nx = buf(t + 1 - t0);
         st.store(nx.a_rows, nx.a_tr, nx.b_rows, nx.b_tr, nx.l2s, nx.dds, tid);
       }
       lds_barrier();
+    }
     }
     if (kvalid) {
 #pragma unroll
@@ -397,8 +515,17 @@ static hipError_t launch_flash_bwd_t(const FlashBwdParams& p, hipStream_t stream
   }
   if (blocks == 0) return hipSuccess;
   if (blocks > 0xffffffffLL || p.n_splits < 1 || p.n_qsplits < 1) return hipErrorInvalidValue;
-  // (the bf16 dQ pass uses the static tile ring instead)
-  const size_t lds = (KIND == kBwdDQ && sizeof(T) == 2) ? 0 : 2 * (size_t)BwdLds<T>::STAGE_BYTES;
+  if (KIND == kBwdDKDV && sizeof(T) == 2) {
+    // the key-side tile ring: log2 denominators, a query map whose rows never
+    // go back (consecutive queries move at most qb token rows), 32-bit row
+    // counters and per-wave byte offsets below 2^31
+    const int64_t span = 7 * std::max<int64_t>(p.qb, 1) * p.row_stride * 2 + 128;
+    if (p.lse_mul != 1.0f || p.qa < 1 || (p.qb == 0 ? p.n_q > p.qa : p.qb < p.qa) ||
+        p.n_q + 4 * kKT > INT32_MAX || p.n_q * p.n_heads * 4 > INT32_MAX || span > INT32_MAX)
+      return hipErrorInvalidValue;
+  }
+  // (the bf16 passes use the static tile rings instead)
+  const size_t lds = sizeof(T) == 2 ? 0 : 2 * (size_t)BwdLds<T>::STAGE_BYTES;
   const void* fn = reinterpret_cast<const void*>(&flash_bwd_kernel<T, WAVES, KIND>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -452,7 +579,7 @@ hipError_t launch_fill(float* x, int64_t n, hipStream_t stream) {
 //   g = sigmoid(W_g . q),  dO_sel = (1 - g) dO,  D_sel = dO_sel . O_sel,
 //   dz = (dO . (O'_i - O_sel)) g (1 - g),  dq = dz W_g (stored),
 // and per window: dO_comp = sum_t g dO, D_comp = dO_comp . O'_i, the dW_g
-// partial sum_t dz q.
+// partial sum_t dz q, and the compressed attention's log2 denominator.
 template <typename T>
 __device__ __forceinline__ f32x4 load4(const T* x) {
   if constexpr (sizeof(T) == 2) {
@@ -542,7 +669,10 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdParams p) {
   if (tg == 0) {
     store4(static_cast<T*>(p.doc) + (win * H + h) * kHeadDim + ch, acc_doc);
     *reinterpret_cast<f32x4*>(p.dwg_part + (win * H + h) * kHeadDim + ch) = acc_dwg;
-    if (cl == 0) p.dc[win * H + h] = dc;
+    if (cl == 0) {
+      p.dc[win * H + h] = dc;
+      p.l2c[win * H + h] = p.lse_c[win * H + h] * kLog2e;
+    }
   }
 }
 

@@ -120,7 +120,7 @@ struct Plan {
   // backward
   int ctx_qsplits;  // query splits of the context frames' key-side pass
   int64_t qblk, qT, kT, vrow, lse_c, spec_o32, spec_l2, spec_dd, osel, l2sel, doblk, doT, l2blk, dblk,
-      dosel_img, dsel_img, doc, dc, dwg_part, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list,
+      dosel_img, dsel_img, doc, dc, l2c, dwg_part, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list,
       ctx_dq, ctx_dkdv;
 };
 
@@ -302,6 +302,7 @@ Plan make_plan(const Call& c, gsa_op op) {
     }
     p.doc = take(g.n_windows * g.n_heads * kHeadDim * c.esz);
     p.dc = take(wl);
+    p.l2c = take(wl);
     p.dwg_part = take(wf);
     p.dqc = take(wf);
     p.dkc = take(wf);
@@ -807,7 +808,6 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t H = g.n_heads;
-  const float kFloatL2 = kLog2e;  // natural log-sum-exp -> log2 denominator
   hipError_t e = hipSuccess;
   auto ok = [&](hipError_t x) { if (e == hipSuccess) e = x; return e == hipSuccess; };
 
@@ -934,6 +934,8 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   }
   gp.doc = at(ws, pl.doc);
   gp.dc = reinterpret_cast<float*>(at(ws, pl.dc));
+  gp.lse_c = lse_c;
+  gp.l2c = reinterpret_cast<float*>(at(ws, pl.l2c));
   gp.dwg_part = reinterpret_cast<float*>(at(ws, pl.dwg_part));
   ok(launch_gate_bwd(c.dtype, gp, st));
   DwgParams dp;
@@ -1017,8 +1019,8 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
     b.qb = 0;
     b.qc = 0;
     b.do_mapped = 0;
-    b.lse = lse_c;
-    b.lse_mul = kFloatL2;
+    b.lse = gp.l2c;
+    b.lse_mul = 1.0f;
     b.dd = gp.dc;
     b.kbeg[0] = 0;
     b.kend[0] = g.n_windows;

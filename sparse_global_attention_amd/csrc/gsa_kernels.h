@@ -283,6 +283,8 @@ struct GateBwdParams {
   float* dsel_img;     // optional [M_img][H]
   void* doc;           // [M'][H][d] dO_comp (dtype)
   float* dc;           // [M'][H] dO_comp . O'_comp
+  const float* lse_c;  // [M'][H] natural log-sum-exp of the compressed attention
+  float* l2c;          // [M'][H] the same as a log2 denominator (lse_c log2 e)
   float* dwg_part;     // [M'][H][d]
 };
 hipError_t launch_gate_bwd(int dtype, const GateBwdParams& p, hipStream_t stream);
