@@ -168,8 +168,10 @@ __shared__ __attribute__((aligned(16))) __bf16 bq_ring2[kKT * kHeadDim * 2];
 // each, of which the tile uses the first 32).  Every buffer is an array of
 // its own: the compiler then knows that reading one does not wait for the
 // loads still filling another.
-constexpr int kBkvQdoElems = kKT * kHeadDim * 2;  // Q rows, then dO rows
-constexpr int kBkvRowVals = 64;                   // L2 / D values one wave loads
+constexpr int kBkvQT = 2;                         // 32-query sub-tiles per ring tile
+constexpr int kBkvTQ = kBkvQT * kKT;               // query rows per ring tile
+constexpr int kBkvQdoElems = kBkvTQ * kHeadDim * 2;  // Q rows, then dO rows
+constexpr int kBkvRowVals = 64;                   // L2 / D values one wave loads (>= kBkvTQ)
 constexpr int kBkvVals = 2 * 4 * kBkvRowVals;     // L2 of 4 waves, then D of 4 waves
 __shared__ __attribute__((aligned(16))) __bf16 bk_ring0[kBkvQdoElems];
 __shared__ __attribute__((aligned(16))) __bf16 bk_ring1[kBkvQdoElems];
@@ -373,19 +375,27 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
     };
 
     if constexpr (sizeof(T) == 2) {
-      // Ring of three (Q, dO, L2, D) buffers as in the query-side pass: step t
-      // loads tile t+2 into the buffer tile t-1 used, computes tile t (tiles
-      // past the split are loaded, not computed), waits for its own loads of
-      // tile t+1 and meets the other waves at a barrier.  Lane l loads chunk
-      // l % 8 of query row 8 w + l / 8 of both Q and dO; it follows that row
-      // through the query map with a running (frame, remainder) pair, so no
-      // tile needs a division.  Offsets are relative to the wave's first row
-      // (the host bounds them below 2^31); rows from n_q on get an offset past
-      // the buffer's limit and read as zeros, as do their L2 and D, and such a
-      // row adds nothing (P = 1 but dO = 0 and dP - D = 0).  The L2 values are
-      // log2 denominators (lse_mul = 1, checked on the host).
-      constexpr int NDMA = 4;  // Q chunk, dO chunk, L2 values, D values
+      // Ring of three (Q, dO, L2, D) buffers as in the query-side pass, over
+      // tiles of kBkvTQ queries (kBkvQT sub-tiles of 32, whose score
+      // products are issued together so the matrix cores have independent
+      // work while the exponentials of the other sub-tile run): step t loads
+      // tile t+2 into the buffer tile t-1 used, computes tile t (tiles past
+      // the split are loaded, not computed), waits for its own loads of tile
+      // t+1 and meets the other waves at a barrier.  Lane l loads chunk l % 8
+      // of query rows 32 j + 8 w + l / 8 (sub-tile j) of both Q and dO; it
+      // follows those rows through the query map with running (frame,
+      // remainder) pairs, so no tile needs a division.  Offsets are relative
+      // to the wave's first row (the host bounds them below 2^31); rows from
+      // n_q on get an offset past the buffer's limit and read as zeros, as do
+      // their L2 and D, and such a row adds nothing (P = 1 but dO = 0 and
+      // dP - D = 0).  The L2 values are log2 denominators (lse_mul = 1,
+      // checked on the host).
+      constexpr int QT = kBkvQT, TQ = kBkvTQ;
+      constexpr int NDMA = 2 * QT + 2;  // Q and dO chunks per sub-tile, L2 values, D values
+      static_assert(TQ <= kBkvRowVals, "one L2 / D load covers the tile");
       using TL = Tile<T>;
+      const int64_t n_ut = (p.n_q + TQ - 1) / TQ;
+      const int64_t u0 = n_ut * z / p.n_qsplits, u1 = n_ut * (z + 1) / p.n_qsplits;
       const int wu = __builtin_amdgcn_readfirstlane(wv);
       const int rowl = 8 * wu + (lane >> 3);
       const uint32_t cbyte = (uint32_t)(((lane & 7) ^ TL::swz(rowl)) << 4);
@@ -393,44 +403,57 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
       const uint32_t df = (uint32_t)kKT / qa, dr = (uint32_t)kKT % qa;
       const uint32_t nq = (uint32_t)p.n_q;
       const uint32_t stride_b = (uint32_t)(p.row_stride * 2);
-      uint32_t rr = (uint32_t)(t0 * kKT) + (uint32_t)rowl;  // this lane's row in the next tile loaded
+      uint32_t rr = (uint32_t)(u0 * TQ) + (uint32_t)rowl;  // this lane's sub-tile 0 row in the next tile loaded
       uint32_t fr = rr / qa, rem = rr - fr * qa;
+      // (frame, remainder) of the row kKT further on
+      auto adv = [&](uint32_t& f, uint32_t& m) __attribute__((always_inline)) {
+        f += df;
+        m += dr;
+        if (m >= qa) {
+          m -= qa;
+          f += 1;
+        }
+      };
       const T* Qb = static_cast<const T*>(p.q) + p.qc * p.row_stride + hoff;
       const T* Gb = static_cast<const T*>(p.d_o) + (p.do_mapped ? p.qc * p.row_stride : 0) + hoff;
       const uint32_t lane_lin = (uint32_t)(lane >> 3) * stride_b + cbyte;  // dO rows by index
       const uint32_t lrow_off = (uint32_t)lane * (uint32_t)H * 4u;
       auto dma_tile = [&](__bf16* b, float* bv, int64_t t) __attribute__((always_inline)) {
-        const bool valid = rr < nq;
         const uint32_t fr0 = __builtin_amdgcn_readfirstlane(fr), rem0 = __builtin_amdgcn_readfirstlane(rem);
-        const bool valid0 = (uint32_t)(t * kKT) + (uint32_t)(8 * wu) < nq;
+        const bool valid0 = (uint32_t)(t * TQ) + (uint32_t)(8 * wu) < nq;
         const int64_t tok0 = valid0 ? (int64_t)fr0 * qb + rem0 : 0;
-        const uint32_t dq_rows = (fr - fr0) * qb + rem - rem0;  // token rows past the wave's first
-        const uint32_t oq = valid ? dq_rows * stride_b + cbyte : 0x80000000u;
-        const int64_t r_first = valid0 ? t * kKT + 8 * wu : 0;
-        const uint32_t og = valid ? (p.do_mapped ? oq : lane_lin) : 0x80000000u;
+        const int64_t r_first = valid0 ? t * TQ + 8 * wu : 0;
         const __amdgpu_buffer_rsrc_t rq =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(Qb + tok0 * p.row_stride), (short)0, 0x7fffffff, 0x00020000);
         const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<T*>(Gb + (p.do_mapped ? tok0 : r_first) * p.row_stride), (short)0, 0x7fffffff, 0x00020000);
-        const int64_t r0 = t * kKT;
+        uint32_t f = fr, m = rem, rj = rr;
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+          const bool valid = rj < nq;
+          const uint32_t rows = (f - fr0) * qb + m - rem0;  // token rows past the wave's first
+          const uint32_t oq = valid ? rows * stride_b + cbyte : 0x80000000u;
+          const uint32_t og = valid ? (p.do_mapped ? oq : lane_lin + 32u * j * stride_b) : 0x80000000u;
+          lds_load16(rq, b + kKT * kHeadDim * j + 512 * wu, (int)oq);
+          lds_load16(rg, b + TQ * kHeadDim + kKT * kHeadDim * j + 512 * wu, (int)og);
+          if (j + 1 < QT) {
+            rj += kKT;
+            adv(f, m);
+          }
+        }
+        const int64_t r0 = t * TQ;
         const int nrec = r0 < p.n_q ? (int)(((p.n_q - r0 - 1) * H + 1) * 4) : 0;
         const int64_t lo = r0 < p.n_q ? r0 * H + h : 0;
         const __amdgpu_buffer_rsrc_t rl =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.lse + lo), (short)0, nrec, 0x00020000);
         const __amdgpu_buffer_rsrc_t rd =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.dd + lo), (short)0, nrec, 0x00020000);
-        lds_load16(rq, b + 512 * wu, (int)oq);
-        lds_load16(rg, b + kKT * kHeadDim + 512 * wu, (int)og);
         lds_load4(rl, bv + kBkvRowVals * wu, (int)lrow_off);
         lds_load4(rd, bv + kBkvRowVals * (4 + wu), (int)lrow_off);
-        // the next tile's row
-        rr += kKT;
-        fr += df;
-        rem += dr;
-        if (rem >= qa) {
-          rem -= qa;
-          fr += 1;
-        }
+        // the next tile's rows
+        rr += TQ;
+#pragma unroll
+        for (int j = 0; j < QT; ++j) adv(fr, rem);
       };
       auto ring_barrier = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0x70 | NDMA);  // vmcnt(NDMA) lgkmcnt(0)
@@ -440,22 +463,47 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
       };
+      // one ring tile: every sub-tile's score and dO . v products first, then
+      // per sub-tile the softmax gradient and the two accumulations
+      auto tile_all = [&](const __bf16* cur, const float* curv) __attribute__((always_inline)) {
+        f32x16 sc[QT], dpv[QT];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+          sc[j] = F::qk(cur + kKT * kHeadDim * j, r, hf, kf);
+          dpv[j] = F::qk(cur + TQ * kHeadDim + kKT * kHeadDim * j, r, hf, vf);
+        }
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+          const float* l2s = curv + kBkvRowVals * wu + kKT * j;
+          const float* dds = l2s + 4 * kBkvRowVals;
+          f32x16 pm, ds;
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 8 * a + 4 * hf);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dds + 8 * a + 4 * hf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pm[4 * a + e] = fast_exp2(fmaf(sc[j][4 * a + e], c, -l4[e]));
+              ds[4 * a + e] = pm[4 * a + e] * (dpv[j][4 * a + e] - d4[e]);
+            }
+          }
+          F::pv(cur + TQ * kHeadDim + kKT * kHeadDim * j, lane, BwdOp<T>::make(pm), dv);
+          F::pv(cur + kKT * kHeadDim * j, lane, BwdOp<T>::make(ds), dk);
+        }
+      };
       auto step = [&](int64_t t, const __bf16* cur, const float* curv, __bf16* fill, float* fillv)
           __attribute__((always_inline)) {
         dma_tile(fill, fillv, t + 2);
-        if (t < t1) {
-          const float* l2s = curv + kBkvRowVals * wu;
-          tile_kv(cur, cur, cur + kKT * kHeadDim, cur + kKT * kHeadDim, l2s, l2s + 4 * kBkvRowVals);
-        }
+        if (t < u1) tile_all(cur, curv);
         ring_barrier();
       };
-      if (t0 < t1) {
+      if (u0 < u1) {
         // the key and value fragments land before any tile load is issued
         __builtin_amdgcn_s_waitcnt(0);
-        dma_tile(bk_ring0, bk_vals0, t0);
-        dma_tile(bk_ring1, bk_vals1, t0 + 1);
+        dma_tile(bk_ring0, bk_vals0, u0);
+        dma_tile(bk_ring1, bk_vals1, u0 + 1);
         ring_barrier();
-        for (int64_t t = t0; t < t1; t += 3) {
+        for (int64_t t = u0; t < u1; t += 3) {
           step(t, bk_ring0, bk_vals0, bk_ring2, bk_vals2);
           step(t + 1, bk_ring1, bk_vals1, bk_ring0, bk_vals0);
           step(t + 2, bk_ring2, bk_vals2, bk_ring1, bk_vals1);
@@ -519,9 +567,9 @@ static hipError_t launch_flash_bwd_t(const FlashBwdParams& p, hipStream_t stream
     // the key-side tile ring: log2 denominators, a query map whose rows never
     // go back (consecutive queries move at most qb token rows), 32-bit row
     // counters and per-wave byte offsets below 2^31
-    const int64_t span = 7 * std::max<int64_t>(p.qb, 1) * p.row_stride * 2 + 128;
+    const int64_t span = (kBkvTQ - kKT + 7) * std::max<int64_t>(p.qb, 1) * p.row_stride * 2 + 128;
     if (p.lse_mul != 1.0f || p.qa < 1 || (p.qb == 0 ? p.n_q > p.qa : p.qb < p.qa) ||
-        p.n_q + 4 * kKT > INT32_MAX || p.n_q * p.n_heads * 4 > INT32_MAX || span > INT32_MAX)
+        p.n_q + 4 * kBkvTQ > INT32_MAX || p.n_q * p.n_heads * 4 > INT32_MAX || span > INT32_MAX)
       return hipErrorInvalidValue;
   }
   // (the bf16 passes use the static tile rings instead)
@@ -687,24 +735,34 @@ hipError_t launch_gate_bwd(int dtype, const GateBwdParams& p, hipStream_t stream
   return hipGetLastError();
 }
 
-// dW_g[h] = sum over windows of the partials: one workgroup per head, a
-// thread per (channel, stride-16 subset of windows), then a fixed-order tree.
-__global__ __launch_bounds__(1024) void dwg_reduce_kernel(DwgParams p) {
-  __shared__ float red[16][kHeadDim];
-  const int h = blockIdx.x, e = threadIdx.x & 63, part = threadIdx.x >> 6;
+// dW_g[h] = sum over windows of the partials, in a fixed order: the windows
+// are cut into kDwgSlices contiguous slices; a workgroup per (slice, head)
+// sums its slice (four interleaved runs, then in order), and one workgroup
+// per head then sums the slice totals.
+__global__ __launch_bounds__(256) void dwg_slice_kernel(DwgParams p) {
+  __shared__ float red[4][kHeadDim];
+  const int sl = blockIdx.x, h = blockIdx.y, e = threadIdx.x & 63, sub = threadIdx.x >> 6;
+  const int64_t per = (p.n_windows + kDwgSlices - 1) / kDwgSlices;
+  const int64_t j0 = sl * per, j1 = j0 + per < p.n_windows ? j0 + per : p.n_windows;
   float acc = 0.0f;
-  for (int64_t j = part; j < p.n_windows; j += 16) acc += p.part[(j * p.n_heads + h) * kHeadDim + e];
-  red[part][e] = acc;
+  for (int64_t j = j0 + sub; j < j1; j += 4) acc += p.part[(j * p.n_heads + h) * kHeadDim + e];
+  red[sub][e] = acc;
   __syncthreads();
-  if (part == 0) {
-    float s = 0.0f;
-    for (int i = 0; i < 16; ++i) s += red[i][e];
-    p.dwg[h * kHeadDim + e] = s;
-  }
+  if (sub == 0) p.slices[((int64_t)sl * p.n_heads + h) * kHeadDim + e] = red[0][e] + red[1][e] + red[2][e] + red[3][e];
+}
+__global__ __launch_bounds__(256) void dwg_total_kernel(DwgParams p) {
+  __shared__ float red[4][kHeadDim];
+  const int h = blockIdx.x, e = threadIdx.x & 63, sub = threadIdx.x >> 6;
+  float acc = 0.0f;
+  for (int sl = sub; sl < kDwgSlices; sl += 4) acc += p.slices[((int64_t)sl * p.n_heads + h) * kHeadDim + e];
+  red[sub][e] = acc;
+  __syncthreads();
+  if (sub == 0) p.dwg[h * kHeadDim + e] = red[0][e] + red[1][e] + red[2][e] + red[3][e];
 }
 
 hipError_t launch_dwg_reduce(const DwgParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(dwg_reduce_kernel, dim3((unsigned)p.n_heads), dim3(1024), 0, stream, p);
+  hipLaunchKernelGGL(dwg_slice_kernel, dim3(kDwgSlices, (unsigned)p.n_heads), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(dwg_total_kernel, dim3((unsigned)p.n_heads), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -120,7 +120,7 @@ struct Plan {
   // backward
   int ctx_qsplits;  // query splits of the context frames' key-side pass
   int64_t qblk, qT, kT, vrow, lse_c, spec_o32, spec_l2, spec_dd, osel, l2sel, doblk, doT, l2blk, dblk,
-      dosel_img, dsel_img, doc, dc, l2c, dwg_part, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list,
+      dosel_img, dsel_img, doc, dc, l2c, dwg_part, dwg_slices, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list,
       ctx_dq, ctx_dkdv;
 };
 
@@ -304,6 +304,7 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.dc = take(wl);
     p.l2c = take(wl);
     p.dwg_part = take(wf);
+    p.dwg_slices = take((int64_t)kDwgSlices * g.n_heads * kHeadDim * 4);
     p.dqc = take(wf);
     p.dkc = take(wf);
     p.dvc = take(wf);
@@ -942,6 +943,7 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   dp.part = gp.dwg_part;
   dp.n_windows = g.n_windows;
   dp.n_heads = (int)H;
+  dp.slices = reinterpret_cast<float*>(at(ws, pl.dwg_slices));
   dp.dwg = dwg;
   ok(launch_dwg_reduce(dp, st));
 

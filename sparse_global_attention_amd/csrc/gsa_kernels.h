@@ -338,10 +338,12 @@ struct PoolBwdParams {
 };
 hipError_t launch_pool_bwd(const PoolBwdParams& p, hipStream_t stream);
 
+constexpr int kDwgSlices = 512;  // window slices of the dW_g reduction
 struct DwgParams {
   const float* part;  // [M'][H][d]
   int64_t n_windows;
   int n_heads;
+  float* slices;      // [kDwgSlices][H][d] slice totals (scratch)
   float* dwg;         // [H][d]
 };
 hipError_t launch_dwg_reduce(const DwgParams& p, hipStream_t stream);
