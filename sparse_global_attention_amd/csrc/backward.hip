@@ -895,6 +895,61 @@ __global__ __launch_bounds__(256) void inv_sort_kernel(InvParams p) {
   }
 }
 
+// Processing order of the key side of the selection backward: the (head,
+// window) lists by length class, longest first (class 0: 512 entries or
+// more, then one class per power of two, class 7: under 8), in list order
+// within a class, so the long lists do not start last and leave a tail.  A
+// counting sort: per block of 1024 lists the class counts, an exclusive scan
+// of the class-major counts, then each block writes its lists at the
+// scanned positions.
+constexpr int kOrdClasses = 8;
+constexpr int kOrdBlock = 1024;
+__device__ __forceinline__ int list_class(int32_t n) {
+  const int bits = 32 - __builtin_clz((uint32_t)n | 1u);
+  const int c = 10 - bits;
+  return c < 0 ? 0 : (c > kOrdClasses - 1 ? kOrdClasses - 1 : c);
+}
+__global__ __launch_bounds__(256) void order_count_kernel(InvParams p) {
+  __shared__ int32_t cnt[kOrdClasses];
+  const int64_t segs = p.n_windows * p.n_heads;
+  const int64_t nblk = (segs + kOrdBlock - 1) / kOrdBlock;
+  if (threadIdx.x < kOrdClasses) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  for (int e = 0; e < kOrdBlock / 256; ++e) {
+    const int64_t seg = (int64_t)blockIdx.x * kOrdBlock + e * 256 + threadIdx.x;
+    if (seg < segs) atomicAdd(&cnt[list_class(p.off[seg + 1] - p.off[seg])], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < kOrdClasses) p.ccnt[threadIdx.x * nblk + blockIdx.x] = cnt[threadIdx.x];
+}
+__global__ __launch_bounds__(256) void order_fill_kernel(InvParams p) {
+  __shared__ int32_t wcnt[kOrdBlock / 64][kOrdClasses];  // per 64-list group, in list order
+  const int64_t segs = p.n_windows * p.n_heads;
+  const int64_t nblk = (segs + kOrdBlock - 1) / kOrdBlock;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  int cls[kOrdBlock / 256];
+  uint64_t below[kOrdBlock / 256];
+  for (int e = 0; e < kOrdBlock / 256; ++e) {
+    const int64_t seg = (int64_t)blockIdx.x * kOrdBlock + e * 256 + threadIdx.x;
+    cls[e] = seg < segs ? list_class(p.off[seg + 1] - p.off[seg]) : -1;
+    uint64_t mine = 0;
+    for (int c = 0; c < kOrdClasses; ++c) {
+      const uint64_t m = __ballot(cls[e] == c);
+      if (cls[e] == c) mine = m;
+      if (lane == 0) wcnt[e * 4 + wv][c] = __builtin_popcountll(m);
+    }
+    below[e] = mine & ((1ull << lane) - 1);
+  }
+  __syncthreads();
+  for (int e = 0; e < kOrdBlock / 256; ++e) {
+    if (cls[e] < 0) continue;
+    const int c = cls[e], grp = e * 4 + wv;
+    int32_t pos = p.ccnt[c * nblk + blockIdx.x] + __builtin_popcountll(below[e]);
+    for (int g = 0; g < grp; ++g) pos += wcnt[g][c];
+    p.order[pos] = (int32_t)((int64_t)blockIdx.x * kOrdBlock + e * 256 + threadIdx.x);
+  }
+}
+
 hipError_t launch_inverse_index(const InvParams& p, hipStream_t stream) {
   const int64_t segs = p.n_windows * p.n_heads;
   const int64_t n = segs + 1;
@@ -911,6 +966,16 @@ hipError_t launch_inverse_index(const InvParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(scan_add_kernel, dim3(gz), dim3(256), 0, stream, p.off, n, (const int32_t*)p.bsum);
   hipLaunchKernelGGL(inv_fill_kernel, dim3(ge), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(inv_sort_kernel, dim3((unsigned)((segs + 3) / 4)), dim3(256), 0, stream, p);
+  if (p.order) {
+    const int64_t ob = (segs + kOrdBlock - 1) / kOrdBlock, nc = kOrdClasses * ob;
+    const int64_t ncb = (nc + kScanBlock - 1) / kScanBlock;
+    hipLaunchKernelGGL(order_count_kernel, dim3((unsigned)ob), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(scan_blocks_kernel, dim3((unsigned)ncb), dim3(256), 0, stream, p.ccnt, nc, p.cbsum);
+    hipLaunchKernelGGL(scan_sums_kernel, dim3(1), dim3(256), 0, stream, p.cbsum, ncb);
+    hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, stream, p.ccnt, nc,
+                       (const int32_t*)p.cbsum);
+    hipLaunchKernelGGL(order_fill_kernel, dim3((unsigned)ob), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -1097,8 +1162,10 @@ __global__ __launch_bounds__(256) void sel_dkdv_kernel(SelBwdParams p) {
   const int64_t item = (int64_t)blockIdx.x * 4 + wv;
   if (item >= geo.n_windows * geo.n_heads * n_grp) return;
   const int kg = (int)(item % n_grp);
-  const int64_t h = item / n_grp / geo.n_windows;
-  const int64_t win = item / n_grp % geo.n_windows;
+  // (head, window) lists in the longest-first order when one is given
+  const int64_t seg = p.order ? p.order[item / n_grp] : item / n_grp;
+  const int64_t h = seg / geo.n_windows;
+  const int64_t win = seg % geo.n_windows;
   const int64_t H = geo.n_heads, sb = geo.sb;
   const float c = p.scale_log2;
   const int32_t lb = p.inv_off[h * geo.n_windows + win];

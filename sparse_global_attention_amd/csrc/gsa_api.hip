@@ -120,7 +120,7 @@ struct Plan {
   // backward
   int ctx_qsplits;  // query splits of the context frames' key-side pass
   int64_t qblk, qT, kT, vrow, lse_c, spec_o32, spec_l2, spec_dd, osel, l2sel, doblk, doT, l2blk, dblk,
-      dosel_img, dsel_img, doc, dc, l2c, dwg_part, dwg_slices, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list,
+      dosel_img, dsel_img, doc, dc, l2c, dwg_part, dwg_slices, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list, inv_order, inv_ccnt, inv_cbsum,
       ctx_dq, ctx_dkdv;
 };
 
@@ -313,6 +313,10 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.inv_bsum = take(((segs + 1 + 1023) / 1024) * 4);
     p.inv_raw = take(entries * 4);
     p.inv_list = take(entries * 4);
+    const int64_t oblk = (segs + 1023) / 1024;
+    p.inv_order = take(segs * 4);
+    p.inv_ccnt = take(8 * oblk * 4);
+    p.inv_cbsum = take(((8 * oblk + 1023) / 1024) * 4);
   }
   p.total = off;
   return p;
@@ -1044,6 +1048,9 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   ip.bsum = reinterpret_cast<int32_t*>(at(ws, pl.inv_bsum));
   ip.raw = reinterpret_cast<int32_t*>(at(ws, pl.inv_raw));
   ip.list = reinterpret_cast<int32_t*>(at(ws, pl.inv_list));
+  ip.order = reinterpret_cast<int32_t*>(at(ws, pl.inv_order));
+  ip.ccnt = reinterpret_cast<int32_t*>(at(ws, pl.inv_ccnt));
+  ip.cbsum = reinterpret_cast<int32_t*>(at(ws, pl.inv_cbsum));
   ok(launch_inverse_index(ip, st));
   SelBwdParams sb;
   sb.qblk = at(ws, pl.qblk);
@@ -1059,6 +1066,7 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   sb.topk = c.topk;
   sb.inv_off = ip.off;
   sb.inv_list = ip.list;
+  sb.order = ip.order;
   sb.g = g;
   sb.scale = c.scale;
   sb.scale_log2 = c.scale * kLog2e;

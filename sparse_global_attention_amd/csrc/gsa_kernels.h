@@ -301,6 +301,9 @@ struct InvParams {
   int32_t* bsum;    // scan block sums
   int32_t* raw;     // [H*M'*k] lists in fill order
   int32_t* list;    // [H*M'*k] lists, ascending
+  int32_t* order;   // optional [H*M']: (head, window) lists, longest length class first
+  int32_t* ccnt;    // [8 * ceil(H*M' / 1024)] class counts per block, then their scan
+  int32_t* cbsum;   // scan block sums of ccnt
 };
 hipError_t launch_inverse_index(const InvParams& p, hipStream_t stream);
 
@@ -318,6 +321,7 @@ struct SelBwdParams {
   int topk;
   const int32_t* inv_off;
   const int32_t* inv_list;
+  const int32_t* order;  // optional processing order of the key side (head * M' + window)
   Geometry g;
   float scale, scale_log2;
   float* dq;  // token rows (float), added
