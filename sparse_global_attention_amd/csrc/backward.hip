@@ -21,7 +21,9 @@
 //                       window's top-k list, the key side walks the inverse
 //                       list (the query windows that selected it); bf16 chunks
 //                       are transposed in LDS, fp32 ones gathered twice;
-//  * inverse-index, reduction, pooling-backward and dW_g kernels.
+//  * inverse-index, reduction and dW_g kernels.  The pooling backward (each
+//    window token gets its pooled row's gradient / s^2) is folded into the
+//    selection kernels' stores, which touch the same token rows.
 // All sums run in a fixed order, so the gradients are deterministic.
 #include <math.h>
 
@@ -1141,15 +1143,18 @@ __global__ __launch_bounds__(256) void sel_dq_kernel(SelBwdParams p) {
     const int64_t tok = window_token(geo, win, kq);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      // + the pooled row's gradient / s^2 (the pooling backward)
+      const f32x4 pooled = *reinterpret_cast<const f32x4*>(p.dqc + (win * H + h) * kHeadDim + 16 * m + 4 * g);
       f32x4* dst = reinterpret_cast<f32x4*>(p.dq + (tok * H + h) * kHeadDim + 16 * m + 4 * g);
-      *dst = *dst + acc[b][m] * p.scale;
+      *dst = *dst + acc[b][m] * p.scale + pooled * p.inv_area;
     }
   }
 }
 
 // Key side: one wave per (key window, head, group of KB blocks of 16 keys);
 // per chunk of the inverse list's query slots: S^T = Q K^T, P, dP^T = dO V^T,
-// dS, dv^T += dO^T P, dk^T += Q^T dS.  Adds scale * dk and dv into the key rows.
+// dS, dv^T += dO^T P, dk^T += Q^T dS.  Adds scale * dk and dv, and the pooled
+// rows' gradients / s^2, into the key rows.
 template <typename T, int KB>
 __global__ __launch_bounds__(256) void sel_dkdv_kernel(SelBwdParams p) {
   using F = Frag16<T>;
@@ -1261,10 +1266,14 @@ __global__ __launch_bounds__(256) void sel_dkdv_kernel(SelBwdParams p) {
     const int64_t tok = window_token(geo, win, kk);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      // + the pooled rows' gradients / s^2 (the pooling backward)
+      const int64_t pr = (win * H + h) * kHeadDim + 16 * m + 4 * g;
+      const f32x4 pk = *reinterpret_cast<const f32x4*>(p.dkc + pr);
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(p.dvc + pr);
       f32x4* k4 = reinterpret_cast<f32x4*>(p.dk + (tok * H + h) * kHeadDim + 16 * m + 4 * g);
       f32x4* v4 = reinterpret_cast<f32x4*>(p.dv + (tok * H + h) * kHeadDim + 16 * m + 4 * g);
-      *k4 = *k4 + dk[b][m] * p.scale;
-      *v4 = *v4 + dv[b][m];
+      *k4 = *k4 + dk[b][m] * p.scale + pk * p.inv_area;
+      *v4 = *v4 + dv[b][m] + pv * p.inv_area;
     }
   }
 }
@@ -1290,30 +1299,6 @@ hipError_t launch_sel_bwd(int dtype, const SelBwdParams& p, hipStream_t stream) 
   const unsigned blocks = (unsigned)((items + 3) / 4);
   if (dtype == kBF16) launch_sel_t<__bf16>(p, n_sub, blocks, stream);
   else launch_sel_t<float>(p, n_sub, blocks, stream);
-  return hipGetLastError();
-}
-
-// ---- pooling backward: each window token gets its pooled row's gradient / s^2 ----
-__global__ __launch_bounds__(256) void pool_bwd_kernel(PoolBwdParams p) {
-  const Geometry& g = p.g;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_tok = g.n_heads * (kHeadDim / 4);
-  if (gid >= g.m_img * per_tok) return;
-  const int64_t u = gid / per_tok, rem = gid - u * per_tok;
-  const int64_t hw = g.grid_h * g.grid_w;
-  const int64_t f = u / hw, pix = u % hw, y = pix / g.grid_w, x = pix % g.grid_w;
-  const int64_t tok = f * g.tf + g.n_special + pix;
-  const int64_t win = f * g.wpf + (y / g.pool) * g.wx + x / g.pool;
-  const int64_t src = win * per_tok + rem, dst = tok * per_tok + rem;
-  reinterpret_cast<f32x4*>(p.dq)[dst] += reinterpret_cast<const f32x4*>(p.dqc)[src] * p.inv_area;
-  reinterpret_cast<f32x4*>(p.dk)[dst] += reinterpret_cast<const f32x4*>(p.dkc)[src] * p.inv_area;
-  reinterpret_cast<f32x4*>(p.dv)[dst] += reinterpret_cast<const f32x4*>(p.dvc)[src] * p.inv_area;
-}
-
-hipError_t launch_pool_bwd(const PoolBwdParams& p, hipStream_t stream) {
-  const int64_t threads = p.g.m_img * p.g.n_heads * (kHeadDim / 4);
-  if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(pool_bwd_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -1037,7 +1037,8 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
     ok(launch_flash_bwd(c.dtype, kBwdDKDV, b, st));
   }
 
-  // 6. selection: inverse top-k lists, then the query and key sides
+  // 6. selection: inverse top-k lists, then the query and key sides (their
+  //    stores also add each window token's pooled-row gradient / s^2)
   InvParams ip;
   ip.topk_idx = topk_idx;
   ip.topk = c.topk;
@@ -1070,6 +1071,10 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   sb.g = g;
   sb.scale = c.scale;
   sb.scale_log2 = c.scale * kLog2e;
+  sb.dqc = dqc;
+  sb.dkc = dkc;
+  sb.dvc = dvc;
+  sb.inv_area = 1.0f / (float)(g.pool * g.pool);
   sb.dq = dq;
   sb.dk = dk;
   sb.dv = dv;
@@ -1144,17 +1149,6 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
     }
   }
 
-  // 8. pooling: each window token gets its pooled row's gradient / s^2
-  PoolBwdParams pb;
-  pb.dqc = dqc;
-  pb.dkc = dkc;
-  pb.dvc = dvc;
-  pb.g = g;
-  pb.inv_area = 1.0f / (float)(g.pool * g.pool);
-  pb.dq = dq;
-  pb.dk = dk;
-  pb.dv = dv;
-  ok(launch_pool_bwd(pb, st));
   return hip_status(e);
 }
 

@@ -324,23 +324,15 @@ struct SelBwdParams {
   const int32_t* order;  // optional processing order of the key side (head * M' + window)
   Geometry g;
   float scale, scale_log2;
-  float* dq;  // token rows (float), added
+  const float* dqc;  // [M'][H][d] gradients of the pooled rows (the compressed branch's)
+  const float* dkc;
+  const float* dvc;
+  float inv_area;    // 1 / s^2
+  float* dq;  // token rows (float), added: selection gradient + pooled row's / s^2
   float* dk;
   float* dv;
 };
 hipError_t launch_sel_bwd(int dtype, const SelBwdParams& p, hipStream_t stream);
-
-struct PoolBwdParams {
-  const float* dqc;  // [M'][H][d]
-  const float* dkc;
-  const float* dvc;
-  Geometry g;
-  float inv_area;
-  float* dq;  // token rows (float), added
-  float* dk;
-  float* dv;
-};
-hipError_t launch_pool_bwd(const PoolBwdParams& p, hipStream_t stream);
 
 constexpr int kDwgSlices = 512;  // window slices of the dW_g reduction
 struct DwgParams {
