@@ -627,7 +627,8 @@ hipError_t launch_fill(float* x, int64_t n, hipStream_t stream) {
 // One wave per (window, head); 16 lanes per token (4 channels each), four
 // tokens per step.  Per image token t (window i, in-window index kk):
 //   g = sigmoid(W_g . q),  dO_sel = (1 - g) dO,  D_sel = dO_sel . O_sel,
-//   dz = (dO . (O'_i - O_sel)) g (1 - g),  dq = dz W_g (stored),
+//   dz = (dO . (O'_i - O_sel)) g (1 - g) (stored; the selection backward
+//   writes the token's dq = dz W_g + ...),
 // and per window: dO_comp = sum_t g dO, D_comp = dO_comp . O'_i, the dW_g
 // partial sum_t dz q, and the compressed attention's log2 denominator.
 template <typename T>
@@ -689,7 +690,6 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdParams p) {
     const f32x4 ds4 = (1.0f - g) * g4;
     const float dsel = sum16(dot4(ds4, os4));
     if (valid) {
-      *reinterpret_cast<f32x4*>(p.dq + (tok * H + h) * kHeadDim + ch) = dz * w4;
       acc_dwg += dz * q4;
       acc_doc += g * g4;
       if (p.dosel_img) {
@@ -706,6 +706,7 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(GateBwdParams p) {
     if (cl == 0) {
       p.l2blk[(win * H + h) * sb + kk] = valid ? p.l2sel[u * H + h] : INFINITY;
       p.dblk[(win * H + h) * sb + kk] = valid ? dsel : 0.0f;
+      p.dzblk[(win * H + h) * sb + kk] = valid ? dz : 0.0f;
     }
   }
 #pragma unroll
@@ -1051,7 +1052,8 @@ __shared__ __attribute__((aligned(16))) __bf16 sel_slab[4][2][kSlabElems];
 
 // Query side: one wave per (window, head, group of QB blocks of 16 queries);
 // per chunk of the window's top-k slots: S^T = K Q^T, P, dP^T = V dO^T,
-// dS, dq^T += K^T dS.  Adds scale * dq into the query rows.
+// dS, dq^T += K^T dS.  Stores dz W_g + scale * dq + the pooled row's gradient / s^2
+// into the query rows (their first store).
 template <typename T, int QB>
 __global__ __launch_bounds__(256) void sel_dq_kernel(SelBwdParams p) {
   using F = Frag16<T>;
@@ -1075,7 +1077,7 @@ __global__ __launch_bounds__(256) void sel_dq_kernel(SelBwdParams p) {
   const int n_chunks = (int)((K * sb + 31) / 32);
 
   typename F::Q qfs[QB], gfs[QB];
-  float l2s[QB], dds[QB];
+  float l2s[QB], dds[QB], dzs[QB];
   f32x4 acc[QB][4];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
@@ -1086,6 +1088,7 @@ __global__ __launch_bounds__(256) void sel_dq_kernel(SelBwdParams p) {
     gfs[b] = F::load_q(qvalid ? static_cast<const T*>(p.doblk) + row * kHeadDim : nullptr, g);
     l2s[b] = qvalid ? p.l2blk[row] : INFINITY;
     dds[b] = qvalid ? p.dblk[row] : 0.0f;
+    dzs[b] = qvalid ? p.dzblk[row] : 0.0f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[b][m] = f32x4{0, 0, 0, 0};
   }
@@ -1143,10 +1146,12 @@ __global__ __launch_bounds__(256) void sel_dq_kernel(SelBwdParams p) {
     const int64_t tok = window_token(geo, win, kq);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      // + the pooled row's gradient / s^2 (the pooling backward)
+      // the gate's dz W_g, + this branch's gradient, + the pooled row's
+      // gradient / s^2 (the pooling backward): the first store of the row
+      const f32x4 w4 = load4(static_cast<const T*>(p.wg) + h * kHeadDim + 16 * m + 4 * g);
       const f32x4 pooled = *reinterpret_cast<const f32x4*>(p.dqc + (win * H + h) * kHeadDim + 16 * m + 4 * g);
       f32x4* dst = reinterpret_cast<f32x4*>(p.dq + (tok * H + h) * kHeadDim + 16 * m + 4 * g);
-      *dst = *dst + acc[b][m] * p.scale + pooled * p.inv_area;
+      *dst = dzs[b] * w4 + acc[b][m] * p.scale + pooled * p.inv_area;
     }
   }
 }

@@ -120,8 +120,8 @@ struct Plan {
   // backward
   int ctx_qsplits;  // query splits of the context frames' key-side pass
   int64_t qblk, qT, kT, vrow, lse_c, spec_o32, spec_l2, spec_dd, osel, l2sel, doblk, doT, l2blk, dblk,
-      dosel_img, dsel_img, doc, dc, l2c, dwg_part, dwg_slices, dqc, dkc, dvc, inv_off, inv_cursor, inv_bsum, inv_raw, inv_list, inv_order, inv_ccnt, inv_cbsum,
-      ctx_dq, ctx_dkdv;
+      dzblk, dosel_img, dsel_img, doc, dc, l2c, dwg_part, dwg_slices, dqc, dkc, dvc;
+  int64_t inv_off, inv_cursor, inv_bsum, inv_raw, inv_list, inv_order, inv_ccnt, inv_cbsum, ctx_dq, ctx_dkdv;
 };
 
 // Training state saved by gsa_forward_train for gsa_backward_train.
@@ -294,6 +294,7 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.doT = take(tblk);
     p.l2blk = take(bl);
     p.dblk = take(bl);
+    p.dzblk = take(bl);
     if (c.n_ctx) {
       p.dosel_img = take(g.m_img * g.n_heads * kHeadDim * c.esz);
       p.dsel_img = take(g.m_img * g.n_heads * 4);
@@ -918,7 +919,8 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
     ok(launch_select(c.dtype, sp, st));
   }
 
-  // 3. gate: dq (image rows) = dz W_g, dO_sel blocks, dO_comp, dW_g partials
+  // 3. gate: dz (the selection backward stores dq = dz W_g + ...), dO_sel blocks,
+  //    dO_comp, dW_g partials
   GateBwdParams gp;
   memset(&gp, 0, sizeof(gp));
   gp.q = q;
@@ -928,7 +930,7 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   gp.osel = osel;
   gp.l2sel = l2sel;
   gp.g = g;
-  gp.dq = dq;
+  gp.dzblk = reinterpret_cast<float*>(at(ws, pl.dzblk));
   gp.doblk = at(ws, pl.doblk);
   gp.doT = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.doT);
   gp.l2blk = reinterpret_cast<float*>(at(ws, pl.l2blk));
@@ -1063,6 +1065,8 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   sb.doT = gp.doT;
   sb.l2blk = gp.l2blk;
   sb.dblk = gp.dblk;
+  sb.dzblk = gp.dzblk;
+  sb.wg = wg;
   sb.topk_idx = topk_idx;
   sb.topk = c.topk;
   sb.inv_off = ip.off;

@@ -274,7 +274,7 @@ struct GateBwdParams {
   const float* osel;   // [M_img][H][d]
   const float* l2sel;  // [M_img][H]
   Geometry g;
-  float* dq;           // token rows (float): image rows stored = dz W_g
+  float* dzblk;        // [M'][H][sb] dz = dO . (O'_i - O_sel) g (1 - g) (0 on padding)
   void* doblk;         // [M'][H][sb][d] dO_sel rows (dtype)
   void* doT;           // [M'][H][d][sb] dO_sel transposed (dtype), or null (bf16: transposed in LDS)
   float* l2blk;        // [M'][H][sb] (+inf on padding)
@@ -317,6 +317,8 @@ struct SelBwdParams {
   const void* doT;
   const float* l2blk;
   const float* dblk;
+  const float* dzblk;  // [M'][H][sb] the gate's dz per query slot
+  const void* wg;      // [H][d] W_g (dtype)
   const int32_t* topk_idx;
   int topk;
   const int32_t* inv_off;
@@ -328,7 +330,7 @@ struct SelBwdParams {
   const float* dkc;
   const float* dvc;
   float inv_area;    // 1 / s^2
-  float* dq;  // token rows (float), added: selection gradient + pooled row's / s^2
+  float* dq;  // token rows (float): image rows stored = dz W_g + selection gradient + pooled row's / s^2
   float* dk;
   float* dv;
 };
