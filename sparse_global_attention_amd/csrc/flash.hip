@@ -85,7 +85,11 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   // batch, e.g. 21 of a frame's 128-row tail tile) still loads its share of
   // every key tile and meets the others at each barrier, but skips the
   // matrix-core and softmax work, leaving its SIMD to the other workgroups.
-  const bool wave_live = wave_any(qvalid);
+  // Not in the split-K partial sweeps: there the 40-odd query tiles of a key
+  // range stream the same K/V tiles through L2 together, and the faster tail
+  // workgroup among them raised the special attention's HBM fetch from 10.7
+  // to 39 GB per launch at 1000 frames (and its time by ~3 %).
+  const bool wave_live = MODE == kFlashPartial || wave_any(qvalid);
   const int64_t hoff = (int64_t)h * kHeadDim;
   const int64_t qtok = batch * p.q_bstride + (qrow / p.qa) * p.qb + p.qc + qrow % p.qa;
   const T* K = static_cast<const T*>(p.k);
