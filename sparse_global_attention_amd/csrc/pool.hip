@@ -16,6 +16,8 @@
 //   trans [M'][H][d][sb]  transposed (tokens contiguous per channel), the
 //                         layout of an operand that contracts over tokens.
 // The forward uses K rows and V transposed; the backward also Q, K^T, V rows.
+#include <type_traits>
+
 #include "gsa_device.h"
 #include "gsa_kernels.h"
 
@@ -46,43 +48,50 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 #pragma unroll
   for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
 
-  // Walk the window's keys 8 at a time (sb is a multiple of 8).
-  for (int k0 = 0; k0 < g.sb; k0 += 8) {
-    uint4 chunk[8];
+  // Walk the window's keys KS at a time (sb is a multiple of 8): 16 when sb
+  // allows, so each channel's 32-byte row of the transposed copy is stored
+  // whole (two halves stored one pass apart were evicted from L2 separately:
+  // the copy's HBM writes doubled).
+  auto walk = [&](auto ks_tag) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks_tag)::value;
+    for (int k0 = 0; k0 < g.sb; k0 += KS) {
+      uint4 chunk[KS];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      int kk = k0 + t;
-      chunk[t] = kk < s2 ? ld16(src + window_token(g, j, kk) * row + col) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (k0 + t < s2) {
-        const T* x = reinterpret_cast<const T*>(&chunk[t]);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[e] += to_f32(x[e]);
+      for (int t = 0; t < KS; ++t) {
+        const int kk = k0 + t;
+        chunk[t] = kk < s2 ? ld16(src + window_token(g, j, kk) * row + col) : make_uint4(0, 0, 0, 0);
       }
-    }
-    if (kb) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) st16(kb + (k0 + t) * kHeadDim + c * VE, chunk[t]);
-    }
-    if (vb) {
-      // channel c*VE+e gets keys k0..k0+7: 8 consecutive elements
+      for (int t = 0; t < KS; ++t) {
+        if (k0 + t < s2) {
+          const T* x = reinterpret_cast<const T*>(&chunk[t]);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        T col8[8];
+          for (int e = 0; e < VE; ++e) acc[e] += to_f32(x[e]);
+        }
+      }
+      if (kb) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) col8[t] = reinterpret_cast<const T*>(&chunk[t])[e];
-        T* dst = vb + (c * VE + e) * g.sb + k0;
-        if constexpr (sizeof(T) == 2) {
-          st16(dst, *reinterpret_cast<const uint4*>(col8));
-        } else {
-          st16(dst, *reinterpret_cast<const uint4*>(col8));
-          st16(dst + 4, *reinterpret_cast<const uint4*>(col8 + 4));
+        for (int t = 0; t < KS; ++t) st16(kb + (k0 + t) * kHeadDim + c * VE, chunk[t]);
+      }
+      if (vb) {
+        // channel c*VE+e gets keys k0 .. k0+KS-1: KS consecutive elements
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          T colk[KS];
+#pragma unroll
+          for (int t = 0; t < KS; ++t) colk[t] = reinterpret_cast<const T*>(&chunk[t])[e];
+          T* d = vb + (c * VE + e) * g.sb + k0;
+#pragma unroll
+          for (int q = 0; q < KS * (int)sizeof(T) / 16; ++q)
+            st16(d + q * VE, *reinterpret_cast<const uint4*>(colk + q * VE));
         }
       }
     }
-  }
+  };
+  if (g.sb % 16 == 0)
+    walk(std::integral_constant<int, 16>{});
+  else
+    walk(std::integral_constant<int, 8>{});
 
   T* dst = static_cast<T*>(p.dst[tensor]);
   if (dst) {
