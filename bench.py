@@ -83,7 +83,15 @@ KERNEL_SOURCES = {
     "pool_kernel<bf16>": ("pool.hip",) + _COMMON,
     "combine_kernel<bf16>": ("select.hip", "select_frag.h") + _COMMON,
     "merge_kernel<bf16>": ("flash.hip", "flash_frag.h") + _COMMON,
+    "flash_kernel<bf16,4,partial>,rloop": ("flash.hip", "flash_frag.h") + _COMMON,
+    "descriptor_kernel": ("descriptor.hip",) + _COMMON,
 }
+# the backward's kernels (all in backward.hip)
+KERNEL_SOURCES.update({k: ("backward.hip", "flash_frag.h", "select_frag.h") + _COMMON for k in (
+    "flash_bwd_kernel<bf16,4,dq>", "flash_bwd_kernel<bf16,4,dkdv>", "sel_dq_kernel", "sel_dkdv_kernel",
+    "gate_bwd_kernel", "dwg_slice_kernel", "dwg_total_kernel", "inv_zero_kernel", "inv_count_kernel",
+    "scan_blocks_kernel", "scan_sums_kernel", "scan_add_kernel", "inv_fill_kernel", "inv_sort_kernel",
+    "order_count_kernel", "order_fill_kernel", "reduce_kernel", "fill_kernel")})
 # the kernels of gsa_compressed_attn_topk, in launch order
 COMPRESSED_KERNELS = ("flash_kernel<bf16,4,bound>", "threshold_kernel<64>", "hot_group_kernel<bf16,8>",
                       "rank_kernel", "refine_kernel<bf16,4,64>")
