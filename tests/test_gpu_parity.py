@@ -39,6 +39,9 @@ SHAPES = {
     "k40": GSAShape("k40 10f-16x16-h2-s4-k40", 10, 1, 16, 16, 2, 64, 4, 40, BF16, seed=32),
     "k64": GSAShape("k64 10f-16x16-h2-s4-k64", 10, 1, 16, 16, 2, 64, 4, 64, BF16, seed=30),
     "k128": GSAShape("k128 10f-16x16-h1-s4-k128", 10, 1, 16, 16, 1, 64, 4, 128, BF16, seed=31),
+    # fp32 with k above 48: the fallback sweep's large tier (144 slots, two
+    # waves per workgroup so its fp32 key tiles fit in LDS)
+    "k64_f32": GSAShape("k64 10f-16x16-h2-s4-k64 fp32", 10, 1, 16, 16, 2, 64, 4, 64, F32, seed=55),
     # enough key tiles for at least k groups: theta is finite and the top-k
     # comes from the hot groups' candidate lists (the shapes above with fewer
     # groups than k, or k beyond the candidates, take the full-sweep path)
