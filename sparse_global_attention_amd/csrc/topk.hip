@@ -194,9 +194,13 @@ __global__ __launch_bounds__(WAVES * 64) void hot_group_kernel(TopkParams p) {
           for (int i = 0; i < 16; ++i)
             if (8 * (i / 4) + (i % 4) >= lim) s[i] = -INFINITY;
         }
+        // bit i: s[i] >= th, i.e. the sign bit of s[i] - th clear (th is finite
+        // for a hot query, +inf for an empty lane; masked keys are -inf), shifted
+        // in from the top with one v_alignbit per key
         uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m |= (s[i] >= th ? 1u : 0u) << i;
+        for (int i = 15; i >= 0; --i) m = __builtin_amdgcn_alignbit(m, __float_as_uint(s[i] - th), 31);
+        m = ~m & 0xffffu;
         if (p.n_excl) {
           const uint32_t em = excl.mask(p, key0);
 #pragma unroll
