@@ -41,12 +41,11 @@ constexpr float kLazyRescale = 8.0f; // rescale only when the max grows by > 2^8
 constexpr float kSumLimit = 0x1p64f;
 
 // ---- the kernel ---------------------------------------------------------------
-// The ring of bf16 K/V tile buffers (three separate arrays, so the compiler
-// can tell which buffer a global-to-LDS load writes and wait only for that).
-// Only the kernels that use them get them allocated.
-__shared__ __attribute__((aligned(16))) __bf16 ring0[kKT * kHeadDim * 2];
-__shared__ __attribute__((aligned(16))) __bf16 ring1[kKT * kHeadDim * 2];
-__shared__ __attribute__((aligned(16))) __bf16 ring2[kKT * kHeadDim * 2];
+// The ring of bf16 K/V tile buffers: two buffers of two 32-key tiles each
+// (separate arrays, so the compiler can tell which buffer a global-to-LDS
+// load writes).  Only the kernels that use them get them allocated.
+__shared__ __attribute__((aligned(16))) __bf16 ring64a[kKT * kHeadDim * 4];
+__shared__ __attribute__((aligned(16))) __bf16 ring64b[kKT * kHeadDim * 4];
 
 // The bf16 bound mode asks for four workgroups per CU (at most 128 VGPRs),
 // the occupancy of the plain attention modes.
@@ -273,17 +272,21 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
   };
 
   if constexpr (DMA) {
-    // Ring of three tile buffers.  Step t issues the loads of tile t+2 into
-    // the buffer tile t-1 used (every wave left it at the last barrier),
-    // computes tile t, waits for its own loads of tile t+1 (only tile t+2's
-    // stay in flight: loads complete in order) and meets the other waves at
-    // a barrier, after which tile t+1 is complete in LDS.
+    // Two buffers of two tiles (64 keys).  Step u issues the loads of tiles
+    // 2u+2 and 2u+3 into the buffer step u-1 used (every wave left it at the
+    // last barrier), computes tiles 2u and 2u+1 (those past the last are
+    // skipped), waits for its own loads and meets the other waves at a
+    // barrier, after which the next pair is complete in LDS: one barrier per
+    // 64 keys with two tiles' compute to cover the loads (a ring of three
+    // 32-key tiles, the same prefetch distance, was 0.3 ms slower on the
+    // compressed step at 1000 frames).
     // A tile is 512 16-byte chunks: K chunks 0..255, then V.  This wave
     // loads NDMA of them, lane l chunk 64 (WAVES j + wave) + l into the same
     // LDS chunk, which holds chunk c' of key row (chunk % 256) / 8 of its
     // operand, i.e. that row's global chunk c' ^ swz(row).
     constexpr int NDMA = (2 * kKT * kHeadDim / 8) / (WAVES * 64);
     static_assert(NDMA >= 1 && NDMA * WAVES * 64 == 2 * kKT * kHeadDim / 8, "tile must split evenly over the waves");
+    constexpr int TE = kKT * kHeadDim * 2;  // elements of one tile (K, then V)
     const int wu = __builtin_amdgcn_readfirstlane(wv);
     int goff[NDMA];
 #pragma unroll
@@ -301,34 +304,34 @@ __global__ __launch_bounds__(WAVES * 64, MODE == kFlashBound && sizeof(T) == 2 ?
         lds_load16(c0 < 256 ? rk : rv, buf + 8 * c0, goff[j]);
       }
     };
-    // Wait until at most the NDMA loads of the newest tile are in flight
-    // and every LDS read has returned, then meet at the barrier.  No memory
-    // fence: a workgroup release fence would also wait for the newest tile's
-    // loads.  The compiler barriers keep every memory access on its side.
-    auto ring_barrier = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_s_waitcnt(0x70 | NDMA);  // vmcnt(NDMA) lgkmcnt(0), expcnt untouched
+    auto dma_pair = [&](__bf16* buf, int u) __attribute__((always_inline)) {
+      dma_tile(buf, 2 * u);
+      dma_tile(buf + TE, 2 * u + 1);
+    };
+    // Wait for this wave's loads and every LDS read, then meet at the
+    // barrier.  No memory fence (the waits cover it); the compiler barriers
+    // keep every memory access on its side.
+    auto pair_barrier = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0x70);  // vmcnt(0) lgkmcnt(0), expcnt untouched
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
-    dma_tile(ring0, 0);
-    dma_tile(ring1, 1);
-    ring_barrier();
-    auto step = [&](int t, const __bf16* cur, __bf16* fill) __attribute__((always_inline)) {
-      dma_tile(fill, t + 2);
-      compute(t, cur);
-      ring_barrier();
+    dma_pair(ring64a, 0);
+    pair_barrier();
+    auto step = [&](int u, const __bf16* cur, __bf16* fill) __attribute__((always_inline)) {
+      dma_pair(fill, u + 1);
+      if (2 * u < n_tiles) compute(2 * u, cur);
+      if (2 * u + 1 < n_tiles) compute(2 * u + 1, cur + TE);
+      pair_barrier();
     };
-    for (int t = 0; t < n_tiles; t += 3) {
-      step(t, ring0, ring2);
-      step(t + 1, ring1, ring0);
-      step(t + 2, ring2, ring1);
+    for (int u = 0; 2 * u < n_tiles; u += 2) {
+      step(u, ring64a, ring64b);
+      step(u + 1, ring64b, ring64a);
     }
-    // the last prefetches (re-reads of the last tile) must land before the
-    // workgroup's LDS can be handed to another workgroup
-    __builtin_amdgcn_s_waitcnt(0x70);  // vmcnt(0) lgkmcnt(0)
+    // (the last barrier waited for every load, so the LDS can be handed on)
   } else {
     // two LDS buffers fed from two register stages: compute tile t from
     // buffer t%2, move tile t+1 from stage `nxt` into the other buffer and
