@@ -241,10 +241,12 @@ __global__ __launch_bounds__(WAVES * 64) void flash_bwd_kernel(FlashBwdParams p)
     };
 
     if constexpr (sizeof(T) == 2) {
-      // Ring of three tile buffers (see flash_kernel): step t loads tile t+2
-      // into the buffer tile t-1 used, computes tile t, waits for its own
-      // loads of tile t+1 and meets the other waves at a barrier (no fence).
-      // Tiles past the last one re-read it (their keys are masked).
+      // Ring of three 32-key tile buffers fed by global-to-LDS loads: step t
+      // loads tile t+2 into the buffer tile t-1 used, computes tile t, waits
+      // for its own loads of tile t+1 and meets the other waves at a barrier
+      // (no fence).  Tiles past the last one re-read it (their keys are
+      // masked).  (The forward flash kernel's two 64-key buffers were
+      // slightly slower for this pass.)
       constexpr int NDMA = (2 * kKT * kHeadDim / 8) / (WAVES * 64);
       static_assert(NDMA >= 1 && NDMA * WAVES * 64 == 2 * kKT * kHeadDim / 8, "tile must split evenly");
       using TL = Tile<T>;
