@@ -184,6 +184,22 @@ __global__ __launch_bounds__(WAVES * 64) void hot_group_kernel(TopkParams p) {
       const typename F::Q qf = F::load_q(qi >= 0 ? Q + (int64_t)qi * p.row_stride + hoff : nullptr, hf);
       const int64_t qh = hq + (qi >= 0 ? qi : 0);
       const float th = qi >= 0 ? p.theta[qh] : INFINITY;
+      // Up to four candidates per lane wait in registers; list slots are
+      // taken with one atomic per four (or at the end of the batch), not per
+      // tile, so the atomic's round trip is rarely on the tile loop's path.
+      uint2 pend0 = {}, pend1 = {}, pend2 = {}, pend3 = {};
+      int np = 0;
+      auto flush = [&]() __attribute__((always_inline)) {
+        if (np > 0) {
+          const int slot = atomicAdd(p.cnt + qh, np);
+          uint2* dst = p.cand + qh * p.cap;
+          if (slot < p.cap) dst[slot] = pend0;
+          if (np > 1 && slot + 1 < p.cap) dst[slot + 1] = pend1;
+          if (np > 2 && slot + 2 < p.cap) dst[slot + 2] = pend2;
+          if (np > 3 && slot + 3 < p.cap) dst[slot + 3] = pend3;
+          np = 0;
+        }
+      };
       ExclCursor excl;
       for (int t = 0; t < nt; ++t) {
         f32x16 s = F::qk(reinterpret_cast<const T*>(smem + t * KBYTES), r, hf, qf);
@@ -211,18 +227,21 @@ __global__ __launch_bounds__(WAVES * 64) void hot_group_kernel(TopkParams p) {
 #pragma unroll
             for (int a = 0; a < 4; ++a)
               *reinterpret_cast<f32x4*>(stash + 4 * a) = f32x4{s[4 * a], s[4 * a + 1], s[4 * a + 2], s[4 * a + 3]};
-            int slot = atomicAdd(p.cnt + qh, __builtin_popcount(m));
-            uint2* dst = p.cand + qh * p.cap;
             while (m != 0) {
               const int i = __builtin_ctz(m);
               m &= m - 1;
-              if (slot < p.cap)
-                dst[slot] = make_uint2(__float_as_uint(stash[i]), (uint32_t)(key0 + 8 * (i >> 2) + 4 * hf + (i & 3)));
-              ++slot;
+              if (np == 4) flush();
+              const uint2 e = make_uint2(__float_as_uint(stash[i]), (uint32_t)(key0 + 8 * (i >> 2) + 4 * hf + (i & 3)));
+              pend0 = np == 0 ? e : pend0;
+              pend1 = np == 1 ? e : pend1;
+              pend2 = np == 2 ? e : pend2;
+              pend3 = np == 3 ? e : pend3;
+              ++np;
             }
           }
         }
       }
+      flush();
     };
 
     uint32_t head = 0, tail = 0;  // wave-uniform ring positions
