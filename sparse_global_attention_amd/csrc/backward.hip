@@ -776,13 +776,15 @@ __global__ __launch_bounds__(256) void inv_zero_kernel(int32_t* x, int64_t n) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < n) x[gid] = 0;
 }
+// Counts per (head, window) list; the count an entry's atomic returns is its
+// rank in the list (in arrival order), parked in `list` until the scatter.
 __global__ __launch_bounds__(256) void inv_count_kernel(InvParams p) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = p.n_windows * p.n_heads * p.topk;
   if (gid >= n) return;
   const int32_t j = p.topk_idx[gid];
   const int64_t h = (gid / p.topk) % p.n_heads;
-  if (j >= 0 && j < p.n_windows) atomicAdd(&p.off[h * p.n_windows + j], 1);
+  if (j >= 0 && j < p.n_windows) p.list[gid] = atomicAdd(&p.off[h * p.n_windows + j], 1);
 }
 // Exclusive scan of off[0 .. n) in blocks of 1024 (4 per thread), block sums
 // scanned by one workgroup, then added back.
@@ -832,6 +834,7 @@ __global__ __launch_bounds__(256) void scan_add_kernel(int32_t* x, int64_t n, co
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < n) x[gid] += bsum[gid / kScanBlock];
 }
+// Each entry to its list at the scanned offset + its rank (no atomics).
 __global__ __launch_bounds__(256) void inv_fill_kernel(InvParams p) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = p.n_windows * p.n_heads * p.topk;
@@ -839,9 +842,7 @@ __global__ __launch_bounds__(256) void inv_fill_kernel(InvParams p) {
   const int32_t j = p.topk_idx[gid];
   const int64_t i = gid / p.topk / p.n_heads, h = (gid / p.topk) % p.n_heads;
   if (j < 0 || j >= p.n_windows) return;
-  const int64_t seg = h * p.n_windows + j;
-  const int32_t pos = p.off[seg] + atomicAdd(&p.cursor[seg], 1);
-  p.raw[pos] = (int32_t)i;
+  p.raw[p.off[h * p.n_windows + j] + p.list[gid]] = (int32_t)i;
 }
 // One wave per list: each element's position is its rank (ties by fill
 // position, so repeated entries keep distinct slots); the result does not
@@ -962,7 +963,6 @@ hipError_t launch_inverse_index(const InvParams& p, hipStream_t stream) {
   if (segs == 0) return hipSuccess;
   const unsigned gz = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL(inv_zero_kernel, dim3(gz), dim3(256), 0, stream, p.off, n);
-  hipLaunchKernelGGL(inv_zero_kernel, dim3(gz), dim3(256), 0, stream, p.cursor, segs);
   const unsigned ge = (unsigned)((entries + 255) / 256);
   hipLaunchKernelGGL(inv_count_kernel, dim3(ge), dim3(256), 0, stream, p);
   const int64_t nb = (n + kScanBlock - 1) / kScanBlock;

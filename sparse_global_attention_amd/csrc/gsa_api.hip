@@ -121,7 +121,7 @@ struct Plan {
   int ctx_qsplits;  // query splits of the context frames' key-side pass
   int64_t qblk, qT, kT, vrow, lse_c, spec_o32, spec_l2, spec_dd, osel, l2sel, doblk, doT, l2blk, dblk,
       dzblk, dosel_img, dsel_img, doc, dc, l2c, dwg_part, dwg_slices, dqc, dkc, dvc;
-  int64_t inv_off, inv_cursor, inv_bsum, inv_raw, inv_list, inv_order, inv_ccnt, inv_cbsum, ctx_dq, ctx_dkdv;
+  int64_t inv_off, inv_bsum, inv_raw, inv_list, inv_order, inv_ccnt, inv_cbsum, ctx_dq, ctx_dkdv;
 };
 
 // Training state saved by gsa_forward_train for gsa_backward_train.
@@ -310,7 +310,6 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.dkc = take(wf);
     p.dvc = take(wf);
     p.inv_off = take((segs + 1) * 4);
-    p.inv_cursor = take(segs * 4);
     p.inv_bsum = take(((segs + 1 + 1023) / 1024) * 4);
     p.inv_raw = take(entries * 4);
     p.inv_list = take(entries * 4);
@@ -1047,7 +1046,6 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   ip.n_windows = g.n_windows;
   ip.n_heads = (int)H;
   ip.off = reinterpret_cast<int32_t*>(at(ws, pl.inv_off));
-  ip.cursor = reinterpret_cast<int32_t*>(at(ws, pl.inv_cursor));
   ip.bsum = reinterpret_cast<int32_t*>(at(ws, pl.inv_bsum));
   ip.raw = reinterpret_cast<int32_t*>(at(ws, pl.inv_raw));
   ip.list = reinterpret_cast<int32_t*>(at(ws, pl.inv_list));

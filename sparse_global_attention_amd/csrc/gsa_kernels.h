@@ -297,10 +297,9 @@ struct InvParams {
   int64_t n_windows;
   int n_heads;
   int32_t* off;     // [H*M' + 1]: counts, then offsets
-  int32_t* cursor;  // [H*M']
   int32_t* bsum;    // scan block sums
   int32_t* raw;     // [H*M'*k] lists in fill order
-  int32_t* list;    // [H*M'*k] lists, ascending
+  int32_t* list;    // [H*M'*k] lists, ascending (before: each entry's rank in its list)
   int32_t* order;   // optional [H*M']: (head, window) lists, longest length class first
   int32_t* ccnt;    // [8 * ceil(H*M' / 1024)] class counts per block, then their scan
   int32_t* cbsum;   // scan block sums of ccnt
