@@ -76,27 +76,39 @@ __global__ __launch_bounds__(256) void threshold_kernel(TopkParams p) {
   const int NG = p.n_groups;
   const float* src = p.gbound + h * NG * p.n_q + q;
   const int g0 = li * VPL;
+  // The keys' top 31 bits (the lowest dropped): the difference of two such
+  // keys is negative exactly when the first is below, so a count is the sign
+  // bits shifted into a mask (one v_alignbit per key) and a popcount per 32
+  // keys.  theta may then come out one key step low, still a lower bound of
+  // the k-th largest bound (which only admits candidates), and the hot test
+  // below, at the same resolution, keeps a superset of the groups.
   uint32_t kv[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int g = min(g0 + i, NG - 1);  // clamped, unconditional loads
     const uint32_t x = order_key(src[(int64_t)g * p.n_q]);
-    kv[i] = g0 + i < NG ? x : 0u;
+    kv[i] = (g0 + i < NG ? x : 0u) >> 1;
   }
   uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 30; b >= 0; --b) {
     const uint32_t cand = T | (1u << b);
-    int cnt = 0;
+    int below = 0;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) cnt += kv[i] >= cand ? 1 : 0;
+    for (int w = 0; w < VPL / 32; ++w) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) m = __builtin_amdgcn_alignbit(m, kv[32 * w + i] - cand, 31);
+      below += __builtin_popcount(m);
+    }
+    int cnt = VPL - below;
     cnt += quad_xor1(cnt);
     cnt += quad_xor2(cnt);
     if (cnt >= p.topk) T = cand;
   }
   const uint32_t k_ninf = order_key(-INFINITY);
-  const bool fin = T > k_ninf;
-  const float theta = fin ? key_value(T) : -INFINITY;
-  const uint32_t thr = fin ? order_key(theta - p.gerr[qh]) - 1u : 0xffffffffu;
+  const bool fin = (T << 1) > k_ninf;
+  const float theta = fin ? key_value(T << 1) : -INFINITY;
+  const uint32_t thr = fin ? (order_key(theta - p.gerr[qh]) - 1u) >> 1 : 0x7fffffffu;
   if (valid) {
 #pragma unroll
     for (int w = 0; w < VPL / 32; ++w) {
@@ -104,7 +116,8 @@ __global__ __launch_bounds__(256) void threshold_kernel(TopkParams p) {
       if (word < p.n_words) {
         uint32_t bits = 0;
 #pragma unroll
-        for (int b = 0; b < 32; ++b) bits |= (kv[32 * w + b] >= thr && kv[32 * w + b] > k_ninf ? 1u : 0u) << b;
+        for (int b = 0; b < 32; ++b)
+          bits |= (kv[32 * w + b] >= thr && kv[32 * w + b] > (k_ninf >> 1) ? 1u : 0u) << b;
         p.hot[(h * p.n_words + word) * p.n_q + q] = bits;
       }
     }
