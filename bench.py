@@ -79,9 +79,9 @@ KERNEL_SOURCES = {
     "hot_group_kernel<bf16,8>": ("topk.hip", "flash_frag.h") + _COMMON,
     "rank_kernel": ("topk.hip", "flash_frag.h") + _COMMON,
     "refine_kernel<bf16,4,64>": ("topk.hip", "flash_frag.h") + _COMMON,
-    "select_kernel<bf16,1>": ("select.hip", "select_frag.h") + _COMMON,
+    "select_kernel<bf16,1>": ("select.hip", "select_frag.h", "flash_frag.h") + _COMMON,
     "pool_kernel<bf16>": ("pool.hip",) + _COMMON,
-    "combine_kernel<bf16>": ("select.hip", "select_frag.h") + _COMMON,
+    "combine_kernel<bf16>": ("select.hip", "select_frag.h", "flash_frag.h") + _COMMON,
     "merge_kernel<bf16>": ("flash.hip", "flash_frag.h") + _COMMON,
     "flash_kernel<bf16,4,partial>,rloop": ("flash.hip", "flash_frag.h") + _COMMON,
     "descriptor_kernel": ("descriptor.hip",) + _COMMON,
@@ -336,8 +336,9 @@ def main():
     idx_bytes = sh.n_windows * H * sh.topk * 4
     # standalone selection: q rows in, the gathers, the index lists, O_sel (fp32) out
     select_bytes = gather_bytes + sh.m_img * H * d * (esz + 4) + idx_bytes
-    # its overhead: the blocked V^T copy it builds first (V read, copy written)
-    select_copy_bytes = sh.m_img * H * d * esz + sh.n_windows * H * sb * d * esz
+    # its overhead: fp32 builds a blocked V^T copy first (V read, copy written);
+    # bf16 gathers V rows from the token layout and builds none
+    select_copy_bytes = 0 if esz == 2 else sh.m_img * H * d * esz + sh.n_windows * H * sb * d * esz
     # the forward's fused selection launch: q in, gathers, lists, O'_comp in, o out
     select_fused_bytes = gather_bytes + 2 * sh.m_img * H * d * esz + idx_bytes + sh.n_windows * H * d * 4
     combine_bytes = sh.m_img * H * d * (esz + 4 + esz) + sh.n_windows * H * d * 4
@@ -348,7 +349,7 @@ def main():
         "flash_kernel<bf16,4,bound>": ("mfma", fl["compressed"], "compressed attention sweep (+ score bounds)"),
         "flash_kernel<bf16,4,partial>": ("mfma", fl["special"], "special-token attention partials"),
         "select_kernel<bf16,1>": ("hbm", select_fused_bytes, "selection attention + fused upsample/gate (forward)"),
-        "pool_kernel<bf16>": ("hbm", pool_bytes, "pooling (the forward's launch also writes the blocked V^T copy)"),
+        "pool_kernel<bf16>": ("hbm", pool_bytes, "pooling of Q, K and V"),
         "hot_group_kernel<bf16,8>": ("overhead", None, "top-k: re-scoring of the hot key groups"),
         "threshold_kernel<64>": ("overhead", None, "top-k: theta and hot-group masks"),
         "rank_kernel": ("overhead", None, "top-k: ranking of the candidate lists"),
@@ -385,8 +386,8 @@ def main():
         "pool_frac_hbm": round(pool_bytes / (st["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "select_gather_bytes": gather_bytes,
         # the standalone selection call: algorithmic bytes (q rows in, gathers,
-        # lists, O_sel out) over the entry point's time; the blocked V^T copy it
-        # builds first is overhead, reported beside
+        # lists, O_sel out) over the entry point's time; the blocked V^T copy an
+        # fp32 call builds first is overhead, reported beside (0 for bf16)
         "select_bytes": select_bytes,
         "select_copy_overhead_bytes": select_copy_bytes,
         "select_hbm_gbs": round(select_bytes / (st["select_standalone"] * 1e-3) / 1e9, 1),

@@ -130,7 +130,8 @@ gsa_status gsa_compressed_attn_topk(const gsa_config* cfg, const void* qc, const
  * full-resolution K/V of its window's top-k windows, the s^2 queries of a
  * window share one KV set; section "Speed3R-VGGT 适配": plus all T_f tokens
  * of each fixed-context frame, in one joint softmax).  topk_idx entries < 0
- * or >= M' are skipped.  Writes o_sel.  Workspace: GSA_OP_SELECT bytes.
+ * or >= M' are skipped.  Writes o_sel.  Workspace: GSA_OP_SELECT bytes (none
+ * for bf16 without context frames).
  */
 gsa_status gsa_select_attn(const gsa_config* cfg, const void* q, const void* k, const void* v,
                            const int32_t* topk_idx, float* o_sel, void* ws, size_t ws_bytes,

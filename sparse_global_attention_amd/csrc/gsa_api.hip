@@ -252,8 +252,11 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.cnt = take(qh * 4);
     p.cand = take(qh * p.cap * 8);
   }
+  // transposed V blocks for the selection gathers: fp32 only (bf16 gathers
+  // V rows and transposes them in LDS)
+  const int64_t vt_blk = c.dtype == GSA_BF16 ? 0 : blk;
   if (op == GSA_OP_FORWARD || op == GSA_OP_SELECT) {
-    p.vblk = take(blk);
+    p.vblk = take(vt_blk);
     p.ctx_o = take(ctx_o);
     p.ctx_lse = take(ctx_lse);
   }
@@ -278,7 +281,7 @@ Plan make_plan(const Call& c, gsa_op op) {
     p.kblk = take(blk);
     p.kT = take(tblk);
     p.vrow = take(blk);
-    p.vblk = take(blk);
+    p.vblk = take(vt_blk);
     p.oc = take(wf);
     p.lse_c = take(wl);
     p.spec_o = take(spec_o);
@@ -489,12 +492,14 @@ PoolParams pool_base(const Call& c) {
   return p;
 }
 
-SelectParams select_base(const Call& c, const Plan& pl, const void* q, const void* k, const int32_t* idx, void* ws) {
+SelectParams select_base(const Call& c, const Plan& pl, const void* q, const void* k, const void* v,
+                         const int32_t* idx, void* ws) {
   SelectParams s;
   memset(&s, 0, sizeof(s));
   s.q = q;
   s.k = k;
-  s.vblk = at(ws, pl.vblk);
+  s.v = v;
+  s.vblk = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.vblk);
   s.topk_idx = idx;
   s.topk = c.topk;
   s.g = c.g;
@@ -571,15 +576,19 @@ gsa_status gsa_select_attn(const gsa_config* cfg, const void* q, const void* k, 
   Plan pl = make_plan(c, GSA_OP_SELECT);
   if ((s = check_ws(pl, ws, ws_bytes)) != GSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the transposed V blocks the selection gathers (K rows come from k itself)
-  PoolParams pp = pool_base(c);
-  pp.src[2] = v;
-  pp.trans[2] = at(ws, pl.vblk);
-  pp.first_tensor = 2;
-  hipError_t e = launch_pool(c.dtype, pp, 1, st);
+  // fp32: the transposed V blocks the selection gathers (bf16 gathers K and V
+  // rows from k and v themselves)
+  hipError_t e = hipSuccess;
+  if (c.dtype != GSA_BF16) {
+    PoolParams pp = pool_base(c);
+    pp.src[2] = v;
+    pp.trans[2] = at(ws, pl.vblk);
+    pp.first_tensor = 2;
+    e = launch_pool(c.dtype, pp, 1, st);
+  }
   if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
   if (e != hipSuccess) return GSA_ERR_HIP;
-  SelectParams sp = select_base(c, pl, q, k, topk_idx, ws);
+  SelectParams sp = select_base(c, pl, q, k, v, topk_idx, ws);
   sp.osel = o_sel;
   return hip_status(launch_select(c.dtype, sp, st));
 }
@@ -637,7 +646,7 @@ gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, con
   if (state && (int64_t)state_bytes < ts.total) return GSA_ERR_WORKSPACE;
   auto saved = [&](int64_t off) { return state ? reinterpret_cast<float*>(at(state, off)) : nullptr; };
 
-  // 1. pooling of Q/K/V plus the transposed V blocks for the gather
+  // 1. pooling of Q/K/V (fp32: plus the transposed V blocks for the gather)
   PoolParams pp = pool_base(c);
   pp.src[0] = q;
   pp.src[1] = k;
@@ -645,7 +654,7 @@ gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, con
   pp.dst[0] = at(ws, pl.qc);
   pp.dst[1] = at(ws, pl.kc);
   pp.dst[2] = at(ws, pl.vc);
-  pp.trans[2] = at(ws, pl.vblk);
+  pp.trans[2] = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.vblk);
   pp.first_tensor = 0;
   hipError_t e = launch_pool(c.dtype, pp, 3, st);
   // 2. special tokens over all tokens
@@ -659,7 +668,7 @@ gsa_status forward_impl(const gsa_config* cfg, const void* q, const void* k, con
   if (e == hipSuccess && c.n_ctx) e = run_context(c, pl, q, k, v, ws, st);
   // 5. selection + upsample + gate
   if (e == hipSuccess) {
-    SelectParams sp = select_base(c, pl, q, k, idx, ws);
+    SelectParams sp = select_base(c, pl, q, k, v, idx, ws);
     sp.wg = wg;
     sp.oc = oc;
     sp.o = o;
@@ -830,7 +839,8 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   pp.rows[1] = at(ws, pl.kblk);
   pp.trans[1] = c.dtype == GSA_BF16 ? nullptr : at(ws, pl.kT);
   pp.rows[2] = at(ws, pl.vrow);
-  pp.trans[2] = state ? nullptr : at(ws, pl.vblk);  // V^T only for the selection recompute
+  // V^T only for an fp32 selection recompute
+  pp.trans[2] = state || c.dtype == GSA_BF16 ? nullptr : at(ws, pl.vblk);
   ok(launch_pool(c.dtype, pp, 3, st));
 
   // 2. forward quantities: compressed output + log-sum-exp (one split)
@@ -912,7 +922,7 @@ gsa_status backward_impl(const gsa_config* cfg, const void* q, const void* k, co
   float* l2sel = state ? saved(ts.l2sel) : reinterpret_cast<float*>(at(ws, pl.l2sel));
   if (!state) {
     if (c.n_ctx && e == hipSuccess) ok(run_context(c, pl, q, k, v, ws, st));
-    SelectParams sp = select_base(c, pl, q, k, topk_idx, ws);
+    SelectParams sp = select_base(c, pl, q, k, v, topk_idx, ws);
     sp.osel = osel;
     sp.l2 = l2sel;
     ok(launch_select(c.dtype, sp, st));

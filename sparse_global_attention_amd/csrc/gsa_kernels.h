@@ -175,7 +175,8 @@ hipError_t launch_merge(int dtype, const MergeParams& p, hipStream_t stream);
 struct SelectParams {
   const void* q;        // token layout
   const void* k;        // token layout (K rows are gathered from it directly)
-  const void* vblk;     // [M'][H][d][sb] transposed V blocks
+  const void* v;        // token layout (bf16: V rows are gathered from it directly)
+  const void* vblk;     // fp32: [M'][H][d][sb] transposed V blocks
   const int32_t* topk_idx;  // [M'][H][topk]
   int topk;
   Geometry g;

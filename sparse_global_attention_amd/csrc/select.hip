@@ -11,12 +11,14 @@
 //  * section "压缩分支" (nearest-neighbour upsampling) and section "门控聚合"
 //    (g = sigmoid(W_g q), O = g O_comp + (1 - g) O_sel): fused epilogue.
 //
-// Gather-bound.  The K rows of a selected (window, head) are read straight
-// from the token layout (a lane reads 32 bytes of one 128-byte row, the same
-// access a blocked copy would give), V from the contiguous transposed block
-// [d][sb] the pooling pass writes (slots contiguous per channel, as the PV
-// operand needs), so every lane issues 16-byte loads that land directly in
-// matrix-core operand layout (no LDS, no barriers; waves are independent).
+// Gather-bound.  The K and V rows of a selected (window, head) are read
+// straight from the token layout.  K lands directly in matrix-core operand
+// layout (a lane reads 32 bytes of one 128-byte row).  V's product contracts
+// over the slots, so its operand needs them contiguous per channel: bf16 V
+// rows go by global-to-LDS loads into a wave-private slab and are read back
+// transposed (ds_read_b64_tr_b16); fp32, which has no such read, gathers V
+// from the transposed block [d][sb] the pooling pass writes.  No barriers:
+// waves are independent.
 // A chunk is 32 key slots (two windows at s = 4); the next chunk's loads are
 // issued before the current chunk's matrix-core work.
 //   S^T[32 slots x 16 q] : 2 tiles x 2 x v_mfma_f32_16x16x32_bf16 (K = d)
@@ -34,9 +36,10 @@ template <typename T>
 struct SelChunk {
   static constexpr int VE = 16 / sizeof(T);
   static constexpr int KV = 16 / VE;  // 16-byte loads per 16 channels of a K row
-  static constexpr int VV = 8 / VE;   // 16-byte loads per 8 slots of a V^T row
+  static constexpr int VV = 8 / VE;   // fp32: 16-byte loads per 8 slots of a V^T row
+  static constexpr bool kSlabV = sizeof(T) == 2;  // bf16: V rows in an LDS slab
   uint4 k[2][KV];
-  uint4 v[4][VV];
+  uint4 v[kSlabV ? 1 : 4][kSlabV ? 1 : VV];  // fp32: the V^T operand
   int jv;    // window of this lane's 8 S^T slots (-1: none)
   int kkv0;  // window-local key of the first of them
 };
@@ -60,21 +63,44 @@ __device__ __forceinline__ int64_t window_base(const Geometry& g, int j) {
   return f * g.tf + g.n_special + wy * g.pool * g.grid_w + wxx * g.pool;
 }
 
+// bf16 V slab of a chunk: 32 rows (the chunk's slots) of 128 bytes, the
+// 16-byte pieces of row r permuted (position x holds channels 8 (x ^ vswz(r))
+// onward) so that the 16 rows one transposing read touches (32 bytes each)
+// spread over the banks: rows 8g + {0, 2} and 8g + {1, 3} of the four lane
+// groups g get four different 32-byte positions.
+__device__ __forceinline__ int vswz(int r) { return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1; }
+
+// Slabs of chunks A and B, one per wave: two arrays, so that the compiler
+// tells the reads of one from the global-to-LDS loads into the other.
+__shared__ __attribute__((aligned(16))) __bf16 sel_vslab_a[4][32 * kHeadDim];
+__shared__ __attribute__((aligned(16))) __bf16 sel_vslab_b[4][32 * kHeadDim];
+
+__device__ __forceinline__ const void* wave_uniform(const void* ptr) {
+  const uint64_t x = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
 template <typename T>
 __device__ __forceinline__ void load_chunk(SelChunk<T>& ch, const SelectParams& p, int64_t h, int c, int ql,
-                                           int g, int tr0, int tr1, int64_t tb0, int64_t tb1) {
+                                           int g, int tr0, int tr1, int64_t tb0, int64_t tb1, __bf16* vslab) {
   using C = SelChunk<T>;
   const int64_t sb = p.g.sb, H = p.g.n_heads;
   const int s = (int)p.g.pool, s2 = s * s;
   const T* K = static_cast<const T*>(p.k);
   const T* vblk = static_cast<const T*>(p.vblk);
+  // Slot positions are multiples of 8 below k sb <= 8192 and sb is a multiple
+  // of 8 up to 64, so entry and key follow from u = position / 8 < 1024 and
+  // sb / 8 <= 8 by one multiply: (u * msb) >> 16 = u / (sb / 8) exactly.
+  const int sb8 = (int)(sb >> 3), msb = (65536 + sb8 - 1) / sb8;
   // K operand: A-row ql of tile tau is slot 8*(ql/4) + 4*tau + ql%4 of the
   // chunk, i.e. key kka + 4 tau (row-major in the s x s window) of top-k
-  // entry ga / sb; keys past s^2 (padding slots) read the window's first
-  // token instead -- their scores are masked below.
-  const int64_t ga = (int64_t)c * 32 + 8 * (ql >> 2);
-  const int64_t base = topk_base(tb0, tb1, (int)(ga / sb));
-  const int kka = (int)(ga % sb) + (ql & 3);
+  // entry ea; keys past s^2 (padding slots) read the window's first token
+  // instead -- their scores are masked below.
+  const int ua = c * 4 + (ql >> 2), ea = (ua * msb) >> 16;
+  const int64_t base = topk_base(tb0, tb1, ea);
+  const int kka = 8 * (ua - ea * sb8) + (ql & 3);
   const int64_t row0 = base < 0 ? 0 : base;
   const int m16 = (65536 + s - 1) / s;  // kk / s = (kk * m16) >> 16 exactly for kk < 64, s <= 8
 #pragma unroll
@@ -85,19 +111,67 @@ __device__ __forceinline__ void load_chunk(SelChunk<T>& ch, const SelectParams& 
 #pragma unroll
     for (int x = 0; x < C::KV; ++x) ch.k[tau][x] = ld16(kb + x * C::VE);
   }
-  // V^T operand and S^T rows of this lane: slots 8g .. 8g+7 of the chunk
-  const int64_t gv = (int64_t)c * 32 + 8 * g;
-  ch.jv = topk_entry(tr0, tr1, (int)(gv / sb), p.topk, p.g.n_windows);
-  ch.kkv0 = (int)(gv % sb);
-  const T* vb = vblk + ((int64_t)(ch.jv < 0 ? 0 : ch.jv) * H + h) * kHeadDim * sb + ch.kkv0;
+  // S^T rows of this lane: slots 8g .. 8g+7 of the chunk
+  const int uv = c * 4 + g, ev = (uv * msb) >> 16;
+  ch.jv = topk_entry(tr0, tr1, ev, p.topk, p.g.n_windows);
+  ch.kkv0 = 8 * (uv - ev * sb8);
+  if constexpr (C::kSlabV) {
+    // V rows into the slab: load i fills rows 8i .. 8i+7 (the same window,
+    // sb being a multiple of 8), lane l row 8i + l/8 at position l%8, from a
+    // buffer whose base is the window's first row of this head; padding keys
+    // and skipped entries read past the buffer's limit, i.e. zeros.
+    const int lane = 16 * g + ql;
+    const T* V = static_cast<const T*>(p.v);
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+    for (int i = 0; i < 4; ++i) {
+      const int u = c * 4 + i, e = (u * msb) >> 16;
+      const int64_t wb = topk_base(tb0, tb1, e);  // the same in every lane
+      const int kk = 8 * (u - e * sb8) + (lane >> 3);
+      const int dy = (kk * m16) >> 16, dx = kk - dy * s;
+      const int r = 8 * i + (lane >> 3);
+      const uint32_t voff = wb >= 0 && kk < s2
+                                ? (uint32_t)((dy * p.g.grid_w + dx) * (int)H * kHeadDim + 8 * ((lane & 7) ^ vswz(r))) * 2u
+                                : 0x80000000u;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<void*>(wave_uniform(V + ((wb < 0 ? 0 : wb) * H + h) * kHeadDim)), (short)0, 0x7fffffff,
+          0x00020000);
+      lds_load16(rs, vslab + 512 * i, (int)voff);
+    }
+  } else {
+    // V^T operand: channel 16 m + ql of the same slots
+    const T* vb = vblk + ((int64_t)(ch.jv < 0 ? 0 : ch.jv) * H + h) * kHeadDim * sb + ch.kkv0;
 #pragma unroll
-    for (int x = 0; x < C::VV; ++x) ch.v[m][x] = ld16(vb + (16 * m + ql) * sb + x * C::VE);
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int x = 0; x < C::VV; ++x) ch.v[m][x] = ld16(vb + (16 * m + ql) * sb + x * C::VE);
+  }
+}
+
+// bf16: the V^T operand of a chunk from its slab.  Lane j of group g addresses
+// row 8 g + j/4 (then + 4), channels 16 m + 4 (j%4) .. + 3; the transposing
+// read hands lane i of the group channel 16 m + i of rows 8 g .. 8 g + 7
+// (within a 16-lane group, lane i gets element i%4 of the 8-byte pieces
+// addressed by lanes 4e + i/4).
+__device__ __forceinline__ void slab_vt(const __bf16* vslab, int ql, int g, uint4 (&vt)[4][1]) {
+  const int r = 8 * g + (ql >> 2), sw = vswz(r);  // row r + 4 has the same permutation
+  // The second row's offset is kept opaque: folded into the read as an
+  // immediate, the read loses the compiler's record of which slab it reads
+  // and then waits for every global-to-LDS load in flight, the next chunk's
+  // included.
+  const int off_lo = r * kHeadDim + 4 * (ql & 1);
+  int off_hi = off_lo + 4 * kHeadDim;
+  asm volatile("" : "+v"(off_hi));
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int x = (2 * m + ((ql >> 1) & 1)) ^ sw;
+    const bf16x4 lo = lds_read_tr16(vslab + off_lo + 8 * x);
+    const bf16x4 hi = lds_read_tr16(vslab + off_hi + 8 * x);
+    vt[m][0] = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
 template <typename T, int QB>
-__global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QB == 1 && sizeof(T) == 2 ? 4 : 1))) void select_kernel(SelectParams p) {
   using F = Frag16<T>;
   const Geometry& geo = p.g;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
@@ -145,7 +219,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
     }
 
     // One chunk: scores of 32 key slots, online softmax, PV, for each block.
-    auto process = [&](const SelChunk<T>& ch) __attribute__((always_inline)) {
+    auto process = [&](const SelChunk<T>& ch, const __bf16* vslab) __attribute__((always_inline)) {
+      uint4 vt[4][1];
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
       const typename F::Q& qf = qfs[b];
@@ -181,26 +256,39 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
         ps += p0[e] + p1[e];
       }
       l_run += ps;
-      F::pv(ch.v, p0, p1, o);
+      if constexpr (SelChunk<T>::kSlabV) {
+        // after the first block's scores, so that V's loads have had their time
+        if (b == 0) slab_vt(vslab, ql, g, vt);
+        F::pv(vt, p0, p1, o);
+      } else {
+        F::pv(ch.v, p0, p1, o);
+      }
       }
     };
 
     // Two chunk buffers alternate so that two chunks of gathers are always in
     // flight; no register copies (a copy would wait for its loads).
     SelChunk<T> A, B;
-    load_chunk<T>(A, p, h, 0, ql, g, tr0, tr1, tb0, tb1);
-    load_chunk<T>(B, p, h, 1, ql, g, tr0, tr1, tb0, tb1);
+    __bf16* sa = nullptr;
+    __bf16* sbb = nullptr;
+    if constexpr (SelChunk<T>::kSlabV) {
+      const int wu = __builtin_amdgcn_readfirstlane(wv);
+      sa = sel_vslab_a[wu];
+      sbb = sel_vslab_b[wu];
+    }
+    load_chunk<T>(A, p, h, 0, ql, g, tr0, tr1, tb0, tb1, sa);
+    load_chunk<T>(B, p, h, 1, ql, g, tr0, tr1, tb0, tb1, sbb);
     int ci = 0;
     for (; ci + 3 < n_chunks; ci += 2) {
-      process(A);
-      load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1, tb0, tb1);
-      process(B);
-      load_chunk<T>(B, p, h, ci + 3, ql, g, tr0, tr1, tb0, tb1);
+      process(A, sa);
+      load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1, tb0, tb1, sa);
+      process(B, sbb);
+      load_chunk<T>(B, p, h, ci + 3, ql, g, tr0, tr1, tb0, tb1, sbb);
     }
-    process(A);
-    if (ci + 2 < n_chunks) load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1, tb0, tb1);
-    if (ci + 1 < n_chunks) process(B);
-    if (ci + 2 < n_chunks) process(A);
+    process(A, sa);
+    if (ci + 2 < n_chunks) load_chunk<T>(A, p, h, ci + 2, ql, g, tr0, tr1, tb0, tb1, sa);
+    if (ci + 1 < n_chunks) process(B, sbb);
+    if (ci + 2 < n_chunks) process(A, sa);
 
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -249,7 +337,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectParams p) {
         for (int m = 0; m < 4; ++m) {
           const int dv0 = 16 * m + 4 * g;
           f32x4 ocv = *reinterpret_cast<const f32x4*>(p.oc + (win * H + h) * kHeadDim + dv0);
-          f32x4 out = gate * ocv + (1.0f - gate) * res[m];
+          // one rounding order whatever the register allocation: (1 - g) O_sel
+          // fused onto the rounded g O'_comp
+          f32x4 out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = fmaf(1.0f - gate, res[m][e], gate * ocv[e]);
           if constexpr (sizeof(T) == 2) {
             bf16x4 b4 = {(__bf16)out[0], (__bf16)out[1], (__bf16)out[2], (__bf16)out[3]};
             *reinterpret_cast<bf16x4*>(dst + dv0) = b4;
@@ -304,7 +396,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const float* osr = p.osel + (u * H + h) * kHeadDim + 8 * part;
   T* dst = static_cast<T*>(p.o) + (tok * H + h) * kHeadDim + 8 * part;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = from_f32<T>(gate * ocr[e] + (1.0f - gate) * osr[e]);
+  for (int e = 0; e < 8; ++e) dst[e] = from_f32<T>(fmaf(1.0f - gate, osr[e], gate * ocr[e]));
 }
 
 hipError_t launch_select(int dtype, const SelectParams& p, hipStream_t stream) {
@@ -313,6 +405,10 @@ hipError_t launch_select(int dtype, const SelectParams& p, hipStream_t stream) {
   const int n_sub = (int)((p.g.pool * p.g.pool + 15) / 16);
   const int64_t items = p.g.n_windows * p.g.n_heads;
   if (items == 0) return hipSuccess;
+  // bf16 V rows are addressed by 32-bit byte offsets from their window's first
+  // row: s token rows of the grid must stay below 2^31 bytes
+  if (dtype == kBF16 && p.g.pool * p.g.grid_w * p.g.n_heads * kHeadDim * 2 >= INT32_MAX - 4096)
+    return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((items + 3) / 4);
   if (dtype == kBF16) {
     if (n_sub == 1) hipLaunchKernelGGL((select_kernel<__bf16, 1>), dim3(blocks), dim3(256), 0, stream, p);

@@ -10,6 +10,7 @@
 //                       lane's own 8 values as the P operand.
 #pragma once
 
+#include "flash_frag.h"
 #include "gsa_device.h"
 
 namespace gsa {
@@ -103,6 +104,35 @@ struct Frag16<float> {
     }
   }
 };
+
+// bf16: the transposed operand of a chunk (slots contiguous per channel, as a
+// product contracting over the slots needs) is built from its rows, already in
+// registers, through a wave-private LDS slab instead of a gather of a
+// transposed copy.  Lane (ql, g) holds rows 8 (ql/4) + 4 tau + ql%4 (tau = 0,
+// 1), channels 16 g .. 16 g + 15; the transposing read (ds_read_b64_tr_b16: within a 16-lane group, lane
+// i gets element i%4 of the 8-byte chunks addressed by lanes 4e + i/4) hands
+// lane i of group g channel 16 m + i of rows 8 g .. 8 g + 7 when lane j of the
+// group addresses row 8 g + j/4 (then + 4), channels 16 m + 4 (j%4).
+constexpr int kSlabStride = kHeadDim + 8;  // bf16 per slab row: 16-byte aligned rows, shifted banks
+constexpr int kSlabElems = 32 * kSlabStride;
+__device__ __forceinline__ void transpose_chunk(const uint4 (&rows)[2][2], uint4 (&tr)[4][1], __bf16* slab, int ql,
+                                                int g) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      st16(slab + (8 * (ql >> 2) + 4 * tau + (ql & 3)) * kSlabStride + 16 * g + 8 * x, rows[tau][x]);
+  // a wave's LDS operations complete in order; the wait keeps the compiler from
+  // moving the transposing reads above the stores
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  const __bf16* r0 = slab + (8 * g + (ql >> 2)) * kSlabStride + 4 * (ql & 3);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bf16x4 lo = lds_read_tr16(r0 + 16 * m);
+    const bf16x4 hi = lds_read_tr16(r0 + 4 * kSlabStride + 16 * m);
+    tr[m][0] = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
 
 // Window id of top-k entry t, from the two registers holding entries lane and
 // lane+64.  Entries past k, negative or not below M' read as -1 (skipped).

@@ -86,9 +86,12 @@ def test_workspace_sizes(lib):
     assert lib.gsa_workspace_size(c, lib.GSA_OP_DENSE) == 0
     mw, H, d = 32 * 64, 16, 64
     pooled = mw * H * d * 2
-    assert sel == mw * H * 16 * d * 2  # the blocked V^T copy, 16 slots per window
-    assert fw >= 3 * pooled + mw * H * d * 4 + mw * H * 16 * 4 + sel + spec
+    assert sel == 0  # bf16 gathers K and V rows from the token layout
+    assert fw >= 3 * pooled + mw * H * d * 4 + mw * H * 16 * 4 + spec
     assert spec > 0
+    # fp32 gathers V from a blocked, transposed copy: 16 slots per window
+    c32 = cfg(lib, n_frames=32, n_special=5, grid_h=32, grid_w=32, n_heads=16, pool=4, topk=16, dtype=lib.GSA_F32)
+    assert lib.gsa_workspace_size(c32, lib.GSA_OP_SELECT) == mw * H * 16 * d * 4
     ctx = cfg(lib, n_frames=8, ctx_frames=(0, 5))
     assert lib.gsa_workspace_size(ctx, lib.GSA_OP_SELECT) > lib.gsa_workspace_size(cfg(lib, n_frames=8),
                                                                                     lib.GSA_OP_SELECT)
@@ -136,8 +139,11 @@ def test_workspace_validation(lib):
     assert lib.call_status("gsa_forward", c, A, A, A, A, o, A, need - 1, None) == 4
     assert lib.call_status("gsa_forward", c, A, A, A, A, o, None, need, None) == 1
     assert lib.call_status("gsa_forward", c, A, A, A, A, o, A + 16, need, None) == 1  # ws not 256-aligned
-    need = lib.gsa_workspace_size(cc, lib.GSA_OP_SELECT)
-    assert lib.call_status("gsa_select_attn", c, A, A, A, A, o, A, need - 256, None) == 4
+    # (bf16 selection needs no workspace without context frames; fp32 does)
+    c32 = cfg(lib, dtype=lib.GSA_F32)
+    need = lib.gsa_workspace_size(c32, lib.GSA_OP_SELECT)
+    assert need > 0
+    assert lib.call_status("gsa_select_attn", ctypes.byref(c32), A, A, A, A, o, A, need - 256, None) == 4
     need = lib.gsa_workspace_size(cc, lib.GSA_OP_SPECIAL)
     assert lib.call_status("gsa_special_attn", c, A, A, A, o, A, need - 1, None) == 4
     need = lib.gsa_workspace_size(cc, lib.GSA_OP_COMPRESSED)
