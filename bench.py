@@ -55,6 +55,9 @@ def parse():
                     help="time only the forward steps (no stage calls or extras; for kernel profiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters) and exit")
+    ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
+                    help="only time a library bf16 GEMM (N x N x N, torch.matmul) with the shader clock "
+                         "sampled, as a reference for what the matrix cores sustain, and exit")
     return ap.parse_args()
 
 
@@ -209,10 +212,43 @@ class ClockSampler:
                 "min_mhz": xs[0], "max_mhz": xs[-1]}
 
 
+def gemm_probe(n: int, seconds: float = 1.5):
+    """A library bf16 GEMM (random N(0,1) operands, fp32 accumulation) timed
+    over ~`seconds` with the shader clock sampled: the rate the matrix cores
+    sustain on dense work at this part's power limit, beside the published peak."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    reps = max(3, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
+    with ClockSampler() as cs:
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"gemm_probe": {"n": n, "dtype": "bf16", "reps": reps, "ms_each": round(ms, 4),
+                                     "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                                     "shader_clock": cs.summary()}}))
+
+
 def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.gemm_probe:
+        gemm_probe(args.gemm_probe)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "

@@ -15,7 +15,8 @@
 //                         the layout of a score-product operand;
 //   trans [M'][H][d][sb]  transposed (tokens contiguous per channel), the
 //                         layout of an operand that contracts over tokens.
-// The forward uses K rows and V transposed; the backward also Q, K^T, V rows.
+// The fp32 forward uses V transposed (bf16 transposes V in LDS and needs no
+// copy); the backward uses Q, K and V rows (fp32 also Q and K transposed).
 #include <type_traits>
 
 #include "gsa_device.h"
