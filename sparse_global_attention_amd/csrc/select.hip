@@ -170,8 +170,12 @@ __device__ __forceinline__ void slab_vt(const __bf16* vslab, int ql, int g, uint
   }
 }
 
+// bf16 with one block of 16 queries per window (s <= 4) fits in 128 VGPRs
+// without spills: four waves per SIMD (the compiler alone picks more registers
+// and three).
 template <typename T, int QB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QB == 1 && sizeof(T) == 2 ? 4 : 1))) void select_kernel(SelectParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QB == 1 && sizeof(T) == 2 ? 4 : 1)))
+void select_kernel(SelectParams p) {
   using F = Frag16<T>;
   const Geometry& geo = p.g;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
