@@ -71,7 +71,10 @@ __device__ __forceinline__ int64_t window_base(const Geometry& g, int j) {
 __device__ __forceinline__ int vswz(int r) { return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1; }
 
 // Slabs of chunks A and B, one per wave: two arrays, so that the compiler
-// tells the reads of one from the global-to-LDS loads into the other.
+// tells the reads of one from the global-to-LDS loads into the other.  A
+// slab's next loads cannot overtake its pending transposing reads: their
+// window bases come from lane permutes issued after the reads, and LDS
+// operations complete in order, so the reads are done when the bases are.
 __shared__ __attribute__((aligned(16))) __bf16 sel_vslab_a[4][32 * kHeadDim];
 __shared__ __attribute__((aligned(16))) __bf16 sel_vslab_b[4][32 * kHeadDim];
 
