@@ -71,10 +71,7 @@ __device__ __forceinline__ int64_t window_base(const Geometry& g, int j) {
 __device__ __forceinline__ int vswz(int r) { return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1; }
 
 // Slabs of chunks A and B, one per wave: two arrays, so that the compiler
-// tells the reads of one from the global-to-LDS loads into the other.  A
-// slab's next loads cannot overtake its pending transposing reads: their
-// window bases come from lane permutes issued after the reads, and LDS
-// operations complete in order, so the reads are done when the bases are.
+// tells the reads of one from the global-to-LDS loads into the other.
 __shared__ __attribute__((aligned(16))) __bf16 sel_vslab_a[4][32 * kHeadDim];
 __shared__ __attribute__((aligned(16))) __bf16 sel_vslab_b[4][32 * kHeadDim];
 
@@ -125,6 +122,9 @@ __device__ __forceinline__ void load_chunk(SelChunk<T>& ch, const SelectParams& 
     // and skipped entries read past the buffer's limit, i.e. zeros.
     const int lane = 16 * g + ql;
     const T* V = static_cast<const T*>(p.v);
+    // The slab's previous chunk must be read out first: a global-to-LDS write
+    // is not ordered after earlier LDS reads of the wave, so wait for them.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int u = c * 4 + i, e = (u * msb) >> 16;
