@@ -56,7 +56,8 @@ typedef enum {
   GSA_OK = 0,
   GSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad k, bad context frame, aliasing */
   GSA_ERR_SHAPE = 2,       /* h or w not divisible by s, non-positive sizes, size overflow
-                              (M' >= 2^29 windows, M >= 2^31 - 64 tokens, M*H*d > 2^40) */
+                              (M' >= 2^29 windows, M >= 2^31 - 64 tokens, M*H*d > 2^40,
+                              s*w*H*d*4 >= 2^31 - 4096 bytes) */
   GSA_ERR_UNSUPPORTED = 3, /* d != 64, s > 8, k > 128, unknown dtype */
   GSA_ERR_WORKSPACE = 4,   /* workspace smaller than gsa_workspace_size() */
   GSA_ERR_HIP = 5          /* a HIP launch failed */

@@ -71,9 +71,11 @@ gsa_status check_cfg(const gsa_config* c, Call* out) {
   // window ids are int32 in topk_idx, key positions inside a kernel's key range
   // are int32, and every element count stays well inside int64
   // (per-head rows of window bounds are addressed with 32-bit byte offsets:
-  // M' * 4 < 2^31)
+  // M' * 4 < 2^31; the selection reads a window's rows at 32-bit byte offsets
+  // from its first row: s grid rows of tokens stay below 2^31 bytes)
   if (g.n_windows >= ((int64_t)1 << 29) || g.m_tokens > INT32_MAX - 64 ||
-      g.m_tokens > ((int64_t)1 << 40) / (g.n_heads * kHeadDim))
+      g.m_tokens > ((int64_t)1 << 40) / (g.n_heads * kHeadDim) ||
+      g.pool * g.grid_w * g.n_heads * kHeadDim * 4 >= (int64_t)INT32_MAX - 4096)
     return GSA_ERR_SHAPE;
 
   out->dtype = c->dtype;

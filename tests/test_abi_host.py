@@ -65,6 +65,9 @@ def cfg(lib, **kw):
     # key positions are int32 inside the kernels: M = 64 N tokens must stay below 2^31 - 64
     (dict(n_frames=(2**31 - 64) // 64, n_special=0, n_heads=1), 2),
     (dict(n_frames=(2**31 - 64) // 64 - 1, n_special=0, n_heads=1), 0),
+    # a window's s grid rows are read at 32-bit byte offsets: s w H d 4 < 2^31 - 4096
+    (dict(n_frames=1, n_special=0, grid_h=8, grid_w=1 << 15, n_heads=32, pool=8), 2),
+    (dict(n_frames=1, n_special=0, grid_h=8, grid_w=1 << 13, n_heads=32, pool=8), 0),
 ])
 def test_config_validation(lib, kw, status):
     size = ctypes.c_size_t()
