@@ -891,7 +891,6 @@ __global__ __launch_bounds__(256) void inv_sort_kernel(InvParams p) {
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int32_t y = c0 + lane < n ? p.raw[b + c0 + lane] : INT32_MAX;
       const int m = n - c0 < 64 ? n - c0 : 64;
-#pragma unroll 8
       for (int f = 0; f < m; ++f) {
         const int32_t yf = __builtin_amdgcn_readlane(y, f);
         rank += (yf < x || (yf == x && c0 + f < e)) ? 1 : 0;
