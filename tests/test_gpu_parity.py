@@ -126,6 +126,33 @@ def test_selection_attention(name):
     assert_close(got, r.osel, sh.dtype, f"{name} O_sel")
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "s3", "s7", "s8", "odd_f32", "ctx"])
+def test_selection_skips_invalid_entries(name):
+    """Top-k entries below 0 or at or past M' are skipped and a repeated entry
+    counts twice (include/gsa.h, gsa_select_attn): the selection over a set
+    with such entries equals the oracle's over the same set with the invalid
+    entries written as -1.  Entry 0 of every row stays valid, so no row is
+    empty; padding slots (s = 3, 7) and context frames take the same path."""
+    r = result(name)
+    sh = r.sh
+    M = sh.n_windows
+    k = r.idx.shape[-1]
+    rng = np.random.default_rng(13)
+    bad = np.array([-1, -7, M, M + 1000, 2**31 - 1], np.int64)
+    idx = r.idx.astype(np.int64).reshape(-1, k).copy()
+    for row in range(idx.shape[0]):
+        pos = rng.permutation(np.arange(1, k))
+        nbad = min(2, k - 1)
+        idx[row, pos[:nbad]] = rng.choice(bad, size=nbad)
+        if k >= 4:
+            idx[row, pos[nbad]] = idx[row, 0]
+    idx = idx.reshape(r.idx.shape)
+    ref_idx = np.where((idx < 0) | (idx >= M), -1, idx).astype(np.int32)
+    got = to_host(r.case.select(torch.from_numpy(idx.astype(np.int32)).to(DEV)))[window_image_ids(sh)]
+    ref = oracle.select(sh, r.case.q, r.case.k, r.case.v, np.arange(M), ref_idx)
+    assert_close(got, ref, sh.dtype, f"{name} O_sel with skipped and repeated entries")
+
+
 @pytest.mark.parametrize("name", [n for n in ALL if SHAPES[n].n_special > 0])
 def test_special_attention(name):
     r = result(name)
