@@ -31,6 +31,9 @@ SHAPES = {
     "s1": GSAShape("s1 2f-6x5-h2-s1-k7", 2, 1, 6, 5, 2, 64, 1, 7, BF16, seed=24),
     "s2": GSAShape("s2 4f-8x8-h2-s2-k4", 4, 3, 8, 8, 2, 64, 2, 4, BF16, seed=25),
     "s5": GSAShape("s5 2f-10x10-h2-s5-k3", 2, 2, 10, 10, 2, 64, 5, 3, BF16, seed=33),
+    # 9 keys in 16 slots and 49 in 56 (padding slots; windows straddle 32-slot chunks)
+    "s3": GSAShape("s3 3f-9x12-h2-s3-k4", 3, 1, 9, 12, 2, 64, 3, 4, BF16, seed=70),
+    "s7": GSAShape("s7 2f-14x14-h2-s7-k3", 2, 1, 14, 14, 2, 64, 7, 3, BF16, seed=71),
     "s6_f32": GSAShape("s6 3f-12x12-h2-s6-k3 fp32", 3, 1, 12, 12, 2, 64, 6, 3, F32, seed=34),
     "p0": GSAShape("p0 4f-8x12-h2-s4-k3", 4, 0, 8, 12, 2, 64, 4, 3, BF16, seed=26),
     "ctx": GSAShape("ctx 6f-8x8-h2-s4-k3+ctx{0,3}", 6, 2, 8, 8, 2, 64, 4, 3, BF16, ctx_frames=(0, 3), seed=27),
