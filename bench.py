@@ -365,7 +365,8 @@ def main():
                 "what": "compressed attention + guide-score top-k (gsa_compressed_attn_topk), the dominant stage",
                 "work_per_launch_flop": fl["compressed"], "avg_launch_ms": round(st["compressed_topk"], 4)}
 
-    # Algorithmic bytes of the memory-bound steps (per unit x units)
+    # Algorithmic bytes of the memory-bound steps: bytes per unit (window, head,
+    # channel or token) times the units one launch processes
     pool_bytes = 3 * sh.m_img * H * d * esz + 3 * sh.n_windows * H * d * esz
     gather_bytes = sh.n_windows * H * sh.topk_eff * sh.pool ** 2 * 2 * d * esz
     sb = (sh.pool ** 2 + 7) // 8 * 8
